@@ -1,0 +1,22 @@
+"""CPU oracle for bidirectional varlen multi-head attention with rotary
+position embedding, forward and backward, in float64.
+
+TEST INFRASTRUCTURE. Only the test-suite, the smoke check and the benchmark's
+CPU-baseline leg may import this package. The product path (the HIP library
+and its Python binding) never imports, links or calls anything here, and this
+package imports nothing from the product path.
+
+Every function is the plain definition written out with numpy, one
+(sequence, head) slice at a time, with no tiling, fusion or reordering.
+"""
+
+from .attention import (  # noqa: F401
+    bf16_bits_to_f64,
+    round_to_bf16,
+    rope_frequencies,
+    rope_rotate,
+    attention_forward_slice,
+    attention_backward_slice,
+    forward,
+    backward,
+)

@@ -1,0 +1,250 @@
+"""Float64 reference for ESM-2-style attention over packed variable-length
+sequences: rotary position embedding, bidirectional softmax attention per
+sequence and head, and its analytic backward.
+
+TEST INFRASTRUCTURE: imported only by tests, the smoke check and the
+benchmark's CPU-baseline leg; never by the product path.
+
+Sources and readings
+--------------------
+* ESM-2 is a BERT-style protein language model ("BioNeMo Framework: a
+  modular, high-performance library for AI model development in drug
+  discovery" review page, Abstract and the "proposed method" list), so
+  attention is bidirectional: every token of a sequence attends to every
+  token of the same sequence and to nothing else.
+* Sequences of different lengths are grouped by a size-aware bucket batch
+  sampler and packed with almost no padding (same review page, "proposed
+  method" and "main findings"). A batch is therefore a packed token-major
+  tensor [T][H][d] plus prefix offsets cu_seqlens[B+1]; sequence b owns
+  tokens cu_seqlens[b] .. cu_seqlens[b+1]-1.
+* Training runs in BF16 (BioNeMo Recipes hub page, multi-precision training
+  section) with FP32 accumulation (BioNeMo blog, section 2.3). Inputs are
+  bf16 values; this oracle upcasts them exactly to float64.
+* The pages do not print the attention formula. The textbook definitions
+  are used: scaled dot-product attention (Vaswani et al. 2017) and rotary
+  position embedding (Su et al. 2021, RoFormer) in the half-split pairing,
+  frequencies theta_j = base^(-2j/d), positions counted from 0 at the start
+  of each sequence.
+* Precision model ("mode"): "exact" keeps the rotated q and k in float64.
+  "bf16_operands" rounds the rotated q and k once to bf16
+  (round-to-nearest-even), as any kernel that feeds bf16 matrix units must;
+  gradients pass straight through that rounding. Everything else is float64
+  in both modes.
+"""
+
+import numpy as np
+
+MODES = ("exact", "bf16_operands")
+
+
+# --------------------------------------------------------------------------
+# bf16 helpers
+# --------------------------------------------------------------------------
+
+def bf16_bits_to_f64(bits):
+    """bf16 bit patterns (uint16) -> float64, exactly (a bf16 value is the
+    float32 whose upper 16 bits are the pattern)."""
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def round_to_bf16(x):
+    """Round float64 values to the nearest bf16 value (ties to even), returned
+    as float64. bf16 has 8 significant bits and float32's exponent range:
+    the grid spacing at |x| in [2^e, 2^(e+1)) is 2^(e-7), never finer than the
+    subnormal spacing 2^-133. Magnitudes that round past the largest finite
+    bf16 become infinities; NaN stays NaN."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.array(x, copy=True)
+    finite = np.isfinite(x) & (x != 0.0)
+    xf = x[finite]
+    _, e = np.frexp(xf)            # xf = m * 2^e with 0.5 <= |m| < 1
+    e = np.maximum(e, -125)        # below 2^-126 the spacing stays 2^-133
+    spacing = np.ldexp(1.0, e - 8)
+    r = np.rint(xf / spacing) * spacing   # np.rint rounds halves to even
+    max_bf16 = float(np.ldexp(255.0, 120))  # (2 - 2^-7) * 2^127
+    r = np.where(np.abs(r) > max_bf16, np.copysign(np.inf, xf), r)
+    out[finite] = r
+    return out
+
+
+# --------------------------------------------------------------------------
+# rotary position embedding
+# --------------------------------------------------------------------------
+
+def rope_frequencies(head_dim, base):
+    """theta_j = base^(-2j/d) for j in [0, d/2), float64. base == 0 means the
+    embedding is switched off (returns None)."""
+    if head_dim % 2:
+        raise ValueError("head_dim must be even for rotary embedding")
+    if base == 0:
+        return None
+    j = np.arange(head_dim // 2, dtype=np.float64)
+    return np.power(float(base), -2.0 * j / head_dim)
+
+
+def rope_rotate(x, positions, base, inverse=False):
+    """Rotate the last axis of x (length d) by the position angles.
+
+    Half-split pairing: coordinate j pairs with coordinate j + d/2, and the
+    pair (x_j, x_{j+d/2}) is turned by the angle a = p * theta_j:
+        x~_j       = x_j cos a - x_{j+d/2} sin a
+        x~_{j+d/2} = x_{j+d/2} cos a + x_j sin a
+    inverse=True applies the transpose (rotation by -a), which is what the
+    gradient of a rotated vector passes back to the unrotated one.
+    x has shape [L, ..., d]; positions has shape [L]."""
+    x = np.asarray(x, dtype=np.float64)
+    theta = rope_frequencies(x.shape[-1], base)
+    if theta is None:
+        return x.copy()
+    half = x.shape[-1] // 2
+    ang = np.asarray(positions, dtype=np.float64)[:, None] * theta[None, :]
+    cos = np.cos(ang)
+    sin = -np.sin(ang) if inverse else np.sin(ang)
+    shape = (x.shape[0],) + (1,) * (x.ndim - 2) + (half,)
+    cos = cos.reshape(shape)
+    sin = sin.reshape(shape)
+    lo = x[..., :half]
+    hi = x[..., half:]
+    out = np.empty_like(x)
+    out[..., :half] = lo * cos - hi * sin
+    out[..., half:] = hi * cos + lo * sin
+    return out
+
+
+def _rotated_operands(q, k, base, mode):
+    if mode not in MODES:
+        raise ValueError("mode must be one of %r" % (MODES,))
+    pos = np.arange(q.shape[0], dtype=np.float64)  # 0-based per sequence
+    qr = rope_rotate(q, pos, base)
+    kr = rope_rotate(k, pos, base)
+    if mode == "bf16_operands":
+        qr = round_to_bf16(qr)
+        kr = round_to_bf16(kr)
+    return pos, qr, kr
+
+
+# --------------------------------------------------------------------------
+# one (sequence, head) slice
+# --------------------------------------------------------------------------
+
+def attention_forward_slice(q, k, v, scale, base, mode="bf16_operands"):
+    """Forward attention of one sequence and one head.
+
+    q, k, v: [L, d] float64 (pre-rotation q and k). Returns
+      O   [L, d]: O_i = sum_j P_ij v_j,
+      LSE [L]   : LSE_i = log sum_j exp(S_ij) (natural log, scale included),
+    with S_ij = scale * (q~_i . k~_j) and P_ij = exp(S_ij - LSE_i).
+    The maximum is subtracted before exponentiating, which changes nothing
+    mathematically and keeps exp() finite."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    L = q.shape[0]
+    if L == 0:
+        return np.zeros_like(v), np.zeros((0,), np.float64)
+    _, qr, kr = _rotated_operands(q, k, base, mode)
+    S = float(scale) * (qr @ kr.T)
+    m = S.max(axis=1)
+    lse = m + np.log(np.exp(S - m[:, None]).sum(axis=1))
+    P = np.exp(S - lse[:, None])
+    return P @ v, lse
+
+
+def attention_backward_slice(q, k, v, do, scale, base, mode="bf16_operands",
+                             return_intermediates=False):
+    """Gradients of sum(dO * O) for one sequence and one head.
+
+    With P from the forward definition:
+      dV_j  = sum_i P_ij dO_i
+      dP_ij = dO_i . v_j
+      D_i   = sum_j P_ij dP_ij
+      dS_ij = P_ij (dP_ij - D_i)
+      dq~_i = scale * sum_j dS_ij k~_j
+      dk~_j = scale * sum_i dS_ij q~_i
+      dq_i  = R(-p_i) dq~_i,   dk_j = R(-p_j) dk~_j
+    Returns (dq, dk, dv), each [L, d]; with return_intermediates also a dict
+    of P, dS, D, LSE and the rotated-space gradients."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    do = np.asarray(do, np.float64)
+    L = q.shape[0]
+    if L == 0:
+        z = np.zeros_like(q)
+        out = (z, z.copy(), z.copy())
+        return out + ({},) if return_intermediates else out
+    pos, qr, kr = _rotated_operands(q, k, base, mode)
+    s = float(scale)
+    S = s * (qr @ kr.T)
+    m = S.max(axis=1)
+    lse = m + np.log(np.exp(S - m[:, None]).sum(axis=1))
+    P = np.exp(S - lse[:, None])
+    dv = P.T @ do
+    dP = do @ v.T
+    D = (P * dP).sum(axis=1)
+    dS = P * (dP - D[:, None])
+    dqr = s * (dS @ kr)
+    dkr = s * (dS.T @ qr)
+    dq = rope_rotate(dqr, pos, base, inverse=True)
+    dk = rope_rotate(dkr, pos, base, inverse=True)
+    if return_intermediates:
+        return dq, dk, dv, dict(P=P, dS=dS, D=D, LSE=lse, dq_rot=dqr,
+                                dk_rot=dkr, q_rot=qr, k_rot=kr)
+    return dq, dk, dv
+
+
+# --------------------------------------------------------------------------
+# packed batches
+# --------------------------------------------------------------------------
+
+def _check_packed(q, cu_seqlens):
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    if cu.ndim != 1 or cu.size < 2 or cu[0] != 0 or np.any(np.diff(cu) < 0):
+        raise ValueError("cu_seqlens must start at 0 and be nondecreasing")
+    if cu[-1] != q.shape[0]:
+        raise ValueError("cu_seqlens[-1] must equal the token count")
+    return cu
+
+
+def forward(q, k, v, cu_seqlens, scale, rope_base, mode="bf16_operands",
+            seqs=None, heads=None):
+    """Packed forward. q, k, v: [T, H, d] float64. Returns O [T, H, d] and
+    LSE [H, T]. Only the listed sequences / heads are computed when seqs /
+    heads are given (for sampled checks at large sizes); other entries are
+    NaN."""
+    cu = _check_packed(q, cu_seqlens)
+    T, H, d = q.shape
+    O = np.full((T, H, d), np.nan)
+    LSE = np.full((H, T), np.nan)
+    seqs = range(cu.size - 1) if seqs is None else seqs
+    heads = range(H) if heads is None else heads
+    for b in seqs:
+        a, e = int(cu[b]), int(cu[b + 1])
+        for h in heads:
+            o, lse = attention_forward_slice(q[a:e, h], k[a:e, h], v[a:e, h],
+                                             scale, rope_base, mode)
+            O[a:e, h] = o
+            LSE[h, a:e] = lse
+    return O, LSE
+
+
+def backward(q, k, v, do, cu_seqlens, scale, rope_base, mode="bf16_operands",
+             seqs=None, heads=None):
+    """Packed backward. Returns dq, dk, dv, each [T, H, d] (NaN where not
+    computed when seqs / heads restrict the work)."""
+    cu = _check_packed(q, cu_seqlens)
+    T, H, d = q.shape
+    dq = np.full((T, H, d), np.nan)
+    dk = np.full((T, H, d), np.nan)
+    dv = np.full((T, H, d), np.nan)
+    seqs = range(cu.size - 1) if seqs is None else seqs
+    heads = range(H) if heads is None else heads
+    for b in seqs:
+        a, e = int(cu[b]), int(cu[b + 1])
+        for h in heads:
+            g = attention_backward_slice(q[a:e, h], k[a:e, h], v[a:e, h],
+                                         do[a:e, h], scale, rope_base, mode)
+            dq[a:e, h], dk[a:e, h], dv[a:e, h] = g
+    return dq, dk, dv
+

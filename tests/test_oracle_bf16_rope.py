@@ -1,0 +1,143 @@
+"""Pins for the oracle's bf16 rounding and rotary embedding, against things
+other than the oracle itself: torch's float32 -> bf16 conversion, the
+complex-number form of the rotation, closed forms and invariants."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+
+def test_bf16_bits_known_patterns():
+    bits = np.array([0x3F80, 0xC000, 0x0000, 0x8000, 0x7F80, 0xFF80, 0x3E80,
+                     0x0001, 0x7F7F], dtype=np.uint16)
+    got = oracle.bf16_bits_to_f64(bits)
+    want = [1.0, -2.0, 0.0, -0.0, np.inf, -np.inf, 0.25, 2.0 ** -133,
+            255.0 * 2.0 ** 120]
+    np.testing.assert_array_equal(got, np.array(want))
+
+
+def test_round_to_bf16_matches_torch_on_float32_values():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([
+        rng.standard_normal(20000) * 10.0 ** rng.integers(-6, 6, 20000),
+        rng.standard_normal(2000) * 1e-39,          # float32 subnormal range
+        np.clip(rng.standard_normal(2000), -3, 3) * 1e38,  # near the top
+    ]).astype(np.float32)
+    want = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    got = oracle.round_to_bf16(x.astype(np.float64))
+    np.testing.assert_array_equal(got, want)
+
+
+def test_round_to_bf16_ties_to_even():
+    one = 1.0
+    cases = {
+        one + 2.0 ** -8: 1.0,                     # halfway, even is 1.0
+        one + 3 * 2.0 ** -8: one + 2.0 ** -6,     # halfway, even is 1+2^-6
+        one + 2.0 ** -8 + 2.0 ** -30: one + 2.0 ** -7,
+        -(one + 2.0 ** -8): -1.0,
+        255.5 * 2.0 ** 120: np.inf,               # tie past the largest finite
+    }
+    for x, want in cases.items():
+        assert oracle.round_to_bf16(np.array([x]))[0] == want, x
+    assert np.isnan(oracle.round_to_bf16(np.array([np.nan]))[0])
+
+
+def test_rope_frequencies_closed_form():
+    np.testing.assert_allclose(oracle.rope_frequencies(4, 10000.0), [1.0, 0.01],
+                               rtol=1e-15)
+    th = oracle.rope_frequencies(64, 10000.0)
+    assert th[0] == 1.0
+    np.testing.assert_allclose(th[16], 0.01, rtol=1e-14)   # 10000^(-32/64)
+    np.testing.assert_allclose(th[31], 10000.0 ** (-62 / 64), rtol=1e-14)
+    assert oracle.rope_frequencies(8, 0.0) is None
+
+
+def _rope_complex(x, pos, base):
+    """Independent form: pair (x_j, x_{j+d/2}) is the complex number
+    x_j + i x_{j+d/2}, multiplied by exp(i p base^(-2j/d))."""
+    d = x.shape[-1]
+    h = d // 2
+    z = x[..., :h] + 1j * x[..., h:]
+    j = np.arange(h)
+    w = np.exp(1j * np.outer(pos, base ** (-2.0 * j / d)))
+    w = w.reshape((x.shape[0],) + (1,) * (x.ndim - 2) + (h,))
+    r = z * w
+    return np.concatenate([r.real, r.imag], axis=-1)
+
+
+@pytest.mark.parametrize("d", [2, 4, 16, 64, 128])
+def test_rope_matches_complex_multiplication(d):
+    rng = np.random.default_rng(d)
+    x = rng.standard_normal((50, 3, d))
+    pos = rng.integers(0, 8192, 50).astype(np.float64)
+    got = oracle.rope_rotate(x, pos, 10000.0)
+    np.testing.assert_allclose(got, _rope_complex(x, pos, 10000.0), atol=1e-12)
+
+
+def test_rope_position_zero_is_identity_and_base_zero_is_off():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((4, 2, 32))
+    np.testing.assert_array_equal(oracle.rope_rotate(x, np.zeros(4), 10000.0), x)
+    np.testing.assert_array_equal(
+        oracle.rope_rotate(x, np.arange(4) * 100.0, 0.0), x)
+
+
+def test_rope_d2_rotates_by_position_radians():
+    x = np.array([[1.0, 0.0], [0.0, 1.0], [3.0, 4.0]])
+    pos = np.array([np.pi / 2, np.pi, 1.0])
+    got = oracle.rope_rotate(x, pos, 10000.0)   # d=2: theta_0 = 1
+    np.testing.assert_allclose(got[0], [0.0, 1.0], atol=1e-15)
+    np.testing.assert_allclose(got[1], [0.0, -1.0], atol=1e-15)
+    c, s = np.cos(1.0), np.sin(1.0)
+    np.testing.assert_allclose(got[2], [3 * c - 4 * s, 4 * c + 3 * s], atol=1e-15)
+
+
+def test_rope_is_orthogonal_and_inverse_is_transpose():
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((64, 1, 64))
+    y = rng.standard_normal((64, 1, 64))
+    pos = np.arange(64) * 37.0
+    rx = oracle.rope_rotate(x, pos, 10000.0)
+    np.testing.assert_allclose(np.linalg.norm(rx, axis=-1),
+                               np.linalg.norm(x, axis=-1), rtol=1e-13)
+    back = oracle.rope_rotate(rx, pos, 10000.0, inverse=True)
+    np.testing.assert_allclose(back, x, atol=1e-12)
+    ry = oracle.rope_rotate(y, pos, 10000.0, inverse=True)
+    np.testing.assert_allclose((rx * y).sum(-1), (x * ry).sum(-1), atol=1e-11)
+
+
+def test_rope_scores_depend_only_on_relative_position():
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((1, 64))
+    k = rng.standard_normal((1, 64))
+    base = 10000.0
+    ref = None
+    for shift in [0.0, 5.0, 1000.0, 8000.0]:
+        qp = oracle.rope_rotate(q, np.array([shift + 17.0]), base)
+        kt = oracle.rope_rotate(k, np.array([shift + 3.0]), base)
+        val = float((qp * kt).sum())
+        ref = val if ref is None else ref
+        assert abs(val - ref) < 1e-10
+    qp = oracle.rope_rotate(q, np.array([18.0]), base)
+    kt = oracle.rope_rotate(k, np.array([3.0]), base)
+    assert abs(float((qp * kt).sum()) - ref) > 1e-6   # offset matters
+
+
+def test_half_split_equals_interleaved_under_permutation():
+    rng = np.random.default_rng(4)
+    d = 16
+    x = rng.standard_normal((10, d))
+    pos = np.arange(10) * 3.0
+    # interleaved pairing, written with complex pairs (x_2j, x_2j+1)
+    z = x[:, 0::2] + 1j * x[:, 1::2]
+    j = np.arange(d // 2)
+    r = z * np.exp(1j * np.outer(pos, 10000.0 ** (-2.0 * j / d)))
+    inter = np.empty_like(x)
+    inter[:, 0::2], inter[:, 1::2] = r.real, r.imag
+    perm = np.concatenate([np.arange(0, d, 2), np.arange(1, d, 2)])
+    half = oracle.rope_rotate(x[:, perm], pos, 10000.0)
+    back = np.empty_like(half)
+    back[:, perm] = half
+    np.testing.assert_allclose(back, inter, atol=1e-12)
