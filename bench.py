@@ -1,0 +1,188 @@
+"""Benchmark of the varlen RoPE attention hot path on one MI355X.
+
+A step is one pass of the whole path over one packed batch held in HBM:
+plan (varlen schedule + rotary table), forward (O, LSE), backward dq pass
+(with D = rowsum(dO*O) and the inverse-rotation finalize) and dk/dv pass.
+The default workload is the ESM-2-650M-shaped dense batch: 16 sequences of
+1024 tokens, 20 heads, head dim 64, bf16, RoPE base 10000.
+
+Prints ONE JSON line. `value` is counted TFLOP/s of forward + backward
+(forward 4*sum(L^2)*H*d, backward 2.5x that), `roofline` describes the
+dominant kernel (timed with events on the stream it is launched on), and
+`cpu_baseline` times the float64 oracle on a bounded sample on the host.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload esm2_650m]
+                    [--no-cpu-baseline] [--cpu-seconds 15]
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="esm2_650m")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0)
+    return p.parse_args()
+
+
+def cpu_baseline(inp, budget_s):
+    """Times the float64 oracle (forward + backward, bf16-operand mode) on
+    (sequence, head) slices of the same workload until about budget_s of CPU
+    work, and scales to counted TFLOP/s."""
+    import oracle
+    from protein_language_model_amd import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    q, k, v, do = (oracle.bf16_bits_to_f64(inp[n]) for n in ("q", "k", "v", "do"))
+    cu = inp["cu_seqlens"]
+    done, flops = [], 0.0
+    t0 = time.perf_counter()
+    for b in range(len(cu) - 1):
+        a, e = int(cu[b]), int(cu[b + 1])
+        for h in range(inp["H"]):
+            oracle.attention_forward_slice(q[a:e, h], k[a:e, h], v[a:e, h], inp["scale"],
+                                           inp["rope_base"])
+            oracle.attention_backward_slice(q[a:e, h], k[a:e, h], v[a:e, h], do[a:e, h],
+                                            inp["scale"], inp["rope_base"])
+            f, bwd = W.counted_flops([e - a], 1, inp["d"])
+            flops += f + bwd
+            done.append((b, h))
+            if time.perf_counter() - t0 > budget_s:
+                break
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": "float64 oracle forward+backward on %d (sequence, head) slices of %s "
+                      "(%.1f s, counted flops scaled to TFLOP/s)" % (len(done), inp["name"], dt)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build runs the attention hot path on a "
+              "single MI355X (no sharding, no collectives); --gpus %d is not supported"
+              % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from protein_language_model_amd import esm_attn as E
+    from protein_language_model_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    inp = W.make_inputs(args.workload)
+    T, H, d, B = inp["T"], inp["H"], inp["d"], len(inp["lengths"])
+    maxL = max(inp["lengths"])
+    scale, base = inp["scale"], inp["rope_base"]
+
+    def dev_bf16(bits):
+        return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    q, k, v, do = (dev_bf16(inp[n]) for n in ("q", "k", "v", "do"))
+    cu = torch.from_numpy(inp["cu_seqlens"]).to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((H, T), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    drow = torch.empty((H, T), dtype=torch.float32, device=dev)
+    plan = torch.empty(E.esm_attn_plan_bytes(B, T, maxL, H, d), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        E.esm_attn_plan(cu, T, maxL, H, d, base, plan=plan)
+        if ev is not None:
+            ev[1].record(stream)
+        E.esm_attn_fwd_planned(q, k, v, B, maxL, plan, scale, base, out=o, lse=lse)
+        if ev is not None:
+            ev[2].record(stream)
+        E.esm_attn_bwd_planned(q, k, v, o, do, lse, B, maxL, plan, scale, base, dq=dq,
+                               drow=drow, passes=E.PASS_DQ)
+        if ev is not None:
+            ev[3].record(stream)
+        E.esm_attn_bwd_planned(q, k, v, o, do, lse, B, maxL, plan, scale, base, dk=dk, dv=dv,
+                               drow=drow, passes=E.PASS_DKV)
+        if ev is not None:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    names = ["plan", "fwd", "bwd_dq", "bwd_dkv"]
+    per = {n: [] for n in names}
+    for ev in events:
+        for j, n in enumerate(names):
+            per[n].append(ev[j].elapsed_time(ev[j + 1]) * 1e3)  # us
+    avg = {n: float(np.mean(x)) for n, x in per.items()}
+    step_ms = wall / args.steps * 1e3
+
+    fwd_f, bwd_f = W.counted_flops(inp["lengths"], H, d)
+    total_f = fwd_f + bwd_f
+    tflops = total_f / (step_ms * 1e-3) / 1e12
+    s2 = float(sum(L * L for L in inp["lengths"]))
+    # algorithmic flops of each kernel: the method's matrix products it runs
+    kernel_flops = {"fwd": 4 * s2 * H * d,            # S = QK^T, O = PV
+                    "bwd_dq": 6 * s2 * H * d,         # S, dP = dO V^T, dQ = dS K
+                    "bwd_dkv": 8 * s2 * H * d}        # S, dP, dV = P^T dO, dK = dS^T Q
+    dom = max(kernel_flops, key=lambda n: avg[n])
+    achieved = kernel_flops[dom] / (avg[dom] * 1e-6) / 1e12
+
+    out = {
+        "metric": "attention fwd+bwd TFLOP/s and % of bf16 MFMA peak; tokens/s (varlen)",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 activations, packed varlen batch)",
+        "config": {"workload": "%s: %d sequences, %d tokens, H=%d, d=%d, RoPE base %g"
+                               % (inp["name"], B, T, H, d, base),
+                   "global_batch": B, "seq_len": maxL, "tokens": T,
+                   "parallelism": "single GPU"},
+        "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "tokens_per_s": round(T / (step_ms * 1e-3), 1),
+        "kernels_us": {n: round(x, 2) for n, x in avg.items()},
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

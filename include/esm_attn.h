@@ -1,0 +1,209 @@
+/*
+ * esm_attn.h -- C ABI of the MI355X (gfx950) attention library for ESM-2-style
+ * protein language model training: bidirectional multi-head self-attention
+ * with rotary position embedding over packed variable-length sequences,
+ * forward and backward.
+ *
+ * What is computed (for every sequence b and head h):
+ *   ESM-2 is a BERT-style model ("BioNeMo Framework: a modular,
+ *   high-performance library for AI model development in drug discovery"
+ *   review page, Abstract and "proposed method"), so a token attends to all
+ *   tokens of its own sequence and to nothing else. Sequences are packed back
+ *   to back by the size-aware bucket batching of the same page, with no
+ *   padding between them. Inputs and outputs are BF16 (BioNeMo Recipes hub
+ *   page, multi-precision training section); products accumulate in FP32
+ *   (BioNeMo blog, section 2.3).
+ *
+ *   p          = t - cu_seqlens[b]          position of token t, 0-based per sequence
+ *   theta_j    = rope_base^(-2j/d)          j in [0, d/2)
+ *   x~         = R(p) x: (x_j, x_{j+d/2}) turned by the angle p*theta_j
+ *                (rotary position embedding, half-split pairing; rope_base = 0
+ *                switches it off)
+ *   S_ij       = softmax_scale * (q~_i . k~_j)       i, j in the same sequence
+ *   LSE_i      = ln sum_j exp(S_ij)
+ *   P_ij       = exp(S_ij - LSE_i)
+ *   O_i        = sum_j P_ij v_j
+ * and, given dO, the gradients of sum(dO * O):
+ *   dv_j = sum_i P_ij dO_i
+ *   dS_ij = P_ij (dO_i . v_j - D_i),  D_i = dO_i . O_i
+ *   dq_i = R(p_i)^T (softmax_scale * sum_j dS_ij k~_j)
+ *   dk_j = R(p_j)^T (softmax_scale * sum_i dS_ij q~_i)
+ * q~ and k~ are rounded once to bf16 before the products (they are operands
+ * of bf16 matrix instructions); everything else accumulates in fp32.
+ *
+ * Layouts
+ *   q, k, v, o, d_o, dq, dk, dv : bf16 bit patterns (uint16_t), [T][H][d],
+ *                                 row-major, d fastest; token-major packing
+ *   lse                         : float, [H][T], natural log
+ *   cu_seqlens                  : int32_t, [batch + 1], DEVICE memory
+ *   head_dim d                  : 16, 32, 64 or 128
+ *
+ * Ownership and execution
+ *   The caller allocates every buffer (inputs, outputs, workspace); the library
+ *   never allocates or frees memory and keeps no pointer after a call returns.
+ *   Calls are enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *   return without waiting; there is no host-device synchronisation and no
+ *   device read on the host, so the calls can be captured in a HIP graph.
+ *   Workspace contents are undefined before and after a call; concurrent calls
+ *   on different streams need different workspaces. Outputs must not alias
+ *   inputs or each other.
+ *
+ * Errors
+ *   Problems visible on the host are reported before anything is enqueued and
+ *   leave every output untouched: null pointers (allowed when total_tokens is
+ *   0), pointers not 16-byte aligned, batch < 1, num_heads < 1,
+ *   total_tokens < 0, max_seqlen < 0 or > 65536, head_dim not in
+ *   {16, 32, 64, 128} (ESM_ATTN_ERR_UNSUPPORTED), total_tokens*num_heads*
+ *   head_dim >= 2^31 (ESM_ATTN_ERR_UNSUPPORTED), non-finite softmax_scale,
+ *   rope_base negative or non-finite, workspace smaller than the matching
+ *   *_workspace_bytes() result. A failed kernel launch returns
+ *   ESM_ATTN_ERR_HIP. Faults during execution surface at the caller's next
+ *   synchronisation, as for any HIP work.
+ *   The library cannot check the contents of the device-resident cu_seqlens
+ *   without a synchronisation; the caller guarantees cu_seqlens[0] = 0,
+ *   nondecreasing entries, cu_seqlens[batch] = total_tokens and every length
+ *   <= max_seqlen (esm_attn_check_cu_seqlens_host checks a host copy).
+ *   Kernels clamp lengths to [0, max_seqlen] and token indices to
+ *   [0, total_tokens), so a bad cu_seqlens gives wrong values, never
+ *   out-of-bounds accesses. Zero-length sequences are legal; total_tokens = 0
+ *   enqueues nothing and returns ESM_ATTN_OK.
+ */
+#ifndef ESM_ATTN_H
+#define ESM_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ESM_ATTN_ABI_VERSION 1
+
+typedef int32_t esm_attn_status_t;
+#define ESM_ATTN_OK 0
+#define ESM_ATTN_ERR_INVALID_ARGUMENT 1
+#define ESM_ATTN_ERR_UNSUPPORTED 2
+#define ESM_ATTN_ERR_WORKSPACE_TOO_SMALL 3
+#define ESM_ATTN_ERR_HIP 4
+
+/* ESM_ATTN_ABI_VERSION of the built library. */
+int32_t esm_attn_abi_version(void);
+
+/* Static, never-NULL description of a status code (unknown codes included). */
+const char* esm_attn_status_string(esm_attn_status_t status);
+
+/* Workspace bytes that esm_attn_fwd / esm_attn_bwd need for these sizes
+ * (a pure host computation; 0 for arguments the calls would reject). The
+ * workspace holds the rotary cos/sin table, the work-item schedule and, for
+ * the backward, the row sums D = rowsum(dO * O), fp32 [H][T]. */
+size_t esm_attn_fwd_workspace_bytes(int32_t batch, int32_t total_tokens,
+                                    int32_t max_seqlen, int32_t num_heads,
+                                    int32_t head_dim);
+size_t esm_attn_bwd_workspace_bytes(int32_t batch, int32_t total_tokens,
+                                    int32_t max_seqlen, int32_t num_heads,
+                                    int32_t head_dim);
+
+/* Forward. q, k, v: pre-rotation inputs, bf16 [T][H][d] (device).
+ * cu_seqlens: int32 [batch+1] (device). softmax_scale: usually 1/sqrt(d);
+ * any finite value. rope_base: usually 10000; 0 = no rotary embedding.
+ * Writes o (bf16 [T][H][d]) and lse (fp32 [H][T], natural log). */
+esm_attn_status_t esm_attn_fwd(
+    const uint16_t* q, const uint16_t* k, const uint16_t* v,
+    const int32_t* cu_seqlens,
+    int32_t batch, int32_t total_tokens, int32_t max_seqlen,
+    int32_t num_heads, int32_t head_dim,
+    float softmax_scale, float rope_base,
+    uint16_t* o, float* lse,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward. q, k, v as given to the forward; o and lse as it returned them;
+ * d_o: gradient of the loss with respect to o, bf16 [T][H][d].
+ * Writes dq, dk, dv (bf16 [T][H][d]): gradients with respect to the
+ * pre-rotation q and k and to v. */
+esm_attn_status_t esm_attn_bwd(
+    const uint16_t* q, const uint16_t* k, const uint16_t* v,
+    const uint16_t* o, const uint16_t* d_o, const float* lse,
+    const int32_t* cu_seqlens,
+    int32_t batch, int32_t total_tokens, int32_t max_seqlen,
+    int32_t num_heads, int32_t head_dim,
+    float softmax_scale, float rope_base,
+    uint16_t* dq, uint16_t* dk, uint16_t* dv,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- plan / execute split ------------------------------------------------
+ * esm_attn_fwd and esm_attn_bwd each build a plan (the work-item schedule for
+ * cu_seqlens and the rotary cos/sin table) in their workspace before their
+ * kernels run. A caller that runs the forward and backward of one batch can
+ * build the plan once and pass it to both planned calls instead.
+ *
+ * esm_attn_plan enqueues the two planning kernels; the plan buffer is device
+ * memory of esm_attn_plan_bytes() bytes, owned by the caller, valid for the
+ * sizes, cu_seqlens contents and rope_base it was built with, and read-only
+ * for the planned calls (several may use one plan, on one stream or after
+ * proper stream ordering). The planned calls do not read cu_seqlens; they
+ * take the same sizes, scale and rope_base (a different rope_base than the
+ * plan's gives wrong values, not an error). */
+size_t esm_attn_plan_bytes(int32_t batch, int32_t total_tokens, int32_t max_seqlen,
+                           int32_t num_heads, int32_t head_dim);
+
+esm_attn_status_t esm_attn_plan(const int32_t* cu_seqlens, int32_t batch,
+                                int32_t total_tokens, int32_t max_seqlen,
+                                int32_t num_heads, int32_t head_dim, float rope_base,
+                                void* plan, size_t plan_bytes, void* stream);
+
+/* Forward kernel only (esm_attn_fwd minus planning). */
+esm_attn_status_t esm_attn_fwd_planned(
+    const uint16_t* q, const uint16_t* k, const uint16_t* v,
+    int32_t batch, int32_t total_tokens, int32_t max_seqlen,
+    int32_t num_heads, int32_t head_dim,
+    float softmax_scale, float rope_base,
+    uint16_t* o, float* lse,
+    const void* plan, size_t plan_bytes, void* stream);
+
+/* Backward passes only. drow: caller-provided fp32 [H][T] buffer for the row
+ * sums D = rowsum(dO * O). passes is a bit mask: ESM_ATTN_PASS_DQ runs the
+ * dq pass (writes dq and drow), ESM_ATTN_PASS_DKV the dk/dv pass (reads drow,
+ * writes dk and dv); both bits give the full backward. Running the dk/dv pass
+ * alone requires a completed dq pass of the same inputs. Pointers a pass does
+ * not use may be NULL. */
+#define ESM_ATTN_PASS_DQ 1
+#define ESM_ATTN_PASS_DKV 2
+esm_attn_status_t esm_attn_bwd_planned(
+    const uint16_t* q, const uint16_t* k, const uint16_t* v,
+    const uint16_t* o, const uint16_t* d_o, const float* lse,
+    int32_t batch, int32_t total_tokens, int32_t max_seqlen,
+    int32_t num_heads, int32_t head_dim,
+    float softmax_scale, float rope_base,
+    uint16_t* dq, uint16_t* dk, uint16_t* dv, float* drow, int32_t passes,
+    const void* plan, size_t plan_bytes, void* stream);
+
+/* Host-only check of a HOST copy of cu_seqlens: cu[0] = 0, nondecreasing,
+ * cu[batch] = total_tokens, every length <= max_seqlen. Returns ESM_ATTN_OK or
+ * ESM_ATTN_ERR_INVALID_ARGUMENT. Reads batch+1 entries; enqueues nothing. */
+esm_attn_status_t esm_attn_check_cu_seqlens_host(const int32_t* cu_host,
+                                                 int32_t batch,
+                                                 int32_t total_tokens,
+                                                 int32_t max_seqlen);
+
+/* Host-only model of the device work-item schedule, for tests and tools.
+ * Given a HOST copy of cu_seqlens, builds the schedule the kernels use for
+ * items of `block_rows` rows (sequences longest first; the items of one
+ * (sequence, head) pair on slots congruent modulo 8, i.e. on one of the
+ * chip's eight XCDs under round-robin dispatch) and decodes every launched
+ * slot into items[4*s .. 4*s+3] = {sequence start, length, head, block} or
+ * {-1, -1, -1, -1} for an idle slot. *n_slots receives the launch size (an
+ * upper bound the host computes without reading cu_seqlens); items must hold
+ * 4 * items_capacity ints. Returns ESM_ATTN_ERR_INVALID_ARGUMENT if the
+ * capacity is too small or an argument is out of range. */
+esm_attn_status_t esm_attn_schedule_host(const int32_t* cu_host, int32_t batch,
+                                         int32_t total_tokens, int32_t max_seqlen,
+                                         int32_t num_heads, int32_t block_rows,
+                                         int32_t* items, int32_t items_capacity,
+                                         int32_t* n_slots);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ESM_ATTN_H */

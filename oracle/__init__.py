@@ -15,6 +15,7 @@ from .attention import (  # noqa: F401
     round_to_bf16,
     rope_frequencies,
     rope_rotate,
+    rope_rotate_f32,
     attention_forward_slice,
     attention_backward_slice,
     forward,

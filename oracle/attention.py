@@ -26,10 +26,14 @@ Sources and readings
   frequencies theta_j = base^(-2j/d), positions counted from 0 at the start
   of each sequence.
 * Precision model ("mode"): "exact" keeps the rotated q and k in float64.
-  "bf16_operands" rounds the rotated q and k once to bf16
-  (round-to-nearest-even), as any kernel that feeds bf16 matrix units must;
-  gradients pass straight through that rounding. Everything else is float64
-  in both modes.
+  "bf16_operands" rounds the rotated q and k to bf16 (round-to-nearest-even),
+  as any kernel that feeds bf16 matrix units must. That rounding is a
+  quantisation decided by floating point, so it is taken in the pages'
+  arithmetic precision, float32 (BF16 storage with FP32 arithmetic): cos and
+  sin are rounded to float32 and x c - y s, y c + x s are evaluated in float32
+  with every product and sum rounded (no fused multiply-add), then rounded
+  to bf16. Gradients pass straight through that rounding. Everything else is
+  float64 in both modes.
 """
 
 import numpy as np
@@ -112,15 +116,41 @@ def rope_rotate(x, positions, base, inverse=False):
     return out
 
 
+def rope_rotate_f32(x, positions, base):
+    """The rotation of rope_rotate evaluated in float32: angles p * theta_j in
+    float64, cos and sin rounded to float32, then
+        x~_j       = fl(fl(x_j c) - fl(x_{j+d/2} s))
+        x~_{j+d/2} = fl(fl(x_{j+d/2} c) + fl(x_j s))
+    with fl() rounding to float32 (numpy float32 arithmetic, no fused
+    multiply-add). x must hold float32-representable values. Returns float64
+    holding the float32 results."""
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    theta = rope_frequencies(x32.shape[-1], base)
+    if theta is None:
+        return x32.astype(np.float64)
+    half = x32.shape[-1] // 2
+    ang = np.asarray(positions, dtype=np.float64)[:, None] * theta[None, :]
+    shape = (x32.shape[0],) + (1,) * (x32.ndim - 2) + (half,)
+    cos = np.cos(ang).astype(np.float32).reshape(shape)
+    sin = np.sin(ang).astype(np.float32).reshape(shape)
+    lo = x32[..., :half]
+    hi = x32[..., half:]
+    out = np.empty_like(x32)
+    out[..., :half] = lo * cos - hi * sin
+    out[..., half:] = hi * cos + lo * sin
+    return out.astype(np.float64)
+
+
 def _rotated_operands(q, k, base, mode):
     if mode not in MODES:
         raise ValueError("mode must be one of %r" % (MODES,))
     pos = np.arange(q.shape[0], dtype=np.float64)  # 0-based per sequence
-    qr = rope_rotate(q, pos, base)
-    kr = rope_rotate(k, pos, base)
     if mode == "bf16_operands":
-        qr = round_to_bf16(qr)
-        kr = round_to_bf16(kr)
+        qr = round_to_bf16(rope_rotate_f32(q, pos, base))
+        kr = round_to_bf16(rope_rotate_f32(k, pos, base))
+    else:
+        qr = rope_rotate(q, pos, base)
+        kr = rope_rotate(k, pos, base)
     return pos, qr, kr
 
 

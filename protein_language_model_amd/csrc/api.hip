@@ -1,0 +1,325 @@
+// C-ABI entry points of libesm_attn.so: argument validation, workspace layout
+// and the launch sequence. Nothing here reads device memory or synchronises.
+#include <math.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "esm_attn.h"
+#include "prep.h"
+#include "schedule.h"
+
+namespace {
+
+using namespace esm;
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+  size_t rope = 0, sorted = 0, chunk = 0, items = 0, drow = 0, total = 0;
+  int64_t n_slots = 0;
+  int32_t n_chunks = 0;
+};
+
+bool head_dim_ok(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+// Scalar checks shared by the calls and the workspace queries.
+esm_attn_status_t check_sizes(int32_t B, int32_t T, int32_t maxL, int32_t H, int32_t d) {
+  if (B < 1 || H < 1 || T < 0 || maxL < 0) return ESM_ATTN_ERR_INVALID_ARGUMENT;
+  if (maxL > kMaxSeqlen) return ESM_ATTN_ERR_UNSUPPORTED;
+  if (!head_dim_ok(d)) return ESM_ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)T * H * d >= ((int64_t)1 << 31)) return ESM_ATTN_ERR_UNSUPPORTED;
+  if (schedule_num_chunks(B, H) + 1 >= ((int64_t)1 << 31)) return ESM_ATTN_ERR_UNSUPPORTED;
+  if (schedule_slot_bound(B, T, H, maxL, kItemRows) >= ((int64_t)1 << 31))
+    return ESM_ATTN_ERR_UNSUPPORTED;
+  return ESM_ATTN_OK;
+}
+
+Layout make_layout(int32_t B, int32_t T, int32_t maxL, int32_t H, int32_t d, bool bwd) {
+  Layout l;
+  l.n_chunks = (int32_t)schedule_num_chunks(B, H);
+  l.n_slots = schedule_slot_bound(B, T, H, maxL, kItemRows);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  l.rope = take((size_t)(maxL > 0 ? maxL : 1) * (d / 2) * sizeof(float2));
+  l.sorted = take((size_t)B * sizeof(int32_t));
+  l.chunk = take((size_t)(l.n_chunks + 1) * sizeof(int32_t));
+  l.items = take((size_t)(l.n_slots > 0 ? l.n_slots : 1) * sizeof(Item));
+  if (bwd) l.drow = take((size_t)T * H * sizeof(float));
+  l.total = off;
+  return l;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+esm_attn_status_t check_scalars(float scale, float rope_base) {
+  if (!isfinite(scale)) return ESM_ATTN_ERR_INVALID_ARGUMENT;
+  if (!isfinite(rope_base) || rope_base < 0.f) return ESM_ATTN_ERR_INVALID_ARGUMENT;
+  return ESM_ATTN_OK;
+}
+
+void fill_common(AttnArgs* a, int32_t T, int32_t H, float scale) {
+  a->T = T;
+  a->H = H;
+  a->scale = scale;
+  a->scale_abs = fabsf(scale);
+  a->q_sign = scale < 0.f ? -1.f : 1.f;
+  a->c = fabsf(scale) * kLog2e;
+}
+
+esm_attn_status_t run_prep(const int32_t* cu, int32_t B, int32_t T, int32_t maxL, int32_t H,
+                           int32_t d, float rope_base, const Layout& l, char* ws,
+                           hipStream_t st) {
+  PrepArgs p;
+  p.cu = cu;
+  p.B = B;
+  p.T = T;
+  p.H = H;
+  p.max_seqlen = maxL;
+  p.block = kItemRows;
+  p.head_dim = d;
+  p.sorted = reinterpret_cast<int32_t*>(ws + l.sorted);
+  p.chunk_base = reinterpret_cast<int32_t*>(ws + l.chunk);
+  p.n_chunks = l.n_chunks;
+  p.items = reinterpret_cast<Item*>(ws + l.items);
+  p.n_slots = l.n_slots;
+  p.rope = rope_base != 0.f ? reinterpret_cast<float2*>(ws + l.rope) : nullptr;
+  p.rope_base = rope_base;
+  return launch_prep(p, st) == hipSuccess ? ESM_ATTN_OK : ESM_ATTN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t esm_attn_abi_version(void) { return ESM_ATTN_ABI_VERSION; }
+
+const char* esm_attn_status_string(esm_attn_status_t s) {
+  switch (s) {
+    case ESM_ATTN_OK: return "esm_attn: success";
+    case ESM_ATTN_ERR_INVALID_ARGUMENT: return "esm_attn: invalid argument";
+    case ESM_ATTN_ERR_UNSUPPORTED: return "esm_attn: unsupported size or head_dim";
+    case ESM_ATTN_ERR_WORKSPACE_TOO_SMALL: return "esm_attn: workspace too small";
+    case ESM_ATTN_ERR_HIP: return "esm_attn: HIP launch failed";
+    default: return "esm_attn: unknown status";
+  }
+}
+
+size_t esm_attn_fwd_workspace_bytes(int32_t batch, int32_t total_tokens, int32_t max_seqlen,
+                                    int32_t num_heads, int32_t head_dim) {
+  if (check_sizes(batch, total_tokens, max_seqlen, num_heads, head_dim) != ESM_ATTN_OK) return 0;
+  return make_layout(batch, total_tokens, max_seqlen, num_heads, head_dim, false).total;
+}
+
+size_t esm_attn_bwd_workspace_bytes(int32_t batch, int32_t total_tokens, int32_t max_seqlen,
+                                    int32_t num_heads, int32_t head_dim) {
+  if (check_sizes(batch, total_tokens, max_seqlen, num_heads, head_dim) != ESM_ATTN_OK) return 0;
+  return make_layout(batch, total_tokens, max_seqlen, num_heads, head_dim, true).total;
+}
+
+size_t esm_attn_plan_bytes(int32_t batch, int32_t total_tokens, int32_t max_seqlen,
+                           int32_t num_heads, int32_t head_dim) {
+  return esm_attn_fwd_workspace_bytes(batch, total_tokens, max_seqlen, num_heads, head_dim);
+}
+
+esm_attn_status_t esm_attn_plan(const int32_t* cu_seqlens, int32_t batch, int32_t total_tokens,
+                                int32_t max_seqlen, int32_t num_heads, int32_t head_dim,
+                                float rope_base, void* plan, size_t plan_bytes, void* stream) {
+  esm_attn_status_t s = check_sizes(batch, total_tokens, max_seqlen, num_heads, head_dim);
+  if (s != ESM_ATTN_OK) return s;
+  if ((s = check_scalars(0.f, rope_base)) != ESM_ATTN_OK) return s;
+  if (total_tokens == 0 || max_seqlen == 0) return ESM_ATTN_OK;
+  if (cu_seqlens == nullptr || !aligned16(cu_seqlens) || plan == nullptr || !aligned16(plan))
+    return ESM_ATTN_ERR_INVALID_ARGUMENT;
+  const Layout l = make_layout(batch, total_tokens, max_seqlen, num_heads, head_dim, false);
+  if (plan_bytes < l.total) return ESM_ATTN_ERR_WORKSPACE_TOO_SMALL;
+  return run_prep(cu_seqlens, batch, total_tokens, max_seqlen, num_heads, head_dim, rope_base, l,
+                  static_cast<char*>(plan), reinterpret_cast<hipStream_t>(stream));
+}
+
+esm_attn_status_t esm_attn_fwd_planned(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                       int32_t batch, int32_t total_tokens, int32_t max_seqlen,
+                                       int32_t num_heads, int32_t head_dim, float softmax_scale,
+                                       float rope_base, uint16_t* o, float* lse, const void* plan,
+                                       size_t plan_bytes, void* stream) {
+  esm_attn_status_t s = check_sizes(batch, total_tokens, max_seqlen, num_heads, head_dim);
+  if (s != ESM_ATTN_OK) return s;
+  if ((s = check_scalars(softmax_scale, rope_base)) != ESM_ATTN_OK) return s;
+  if (total_tokens == 0) return ESM_ATTN_OK;
+  const void* ptrs[] = {q, k, v, o, lse, plan};
+  for (const void* p : ptrs)
+    if (p == nullptr || !aligned16(p)) return ESM_ATTN_ERR_INVALID_ARGUMENT;
+  const Layout l = make_layout(batch, total_tokens, max_seqlen, num_heads, head_dim, false);
+  if (plan_bytes < l.total) return ESM_ATTN_ERR_WORKSPACE_TOO_SMALL;
+  if (max_seqlen == 0) return ESM_ATTN_OK;  // every sequence is empty
+  const char* ws = static_cast<const char*>(plan);
+  AttnArgs a = {};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = o;
+  a.lse = lse;
+  a.rope = reinterpret_cast<const float2*>(ws + l.rope);
+  a.items = reinterpret_cast<const Item*>(ws + l.items);
+  fill_common(&a, total_tokens, num_heads, softmax_scale);
+  if (launch_fwd(head_dim, rope_base != 0.f, a, l.n_slots, reinterpret_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return ESM_ATTN_ERR_HIP;
+  return ESM_ATTN_OK;
+}
+
+esm_attn_status_t esm_attn_bwd_planned(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                       const uint16_t* o, const uint16_t* d_o, const float* lse,
+                                       int32_t batch, int32_t total_tokens, int32_t max_seqlen,
+                                       int32_t num_heads, int32_t head_dim, float softmax_scale,
+                                       float rope_base, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+                                       float* drow, int32_t passes, const void* plan,
+                                       size_t plan_bytes, void* stream) {
+  esm_attn_status_t s = check_sizes(batch, total_tokens, max_seqlen, num_heads, head_dim);
+  if (s != ESM_ATTN_OK) return s;
+  if ((s = check_scalars(softmax_scale, rope_base)) != ESM_ATTN_OK) return s;
+  if (passes < 1 || passes > (ESM_ATTN_PASS_DQ | ESM_ATTN_PASS_DKV))
+    return ESM_ATTN_ERR_INVALID_ARGUMENT;
+  if (total_tokens == 0) return ESM_ATTN_OK;
+  const bool pdq = passes & ESM_ATTN_PASS_DQ, pdkv = passes & ESM_ATTN_PASS_DKV;
+  const void* common[] = {q, k, v, lse, d_o, drow, plan};
+  for (const void* p : common)
+    if (p == nullptr || !aligned16(p)) return ESM_ATTN_ERR_INVALID_ARGUMENT;
+  if (pdq && (o == nullptr || !aligned16(o) || dq == nullptr || !aligned16(dq)))
+    return ESM_ATTN_ERR_INVALID_ARGUMENT;
+  if (pdkv && (dk == nullptr || !aligned16(dk) || dv == nullptr || !aligned16(dv)))
+    return ESM_ATTN_ERR_INVALID_ARGUMENT;
+  const Layout l = make_layout(batch, total_tokens, max_seqlen, num_heads, head_dim, false);
+  if (plan_bytes < l.total) return ESM_ATTN_ERR_WORKSPACE_TOO_SMALL;
+  if (max_seqlen == 0) return ESM_ATTN_OK;
+  const char* ws = static_cast<const char*>(plan);
+  AttnArgs a = {};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = d_o;
+  a.lse_in = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.drow = drow;
+  a.rope = reinterpret_cast<const float2*>(ws + l.rope);
+  a.items = reinterpret_cast<const Item*>(ws + l.items);
+  fill_common(&a, total_tokens, num_heads, softmax_scale);
+  if (launch_bwd(head_dim, rope_base != 0.f, a, l.n_slots, pdq, pdkv,
+                 reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return ESM_ATTN_ERR_HIP;
+  return ESM_ATTN_OK;
+}
+
+esm_attn_status_t esm_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                               const int32_t* cu_seqlens, int32_t batch, int32_t total_tokens,
+                               int32_t max_seqlen, int32_t num_heads, int32_t head_dim,
+                               float softmax_scale, float rope_base, uint16_t* o, float* lse,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  esm_attn_status_t s = check_sizes(batch, total_tokens, max_seqlen, num_heads, head_dim);
+  if (s != ESM_ATTN_OK) return s;
+  if ((s = check_scalars(softmax_scale, rope_base)) != ESM_ATTN_OK) return s;
+  if (total_tokens == 0) return ESM_ATTN_OK;
+  const void* ptrs[] = {q, k, v, cu_seqlens, o, lse, workspace};
+  for (const void* p : ptrs)
+    if (p == nullptr || !aligned16(p)) return ESM_ATTN_ERR_INVALID_ARGUMENT;
+  const Layout l = make_layout(batch, total_tokens, max_seqlen, num_heads, head_dim, false);
+  if (workspace_bytes < l.total) return ESM_ATTN_ERR_WORKSPACE_TOO_SMALL;
+  if (max_seqlen == 0) return ESM_ATTN_OK;
+  if ((s = esm_attn_plan(cu_seqlens, batch, total_tokens, max_seqlen, num_heads, head_dim,
+                         rope_base, workspace, workspace_bytes, stream)) != ESM_ATTN_OK)
+    return s;
+  return esm_attn_fwd_planned(q, k, v, batch, total_tokens, max_seqlen, num_heads, head_dim,
+                              softmax_scale, rope_base, o, lse, workspace, workspace_bytes, stream);
+}
+
+esm_attn_status_t esm_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                               const uint16_t* o, const uint16_t* d_o, const float* lse,
+                               const int32_t* cu_seqlens, int32_t batch, int32_t total_tokens,
+                               int32_t max_seqlen, int32_t num_heads, int32_t head_dim,
+                               float softmax_scale, float rope_base, uint16_t* dq, uint16_t* dk,
+                               uint16_t* dv, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  esm_attn_status_t s = check_sizes(batch, total_tokens, max_seqlen, num_heads, head_dim);
+  if (s != ESM_ATTN_OK) return s;
+  if ((s = check_scalars(softmax_scale, rope_base)) != ESM_ATTN_OK) return s;
+  if (total_tokens == 0) return ESM_ATTN_OK;
+  const void* ptrs[] = {q, k, v, o, d_o, lse, cu_seqlens, dq, dk, dv, workspace};
+  for (const void* p : ptrs)
+    if (p == nullptr || !aligned16(p)) return ESM_ATTN_ERR_INVALID_ARGUMENT;
+  const Layout l = make_layout(batch, total_tokens, max_seqlen, num_heads, head_dim, true);
+  if (workspace_bytes < l.total) return ESM_ATTN_ERR_WORKSPACE_TOO_SMALL;
+  if (max_seqlen == 0) return ESM_ATTN_OK;
+  char* ws = static_cast<char*>(workspace);
+  if ((s = esm_attn_plan(cu_seqlens, batch, total_tokens, max_seqlen, num_heads, head_dim,
+                         rope_base, ws, l.drow, stream)) != ESM_ATTN_OK)
+    return s;
+  return esm_attn_bwd_planned(q, k, v, o, d_o, lse, batch, total_tokens, max_seqlen, num_heads,
+                              head_dim, softmax_scale, rope_base, dq, dk, dv,
+                              reinterpret_cast<float*>(ws + l.drow),
+                              ESM_ATTN_PASS_DQ | ESM_ATTN_PASS_DKV, ws, l.drow, stream);
+}
+
+esm_attn_status_t esm_attn_check_cu_seqlens_host(const int32_t* cu, int32_t batch,
+                                                 int32_t total_tokens, int32_t max_seqlen) {
+  if (cu == nullptr || batch < 1 || total_tokens < 0 || max_seqlen < 0)
+    return ESM_ATTN_ERR_INVALID_ARGUMENT;
+  if (cu[0] != 0 || cu[batch] != total_tokens) return ESM_ATTN_ERR_INVALID_ARGUMENT;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t L = (int64_t)cu[b + 1] - cu[b];
+    if (L < 0 || L > max_seqlen) return ESM_ATTN_ERR_INVALID_ARGUMENT;
+  }
+  return ESM_ATTN_OK;
+}
+
+esm_attn_status_t esm_attn_schedule_host(const int32_t* cu, int32_t batch, int32_t total_tokens,
+                                         int32_t max_seqlen, int32_t num_heads,
+                                         int32_t block_rows, int32_t* items,
+                                         int32_t items_capacity, int32_t* n_slots) {
+  if (cu == nullptr || items == nullptr || n_slots == nullptr || batch < 1 || num_heads < 1 ||
+      total_tokens < 0 || max_seqlen < 0 || max_seqlen > kMaxSeqlen || block_rows < 16)
+    return ESM_ATTN_ERR_INVALID_ARGUMENT;
+  if (ceil_div64(max_seqlen, block_rows) + 1 > kMaxBuckets) return ESM_ATTN_ERR_INVALID_ARGUMENT;
+  const int64_t slots = schedule_slot_bound(batch, total_tokens, num_heads, max_seqlen, block_rows);
+  if (slots > items_capacity) return ESM_ATTN_ERR_INVALID_ARGUMENT;
+  *n_slots = (int32_t)slots;
+  // sequences by item count, longest first (ties by index)
+  std::vector<int32_t> nblk(batch), sorted;
+  sorted.reserve(batch);
+  for (int32_t b = 0; b < batch; ++b) {
+    int32_t st, L;
+    seq_bounds(cu, b, total_tokens, max_seqlen, &st, &L);
+    nblk[b] = (L + block_rows - 1) / block_rows;
+  }
+  for (int32_t k = (int32_t)ceil_div64(max_seqlen, block_rows); k >= 0; --k)
+    for (int32_t b = 0; b < batch; ++b)
+      if (nblk[b] == k) sorted.push_back(b);
+  const int32_t n_chunks = (int32_t)schedule_num_chunks(batch, num_heads);
+  std::vector<int32_t> base(n_chunks + 1, 0);
+  const int64_t groups = (int64_t)batch * num_heads;
+  for (int32_t c = 0; c < n_chunks; ++c) {
+    const int64_t g0 = 8 * (int64_t)c;
+    const int64_t g1 = (g0 + 8 < groups ? g0 + 8 : groups) - 1;
+    int32_t height = 0;
+    for (int64_t s = g0 / num_heads; s <= g1 / num_heads; ++s)
+      height = nblk[sorted[s]] > height ? nblk[sorted[s]] : height;
+    base[c + 1] = base[c] + 8 * height;
+  }
+  for (int64_t i = 0; i < slots; ++i) {
+    int32_t* it = items + 4 * i;
+    if (!schedule_decode(i, cu, sorted.data(), base.data(), n_chunks, batch, total_tokens,
+                         num_heads, max_seqlen, block_rows, it, it + 1, it + 2, it + 3)) {
+      it[0] = it[1] = it[2] = it[3] = -1;
+    }
+  }
+  return ESM_ATTN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,56 @@
+// Launch interfaces between the C-ABI layer (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace esm {
+
+struct PrepArgs {
+  const int32_t* cu;
+  int32_t B, T, H, max_seqlen, block, head_dim;
+  int32_t* sorted;      // [B]
+  int32_t* chunk_base;  // [n_chunks + 1]
+  int32_t n_chunks;
+  Item* items;          // [n_slots]
+  int64_t n_slots;
+  float2* rope;         // [max_seqlen][head_dim/2], or null
+  double rope_base;
+};
+
+hipError_t launch_prep(const PrepArgs& a, hipStream_t stream);
+
+// Everything the attention kernels read. Pointers to bf16 data are uint16_t.
+struct AttnArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;    // backward: forward output
+  const uint16_t* dout; // backward: dO
+  uint16_t* out;        // forward: O
+  float* lse;           // [H][T]
+  const float* lse_in;  // backward: LSE from the forward
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* drow;          // backward: D = rowsum(dO * O), [H][T]
+  const float2* rope;   // [max_seqlen][d/2]
+  const Item* items;
+  int32_t T, H;
+  float c;              // |softmax_scale| * log2(e)
+  float q_sign;         // sign applied to rotated q so that scores use |scale|
+  float scale;          // softmax_scale (signed)
+  float scale_abs;
+};
+
+hipError_t launch_fwd(int head_dim, bool rope, const AttnArgs& a, int64_t n_slots,
+                      hipStream_t stream);
+hipError_t launch_bwd(int head_dim, bool rope, const AttnArgs& a, int64_t n_slots, bool dq_pass,
+                      bool dkv_pass, hipStream_t stream);
+
+// Rows per work item of every kernel (the schedule is built for it).
+constexpr int kItemRows = 128;
+
+}  // namespace esm

