@@ -36,7 +36,23 @@ def parse():
     p.add_argument("--workload", default="esm2_650m")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 256 MiB device copy (calibrates HBM byte counters)")
     return p.parse_args()
+
+
+def copy_calibration():
+    """A plain device-to-device copy of 256 MiB, three times: under a
+    FETCH_SIZE / WRITE_SIZE counter run it gives the counters' reading for
+    known traffic (256 MiB read + 256 MiB written per dispatch)."""
+    import torch
+    n = 256 << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "dispatches": 3}), flush=True)
 
 
 def cpu_baseline(inp, budget_s):
@@ -78,6 +94,9 @@ def cpu_baseline(inp, budget_s):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build runs the attention hot path on a "
               "single MI355X (no sharding, no collectives); --gpus %d is not supported"

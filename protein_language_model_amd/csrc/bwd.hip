@@ -11,40 +11,21 @@
 //             (32 at d=128): S = Q~ K~^T, dP = dO V^T, dS = P (dP - D),
 //             dV^T += dO^T P, dK~^T += Q~^T dS. Epilogue: dk = R(-p)(|scale| dK~),
 //             dv -> bf16.
-// Operands that the products contract over the sequence axis (K~^T, Q~^T,
-// dO^T) are stored transposed in LDS so every MFMA operand is one 16-byte LDS
-// read; the next block's global loads are issued before the current block's
-// math (double-buffered LDS, one barrier per block).
+// All LDS tiles are row-major (token rows, d columns). Operands that a product
+// contracts over the token axis (K~^T, Q~^T, dO^T) are read from those same
+// tiles with the LDS transpose load, so nothing is stored twice. The next
+// block's global loads are issued before the current block's math
+// (double-buffered LDS, one barrier per block).
 #include "common.h"
 #include "prep.h"
 
 namespace esm {
 
-__device__ __forceinline__ void load_cs8(const float2* rope, int64_t idx, float2* cs) {
-  const u32x4* p = reinterpret_cast<const u32x4*>(rope + idx);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const u32x4 v = p[i];
-    cs[2 * i] = make_float2(__uint_as_float(v[0]), __uint_as_float(v[1]));
-    cs[2 * i + 1] = make_float2(__uint_as_float(v[2]), __uint_as_float(v[3]));
-  }
-}
-
-// Stores 8 bf16 values (one chunk of a row) as column entries of a transposed
-// LDS tile: dst[(d0 + e) * pitch + col] = v[e].
-__device__ __forceinline__ void st_col8(uint16_t* dst, int d0, int pitch, int col, const u32x4& v) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const uint32_t wv = v[e >> 1];
-    dst[(d0 + e) * pitch + col] = (uint16_t)((e & 1) ? (wv >> 16) : (wv & 0xffffu));
-  }
-}
-
 // Cooperative epilogue: fp32 tile F[rows][D + 4] in LDS (row = position
 // pos0 + row inside the sequence) -> optional inverse rotation -> bf16 global.
 template <int D, bool ROPE>
 __device__ __forceinline__ void store_rows(const float* F, int rows, int pos0, int L,
-                                           uint16_t* G, int64_t rs, const float2* rope,
+                                           uint16_t* G, int rs, const float2* rope,
                                            bool rotate, int tid) {
   constexpr int FP = D + 4;
   for (int u = tid; u < rows * (D / 16); u += 256) {
@@ -58,8 +39,8 @@ __device__ __forceinline__ void store_rows(const float* F, int rows, int pos0, i
     }
     if (ROPE && rotate) {
       float2 cs[8];
-      load_cs8(rope, (int64_t)pos * (D / 2) + j0, cs);
-      rotate8(lo, hi, cs, true, 1.0f);
+      load_cs8(rope, pos * (D / 2) + j0, cs);
+      rotate8<true, false>(lo, hi, cs);
     }
     st16(G + pos * rs + j0, pack8(lo));
     st16(G + pos * rs + j0 + D / 2, pack8(hi));
@@ -74,15 +55,13 @@ struct DqCfg {
   static constexpr int BM = 128;
   static constexpr int BN = D == 128 ? 32 : 64;
   static constexpr int KP = D + 8;
-  static constexpr int TP = BN + 8;
   static constexpr int NS = D / 16;
   static constexpr int ND = D >= 32 ? D / 32 : 1;
   static constexpr int NT = BN / 32;
   static constexpr int NU = BN / 16;
   static constexpr int K_ELEMS = BN * KP;  // K~ rows
   static constexpr int V_ELEMS = BN * KP;  // V rows
-  static constexpr int T_ELEMS = D * TP;   // K~^T
-  static constexpr int STAGE = K_ELEMS + V_ELEMS + T_ELEMS;
+  static constexpr int STAGE = K_ELEMS + V_ELEMS;
   static constexpr int PRO = BM * KP;
   static constexpr int EPI = BM * (D + 4) * 2;  // fp32 tile, in uint16 units
   static constexpr int LDS0 = 2 * STAGE > PRO ? 2 * STAGE : PRO;
@@ -103,7 +82,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnArgs a) {
   const int L = it.len, h = it.head, q0 = it.blk * C::BM;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r = lane & 31, g = lane >> 5, prow = perm_row(r);
-  const int64_t rs = (int64_t)a.H * D;
+  const int rs = a.H * D;  // row stride; T*H*d < 2^31 is checked on the host
   const int64_t base = (int64_t)it.seq0 * rs + (int64_t)h * D;
   const uint16_t* __restrict__ Qg = a.q + base;
   const uint16_t* __restrict__ Kg = a.k + base;
@@ -112,6 +91,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnArgs a) {
   const uint16_t* __restrict__ dOg = a.dout + base;
   const int qi = q0 + w * 32 + r;  // this lane's query
   const bool qvalid = qi < L;
+  const bool qneg = a.q_sign < 0.f;
 
   // ---- prologue: rotated queries (B operands)
   for (int u = tid; u < C::BM * (D / 16); u += 256) {
@@ -122,11 +102,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnArgs a) {
       unpack8(ld16(Qg + qq * rs + j0 + D / 2), hi);
       if (ROPE) {
         float2 cs[8];
-        load_cs8(a.rope, (int64_t)qq * (D / 2) + j0, cs);
-        rotate8(lo, hi, cs, false, a.q_sign);
-      } else {
+        load_cs8(a.rope, qq * (D / 2) + j0, cs);
+        rotate8_signed(lo, hi, cs, qneg);
+      } else if (qneg) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) { lo[e] *= a.q_sign; hi[e] *= a.q_sign; }
+        for (int e = 0; e < 8; ++e) { lo[e] = -lo[e]; hi[e] = -hi[e]; }
       }
     } else {
 #pragma unroll
@@ -167,70 +147,62 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnArgs a) {
   // ---- K/V staging
   u32x4 kl[C::KU], kh[C::KU], vv[C::VU];
   float2 kcs[C::KU][8];
+  // Rows past the end of the sequence are loaded as copies of its last row
+  // (finite, in bounds); the ragged block masks their P to 0.
   auto issue = [&](int kb) {
     const int k0 = kb * C::BN;
 #pragma unroll
     for (int x = 0; x < C::KU; ++x) {
       const int u = tid + 256 * x;
-      kl[x] = zero4();
-      kh[x] = zero4();
-      if (u < C::K_UNITS) {
-        const int row = u / (D / 16), j0 = (u % (D / 16)) * 8, key = k0 + row;
-        if (key < L) {
-          kl[x] = ld16(Kg + key * rs + j0);
-          kh[x] = ld16(Kg + key * rs + j0 + D / 2);
-          if (ROPE) load_cs8(a.rope, (int64_t)key * (D / 2) + j0, kcs[x]);
-        }
+      if (C::K_UNITS % 256 == 0 || u < C::K_UNITS) {
+        const int row = u / (D / 16), j0 = (u % (D / 16)) * 8;
+        const int key = min(k0 + row, L - 1);
+        kl[x] = ld16(Kg + key * rs + j0);
+        kh[x] = ld16(Kg + key * rs + j0 + D / 2);
+        if (ROPE) load_cs8(a.rope, key * (D / 2) + j0, kcs[x]);
       }
     }
 #pragma unroll
     for (int x = 0; x < C::VU; ++x) {
       const int u = tid + 256 * x;
-      vv[x] = zero4();
-      if (u < C::V_UNITS) {
-        const int row = u / (D / 8), c8 = (u % (D / 8)) * 8, key = k0 + row;
-        if (key < L) vv[x] = ld16(Vg + key * rs + c8);
+      if (C::V_UNITS % 256 == 0 || u < C::V_UNITS) {
+        const int row = u / (D / 8), c8 = (u % (D / 8)) * 8;
+        vv[x] = ld16(Vg + min(k0 + row, L - 1) * rs + c8);
       }
     }
   };
-  auto commit = [&](int kb, int stage) {
+  auto commit = [&](int stage) {
     uint16_t* Ks = lds + stage * C::STAGE;
     uint16_t* Vs = Ks + C::K_ELEMS;
-    uint16_t* Ts = Vs + C::V_ELEMS;
-    const int k0 = kb * C::BN;
 #pragma unroll
     for (int x = 0; x < C::KU; ++x) {
       const int u = tid + 256 * x;
-      if (u < C::K_UNITS) {
+      if (C::K_UNITS % 256 == 0 || u < C::K_UNITS) {
         const int row = u / (D / 16), j0 = (u % (D / 16)) * 8;
         u32x4 lo = kl[x], hi = kh[x];
-        if (ROPE && k0 + row < L) {
+        if (ROPE) {
           float fl[8], fh[8];
           unpack8(lo, fl);
           unpack8(hi, fh);
-          rotate8(fl, fh, kcs[x], false, 1.0f);
+          rotate8<false, false>(fl, fh, kcs[x]);
           lo = pack8(fl);
           hi = pack8(fh);
         }
         st16(&Ks[row * C::KP + j0], lo);
         st16(&Ks[row * C::KP + j0 + D / 2], hi);
-        st_col8(Ts, j0, C::TP, row, lo);
-        st_col8(Ts, j0 + D / 2, C::TP, row, hi);
       }
     }
 #pragma unroll
     for (int x = 0; x < C::VU; ++x) {
       const int u = tid + 256 * x;
-      if (u < C::V_UNITS) {
-        const int row = u / (D / 8), c8 = (u % (D / 8)) * 8;
-        st16(&Vs[row * C::KP + c8], vv[x]);
-      }
+      if (C::V_UNITS % 256 == 0 || u < C::V_UNITS)
+        st16(&Vs[(u / (D / 8)) * C::KP + (u % (D / 8)) * 8], vv[x]);
     }
   };
 
   const int nkb = (L + C::BN - 1) / C::BN;
   issue(0);
-  commit(0, 0);
+  commit(0);
   __syncthreads();
 
   const float c = a.c;
@@ -243,9 +215,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnArgs a) {
     if (kb + 1 < nkb) issue(kb + 1);
     const uint16_t* Ks = lds + stage * C::STAGE;
     const uint16_t* Vs = Ks + C::K_ELEMS;
-    const uint16_t* Ts = Vs + C::V_ELEMS;
-    const int lim = L - kb * C::BN;
-    const bool ragged = lim < C::BN;
+    const int lim = L - kb * C::BN;  // valid keys in this block
 
     u32x4 dsreg[C::NU];
 #pragma unroll
@@ -260,9 +230,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnArgs a) {
       float dsv[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float p = fast_exp2(fmaf(sacc[i], c, -lse2));
-        if (ragged && 32 * t + 16 * g + i >= lim) p = 0.f;
+        const float p = fast_exp2(fmaf(sacc[i], c, -lse2));
         dsv[i] = p * (pacc[i] - Dq);
+      }
+      if (lim < C::BN) {  // keys past the end: dS = 0
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (32 * t + 16 * g + i >= lim) dsv[i] = 0.f;
       }
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
@@ -274,13 +248,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnArgs a) {
     for (int dt = 0; dt < C::ND; ++dt) {
 #pragma unroll
       for (int u = 0; u < C::NU; ++u) {
-        u32x4 at = zero4();
-        if (D >= 32 || prow < D)
-          at = ld16(&Ts[(32 * dt + prow) * C::TP + 32 * (u >> 1) + 16 * g + 8 * (u & 1)]);
+        const u32x4 at =
+            ld_tr8<(D < 32)>(Ks, C::KP, 32 * (u >> 1) + 8 * (u & 1), 32 * dt, D);
         dqacc[dt] = mfma32(at, dsreg[u], dqacc[dt]);
       }
     }
-    if (kb + 1 < nkb) commit(kb + 1, stage ^ 1);
+    if (kb + 1 < nkb) commit(stage ^ 1);
     __syncthreads();
   }
 
@@ -307,17 +280,14 @@ struct DkvCfg {
   static constexpr int BK = 128;
   static constexpr int BQ = D == 128 ? 32 : 64;
   static constexpr int KP = D + 8;
-  static constexpr int TP = BQ + 8;
   static constexpr int NS = D / 16;
   static constexpr int ND = D >= 32 ? D / 32 : 1;
   static constexpr int NT = BQ / 32;
   static constexpr int NU = BQ / 16;
   static constexpr int Q_ELEMS = BQ * KP;   // Q~ rows
-  static constexpr int QT_ELEMS = D * TP;   // Q~^T
   static constexpr int O_ELEMS = BQ * KP;   // dO rows
-  static constexpr int OT_ELEMS = D * TP;   // dO^T
   static constexpr int F_ELEMS = 4 * BQ;    // lse2[BQ], D[BQ] as fp32
-  static constexpr int STAGE = Q_ELEMS + QT_ELEMS + O_ELEMS + OT_ELEMS + F_ELEMS;
+  static constexpr int STAGE = Q_ELEMS + O_ELEMS + F_ELEMS;
   static constexpr int PRO = 2 * BK * KP;
   static constexpr int EPI = BK * (D + 4) * 2;
   static constexpr int LDS0 = 2 * STAGE > PRO ? 2 * STAGE : PRO;
@@ -338,13 +308,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(AttnArgs a) {
   const int L = it.len, h = it.head, k0 = it.blk * C::BK;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r = lane & 31, g = lane >> 5, prow = perm_row(r);
-  const int64_t rs = (int64_t)a.H * D;
+  const int rs = a.H * D;  // row stride; T*H*d < 2^31 is checked on the host
   const int64_t base = (int64_t)it.seq0 * rs + (int64_t)h * D;
   const uint16_t* __restrict__ Qg = a.q + base;
   const uint16_t* __restrict__ Kg = a.k + base;
   const uint16_t* __restrict__ Vg = a.v + base;
   const uint16_t* __restrict__ dOg = a.dout + base;
   const int64_t row0 = (int64_t)h * a.T + it.seq0;
+  const bool qneg = a.q_sign < 0.f;
 
   // ---- prologue: rotated keys and values -> LDS -> B-operand registers
   {
@@ -359,8 +330,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(AttnArgs a) {
         unpack8(ld16(Kg + key * rs + j0 + D / 2), hi);
         if (ROPE) {
           float2 cs[8];
-          load_cs8(a.rope, (int64_t)key * (D / 2) + j0, cs);
-          rotate8(lo, hi, cs, false, 1.0f);
+          load_cs8(a.rope, key * (D / 2) + j0, cs);
+          rotate8<false, false>(lo, hi, cs);
         }
         vlo = ld16(Vg + key * rs + j0);
         vhi = ld16(Vg + key * rs + j0 + D / 2);
@@ -387,34 +358,32 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(AttnArgs a) {
   u32x4 ql[C::QU], qh[C::QU], ov[C::OU];
   float2 qcs[C::QU][8];
   float fl_lse = 0.f, fl_d = 0.f;
+  // Rows past the end of the sequence are loaded as copies of its last row
+  // (finite, in bounds); their LSE is set to +inf so that P = 0.
   auto issue = [&](int qb) {
     const int q0 = qb * C::BQ;
 #pragma unroll
     for (int x = 0; x < C::QU; ++x) {
       const int u = tid + 256 * x;
-      ql[x] = zero4();
-      qh[x] = zero4();
-      if (u < C::Q_UNITS) {
-        const int row = u / (D / 16), j0 = (u % (D / 16)) * 8, qq = q0 + row;
-        if (qq < L) {
-          ql[x] = ld16(Qg + qq * rs + j0);
-          qh[x] = ld16(Qg + qq * rs + j0 + D / 2);
-          if (ROPE) load_cs8(a.rope, (int64_t)qq * (D / 2) + j0, qcs[x]);
-        }
+      if (C::Q_UNITS % 256 == 0 || u < C::Q_UNITS) {
+        const int row = u / (D / 16), j0 = (u % (D / 16)) * 8;
+        const int qq = min(q0 + row, L - 1);
+        ql[x] = ld16(Qg + qq * rs + j0);
+        qh[x] = ld16(Qg + qq * rs + j0 + D / 2);
+        if (ROPE) load_cs8(a.rope, qq * (D / 2) + j0, qcs[x]);
       }
     }
 #pragma unroll
     for (int x = 0; x < C::OU; ++x) {
       const int u = tid + 256 * x;
-      ov[x] = zero4();
-      if (u < C::O_UNITS) {
-        const int row = u / (D / 8), c8 = (u % (D / 8)) * 8, qq = q0 + row;
-        if (qq < L) ov[x] = ld16(dOg + qq * rs + c8);
+      if (C::O_UNITS % 256 == 0 || u < C::O_UNITS) {
+        const int row = u / (D / 8), c8 = (u % (D / 8)) * 8;
+        ov[x] = ld16(dOg + min(q0 + row, L - 1) * rs + c8);
       }
     }
     if (tid < C::BQ) {
       const int qq = q0 + tid;
-      fl_lse = INFINITY;  // padding rows: P = exp2(-inf) = 0
+      fl_lse = INFINITY;
       fl_d = 0.f;
       if (qq < L) {
         fl_lse = a.lse_in[row0 + qq] * kLog2e;
@@ -422,42 +391,33 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(AttnArgs a) {
       }
     }
   };
-  auto commit = [&](int qb, int stage) {
+  auto commit = [&](int stage) {
     uint16_t* Qs = lds + stage * C::STAGE;
-    uint16_t* QTs = Qs + C::Q_ELEMS;
-    uint16_t* Os = QTs + C::QT_ELEMS;
-    uint16_t* OTs = Os + C::O_ELEMS;
-    float* Fs = reinterpret_cast<float*>(OTs + C::OT_ELEMS);
-    const int q0 = qb * C::BQ;
+    uint16_t* Os = Qs + C::Q_ELEMS;
+    float* Fs = reinterpret_cast<float*>(Os + C::O_ELEMS);
 #pragma unroll
     for (int x = 0; x < C::QU; ++x) {
       const int u = tid + 256 * x;
-      if (u < C::Q_UNITS) {
+      if (C::Q_UNITS % 256 == 0 || u < C::Q_UNITS) {
         const int row = u / (D / 16), j0 = (u % (D / 16)) * 8;
         float fl[8], fh[8];
         unpack8(ql[x], fl);
         unpack8(qh[x], fh);
-        if (ROPE && q0 + row < L) {
-          rotate8(fl, fh, qcs[x], false, a.q_sign);
-        } else {
+        if (ROPE) {
+          rotate8_signed(fl, fh, qcs[x], qneg);
+        } else if (qneg) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) { fl[e] *= a.q_sign; fh[e] *= a.q_sign; }
+          for (int e = 0; e < 8; ++e) { fl[e] = -fl[e]; fh[e] = -fh[e]; }
         }
-        const u32x4 lo = pack8(fl), hi = pack8(fh);
-        st16(&Qs[row * C::KP + j0], lo);
-        st16(&Qs[row * C::KP + j0 + D / 2], hi);
-        st_col8(QTs, j0, C::TP, row, lo);
-        st_col8(QTs, j0 + D / 2, C::TP, row, hi);
+        st16(&Qs[row * C::KP + j0], pack8(fl));
+        st16(&Qs[row * C::KP + j0 + D / 2], pack8(fh));
       }
     }
 #pragma unroll
     for (int x = 0; x < C::OU; ++x) {
       const int u = tid + 256 * x;
-      if (u < C::O_UNITS) {
-        const int row = u / (D / 8), c8 = (u % (D / 8)) * 8;
-        st16(&Os[row * C::KP + c8], ov[x]);
-        st_col8(OTs, c8, C::TP, row, ov[x]);
-      }
+      if (C::O_UNITS % 256 == 0 || u < C::O_UNITS)
+        st16(&Os[(u / (D / 8)) * C::KP + (u % (D / 8)) * 8], ov[x]);
     }
     if (tid < C::BQ) {
       Fs[tid] = fl_lse;
@@ -467,7 +427,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(AttnArgs a) {
 
   const int nqb = (L + C::BQ - 1) / C::BQ;
   issue(0);
-  commit(0, 0);
+  commit(0);
   __syncthreads();
 
   const float c = a.c;
@@ -482,10 +442,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(AttnArgs a) {
     const int stage = qb & 1;
     if (qb + 1 < nqb) issue(qb + 1);
     const uint16_t* Qs = lds + stage * C::STAGE;
-    const uint16_t* QTs = Qs + C::Q_ELEMS;
-    const uint16_t* Os = QTs + C::QT_ELEMS;
-    const uint16_t* OTs = Os + C::O_ELEMS;
-    const float* Fs = reinterpret_cast<const float*>(OTs + C::OT_ELEMS);
+    const uint16_t* Os = Qs + C::Q_ELEMS;
+    const float* Fs = reinterpret_cast<const float*>(Os + C::O_ELEMS);
 
     u32x4 preg[C::NU], dsreg[C::NU];
 #pragma unroll
@@ -527,17 +485,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(AttnArgs a) {
     for (int dt = 0; dt < C::ND; ++dt) {
 #pragma unroll
       for (int u = 0; u < C::NU; ++u) {
-        u32x4 ao = zero4(), aq = zero4();
-        if (D >= 32 || prow < D) {
-          const int off = (32 * dt + prow) * C::TP + 32 * (u >> 1) + 16 * g + 8 * (u & 1);
-          ao = ld16(&OTs[off]);
-          aq = ld16(&QTs[off]);
-        }
+        const int k0 = 32 * (u >> 1) + 8 * (u & 1);
+        const u32x4 ao = ld_tr8<(D < 32)>(Os, C::KP, k0, 32 * dt, D);
+        const u32x4 aq = ld_tr8<(D < 32)>(Qs, C::KP, k0, 32 * dt, D);
         dvacc[dt] = mfma32(ao, preg[u], dvacc[dt]);
         dkacc[dt] = mfma32(aq, dsreg[u], dkacc[dt]);
       }
     }
-    if (qb + 1 < nqb) commit(qb + 1, stage ^ 1);
+    if (qb + 1 < nqb) commit(stage ^ 1);
     __syncthreads();
   }
 

@@ -7,11 +7,22 @@
 
 namespace esm {
 
+// Compile-time flag passed to generic lambdas: selects the full-tile code path
+// (no per-row bounds checks or masks) or the ragged-tile one.
+template <bool B>
+struct Tag {
+  static constexpr bool value = B;
+};
+using Full = Tag<true>;
+using Ragged = Tag<false>;
+
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
@@ -81,21 +92,75 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // cs[0..7]: x' = x c - y s, y' = y c + x s, every product and sum rounded to
 // float32 (no fused multiply-add), so that the later rounding of x' and y' to
 // bf16 is decided on exactly the float32 values a plain float32 evaluation
-// gives. inverse rotates by the negative angles (the transpose). The results
-// are multiplied by mul (+1 or -1, exact).
-__device__ __forceinline__ void rotate8(float* lo, float* hi, const float2* cs, bool inverse,
-                                        float mul) {
+// gives. INVERSE rotates by the negative angles (the transpose); NEG negates
+// the results (exact).
+template <bool INVERSE, bool NEG>
+__device__ __forceinline__ void rotate8(float* lo, float* hi, const float2* cs) {
 #pragma clang fp contract(off)
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const float c = cs[e].x;
-    const float s = inverse ? -cs[e].y : cs[e].y;
+    const float s = INVERSE ? -cs[e].y : cs[e].y;
     const float x = lo[e], y = hi[e];
     const float xc = x * c, ys = y * s, yc = y * c, xs = x * s;
-    lo[e] = (xc - ys) * mul;
-    hi[e] = (yc + xs) * mul;
+    lo[e] = NEG ? ys - xc : xc - ys;
+    hi[e] = NEG ? -(yc + xs) : yc + xs;
   }
 }
+
+// Rotation with a run-time sign (q is negated when the softmax scale is
+// negative, so that scores can use |scale|).
+__device__ __forceinline__ void rotate8_signed(float* lo, float* hi, const float2* cs, bool neg) {
+  if (neg) rotate8<false, true>(lo, hi, cs);
+  else rotate8<false, false>(lo, hi, cs);
+}
+
+// Loads (cos, sin) for the angles p * theta_{j0 .. j0+7}: 64 contiguous bytes.
+__device__ __forceinline__ void load_cs8(const float2* rope, int64_t idx, float2* cs) {
+  const u32x4* p = reinterpret_cast<const u32x4*>(rope + idx);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const u32x4 v = p[i];
+    cs[2 * i] = make_float2(__uint_as_float(v[0]), __uint_as_float(v[1]));
+    cs[2 * i + 1] = make_float2(__uint_as_float(v[2]), __uint_as_float(v[3]));
+  }
+}
+
+// MFMA operand whose k index runs along the ROWS of a row-major bf16 LDS tile
+// T (pitch in elements; every row start and col0 8-byte aligned). Lane
+// (r = l % 32, g = l / 32) receives T[k0 + 16g + e][col0 + perm_row(r)] for
+// e = 0..7, through two ds_read_b64_tr_b16. That instruction works on groups of
+// 16 lanes: lane 4a + b of a group receives element b of the 8-byte chunks
+// addressed by lanes a, a+4, a+8, a+12 of the group. Here lane s of group G
+// addresses row k0 + 16g + 4h + s/4 at column col0 + perm_row(16(G%2) + 4(s%4)),
+// so lane 4a + b collects four consecutive rows of column
+// col0 + perm_row(16(G%2) + 4a) + b = col0 + perm_row(r).
+// ZERO_HI: lanes whose perm_row(r) >= ncols get zeros (tiles narrower than
+// 32 columns); their source addresses are clamped into the tile.
+template <bool ZERO_HI>
+__device__ __forceinline__ u32x4 ld_tr8(const uint16_t* T, int pitch, int k0, int col0,
+                                        int ncols) {
+  const int l = threadIdx.x & 63;
+  const int s = l & 15, G = l >> 4, g = l >> 5;
+  int col = perm_row(16 * (G & 1) + 4 * (s & 3));
+  if (ZERO_HI && col >= ncols) col = 0;
+  const uint16_t* p0 = T + (k0 + 16 * g + (s >> 2)) * pitch + col0 + col;
+  const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p0);
+  const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0 + 4 * pitch));
+  const uint2 a = __builtin_bit_cast(uint2, v0), b = __builtin_bit_cast(uint2, v1);
+  u32x4 out = {a.x, a.y, b.x, b.y};
+  if (ZERO_HI && perm_row(l & 31) >= ncols) out = u32x4{0u, 0u, 0u, 0u};
+  return out;
+}
+
+// sum += x.lo + x.hi for a packed bf16 pair (v_dot2c_f32_bf16 against (1, 1)).
+__device__ __forceinline__ float add_bf16x2(uint32_t x, float sum) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x),
+                                         __builtin_bit_cast(bf16x2, 0x3f803f80u), sum, false);
+}
+
+// True if any lane of the wave has pred set (wave-uniform result).
+__device__ __forceinline__ bool wave_any(bool pred) { return __ballot(pred) != 0ull; }
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
