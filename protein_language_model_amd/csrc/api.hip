@@ -69,7 +69,10 @@ void fill_common(AttnArgs* a, int32_t T, int32_t H, float scale) {
   a->scale = scale;
   a->scale_abs = fabsf(scale);
   a->q_sign = scale < 0.f ? -1.f : 1.f;
-  a->c = fabsf(scale) * kLog2e;
+  // exp2 scale. A floor of 1e-30 keeps it positive, so that masked scores
+  // (-inf) still give exp2(-inf) = 0 when softmax_scale is 0; below the floor
+  // every |S c| rounds exp2 to exactly 1 either way.
+  a->c = fmaxf(fabsf(scale) * kLog2e, 1e-30f);
 }
 
 esm_attn_status_t run_prep(const int32_t* cu, int32_t B, int32_t T, int32_t maxL, int32_t H,

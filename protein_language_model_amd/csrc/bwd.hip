@@ -21,32 +21,6 @@
 
 namespace esm {
 
-// Cooperative epilogue: fp32 tile F[rows][D + 4] in LDS (row = position
-// pos0 + row inside the sequence) -> optional inverse rotation -> bf16 global.
-template <int D, bool ROPE>
-__device__ __forceinline__ void store_rows(const float* F, int rows, int pos0, int L,
-                                           uint16_t* G, int rs, const float2* rope,
-                                           bool rotate, int tid) {
-  constexpr int FP = D + 4;
-  for (int u = tid; u < rows * (D / 16); u += 256) {
-    const int row = u / (D / 16), j0 = (u % (D / 16)) * 8, pos = pos0 + row;
-    if (pos >= L) continue;
-    float lo[8], hi[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      lo[e] = F[row * FP + j0 + e];
-      hi[e] = F[row * FP + j0 + D / 2 + e];
-    }
-    if (ROPE && rotate) {
-      float2 cs[8];
-      load_cs8(rope, pos * (D / 2) + j0, cs);
-      rotate8<true, false>(lo, hi, cs);
-    }
-    st16(G + pos * rs + j0, pack8(lo));
-    st16(G + pos * rs + j0 + D / 2, pack8(hi));
-  }
-}
-
 // =========================================================================
 // dq pass
 // =========================================================================

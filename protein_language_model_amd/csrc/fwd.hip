@@ -5,7 +5,7 @@
 //   Q rows (pre-rotation bf16) -> rotated in fp32 with the cos/sin table,
 //   rounded once to bf16 -> LDS -> registers (MFMA B operands, kept for the
 //   whole item).
-//   For each block of 64 keys: K rows are rotated the same way into a
+//   For each block of 64 keys (32 at d = 128): K rows are rotated the same way into a
 //   row-major LDS tile (the MFMA A operand of S^T = K~ Q~^T) and V rows are
 //   copied row-major into LDS; the A operand of O^T += V^T P^T, which runs
 //   along the key (row) axis, is read with the LDS transpose load. The next
@@ -19,7 +19,7 @@
 //   rescale of O and l by exp2(m_old - m_new) is skipped otherwise, and
 //   P = exp2(S c - m c) <= 256 stays well inside bf16/fp32 range.
 //   The row sum l accumulates P in fp32; P is rounded once to bf16 for the
-//   MFMA.
+//   MFMA. Keys past the end of the sequence get S = -inf, so P = 0.
 //   Epilogue: O = acc / l -> bf16; LSE = (m c + log2 l) ln 2.
 //
 // Tiled attention keeps the L x L matrices on chip (BioNeMo blog, section 2.3
@@ -33,7 +33,7 @@ namespace esm {
 template <int D>
 struct FwdCfg {
   static constexpr int BM = 128;                  // queries per item
-  static constexpr int BN = 64;                   // keys per block
+  static constexpr int BN = D == 128 ? 32 : 64;   // keys per block
   static constexpr int KP = D + 8;                // row pitch of the LDS tiles (bf16)
   static constexpr int NS = D / 16;               // k-steps over d
   static constexpr int ND = D >= 32 ? D / 32 : 1; // 32-row d tiles of O^T
@@ -181,13 +181,12 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a) {
         sacc[t] = mfma32(ld16(&Ks[(32 * t + prow) * C::KP + 16 * s + 8 * g]), qreg[s], sacc[t]);
     }
     const int lim = L - kb * C::BN;  // valid keys in this block
-    const bool ragged = lim < C::BN;
-    if (ragged) {
+    if (lim < C::BN) {  // keys past the end: S = -inf, so P = 0
 #pragma unroll
       for (int t = 0; t < C::NT; ++t)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          if (32 * t + 16 * g + i >= lim) sacc[t][i] = -INFINITY;
+          sacc[t][i] = (32 * t + 16 * g + i < lim) ? sacc[t][i] : -INFINITY;
     }
     float mx = sacc[0][0];
 #pragma unroll
@@ -208,25 +207,20 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a) {
     const float mc = m * c;
 
     u32x4 preg[C::NU];
-    auto probs = [&](auto full) {
-      constexpr bool FULL = decltype(full)::value;
 #pragma unroll
-      for (int t = 0; t < C::NT; ++t) {
-        float p[16];
+    for (int t = 0; t < C::NT; ++t) {
+      float p[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          p[i] = fast_exp2(fmaf(sacc[t][i], c, -mc));
-          if (!FULL && 32 * t + 16 * g + i >= lim) p[i] = 0.f;
-          l += p[i];
-        }
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            preg[2 * t + hh][e] = pack_bf16(p[8 * hh + 2 * e], p[8 * hh + 2 * e + 1]);
+      for (int i = 0; i < 16; ++i) {
+        p[i] = fast_exp2(fmaf(sacc[t][i], c, -mc));
+        l += p[i];
       }
-    };
-    if (ragged) probs(Ragged{}); else probs(Full{});
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          preg[2 * t + hh][e] = pack_bf16(p[8 * hh + 2 * e], p[8 * hh + 2 * e + 1]);
+    }
 #pragma unroll
     for (int dt = 0; dt < C::ND; ++dt) {
 #pragma unroll
