@@ -55,6 +55,40 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": n, "dispatches": 3}), flush=True)
 
 
+def _source_sha256():
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "protein_language_model_amd",
+                        "csrc")
+    for p in sorted(glob.glob(os.path.join(csrc, "*"))):
+        h.update(os.path.basename(p).encode())
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, kernel_name):
+    """HBM bytes per launch of a kernel from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE, each scaled by the reading of a plain
+    copy of known size), or None when the summary is missing or was taken on
+    other kernel sources."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                        "hbm_traffic_%s.json" % workload)
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except OSError:
+        return None
+    if rec.get("source_sha256") != _source_sha256():
+        return None
+    for name, t in rec["kernels"].items():
+        if kernel_name in name:
+            return {"bytes": t["read_bytes"] + t["write_bytes"], "read_bytes": t["read_bytes"],
+                    "write_bytes": t["write_bytes"], "commit": rec.get("commit")}
+    return None
+
+
 def cpu_baseline(inp, budget_s):
     """Times the float64 oracle (forward + backward, bf16-operand mode) on
     (sequence, head) slices of the same workload until about budget_s of CPU
@@ -173,6 +207,9 @@ def main():
                     "bwd_dkv": 8 * s2 * H * d}        # S, dP, dV = P^T dO, dK = dS^T Q
     dom = max(kernel_flops, key=lambda n: avg[n])
     achieved = kernel_flops[dom] / (avg[dom] * 1e-6) / 1e12
+    kernel_symbol = {"fwd": "fwd_kernel<%d" % d, "bwd_dq": "bwd_dq_kernel<%d" % d,
+                     "bwd_dkv": "bwd_dkv_kernel<%d" % d}[dom]
+    traffic = measured_traffic(args.workload, kernel_symbol)
 
     out = {
         "metric": "attention fwd+bwd TFLOP/s and % of bf16 MFMA peak; tokens/s (varlen)",
@@ -196,7 +233,11 @@ def main():
         "kernels_us": {n: round(x, 2) for n, x in avg.items()},
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None if traffic is None else round(traffic["bytes"]),
+                     "traffic_detail": traffic,
+                     "algorithmic_flops": kernel_flops[dom],
+                     "avg_launch_us": round(avg[dom], 2)},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
