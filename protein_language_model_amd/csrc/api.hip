@@ -30,6 +30,7 @@ esm_attn_status_t check_sizes(int32_t B, int32_t T, int32_t maxL, int32_t H, int
   if (maxL > kMaxSeqlen) return ESM_ATTN_ERR_UNSUPPORTED;
   if (!head_dim_ok(d)) return ESM_ATTN_ERR_UNSUPPORTED;
   if ((int64_t)T * H * d >= ((int64_t)1 << 31)) return ESM_ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)H * d >= ((int64_t)1 << 24)) return ESM_ATTN_ERR_UNSUPPORTED;  // row stride
   if (schedule_num_chunks(B, H) + 1 >= ((int64_t)1 << 31)) return ESM_ATTN_ERR_UNSUPPORTED;
   if (schedule_slot_bound(B, T, H, maxL, kItemRows) >= ((int64_t)1 << 31))
     return ESM_ATTN_ERR_UNSUPPORTED;

@@ -7,6 +7,10 @@
 //             stores it for the second pass. Per 64-key block (32 at d=128):
 //             S^T = K~ Q~^T, dP^T = V dO^T, dS = P (dP - D),
 //             dQ~^T += K~^T dS^T. Epilogue: dq = R(-p) (scale dQ~) -> bf16.
+// In the dq pass dP - D comes out of the dP MFMA itself: one extra k-step
+// multiplies (1, 1) by (-D_hi, -D_lo) (D split into two bf16 values), which
+// replaces one vector subtraction per score. (In the dkv pass D varies along
+// the lane's 16 rows; there the extra MFMA measured slower than subtracting.)
 //   dkv pass: one workgroup per 128 keys (lane owns a key). Per 64-query block
 //             (32 at d=128): S = Q~ K~^T, dP = dO V^T, dS = P (dP - D),
 //             dV^T += dO^T P, dK~^T += Q~^T dS. Epilogue: dk = R(-p)(|scale| dK~),
@@ -110,6 +114,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnArgs a) {
     }
   }
   const float Dq = dpart + xor32(dpart);
+  // dP - D in one more MFMA k-step: A = (1, 1), B = (-D_hi, -D_lo), in the
+  // k slots of lane half 0.
+  const u32x4 a_one = {g == 0 ? kBf16OnePair : 0u, 0u, 0u, 0u};
+  const u32x4 b_negd = {g == 0 ? neg_bf16_pair(Dq) : 0u, 0u, 0u, 0u};
   const int64_t rowidx = (int64_t)h * a.T + it.seq0 + qi;
   float lse2 = 0.f;
   if (qvalid) {
@@ -124,24 +132,26 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnArgs a) {
   // Rows past the end of the sequence are loaded as copies of its last row
   // (finite, in bounds); the ragged block masks their P to 0.
   auto issue = [&](int kb) {
-    const int k0 = kb * C::BN;
+    const int k0 = kb * C::BN, lim = L - k0;
+    const uint16_t* __restrict__ Kb = Kg + (int64_t)k0 * rs;
+    const uint16_t* __restrict__ Vb = Vg + (int64_t)k0 * rs;
+    const float2* __restrict__ Rb = a.rope + k0 * (D / 2);
 #pragma unroll
     for (int x = 0; x < C::KU; ++x) {
       const int u = tid + 256 * x;
       if (C::K_UNITS % 256 == 0 || u < C::K_UNITS) {
-        const int row = u / (D / 16), j0 = (u % (D / 16)) * 8;
-        const int key = min(k0 + row, L - 1);
-        kl[x] = ld16(Kg + key * rs + j0);
-        kh[x] = ld16(Kg + key * rs + j0 + D / 2);
-        if (ROPE) load_cs8(a.rope, key * (D / 2) + j0, kcs[x]);
+        const int row = min(u / (D / 16), lim - 1), j0 = (u % (D / 16)) * 8;
+        kl[x] = ld16(Kb + row * rs + j0);
+        kh[x] = ld16(Kb + row * rs + j0 + D / 2);
+        if (ROPE) load_cs8(Rb, row * (D / 2) + j0, kcs[x]);
       }
     }
 #pragma unroll
     for (int x = 0; x < C::VU; ++x) {
       const int u = tid + 256 * x;
       if (C::V_UNITS % 256 == 0 || u < C::V_UNITS) {
-        const int row = u / (D / 8), c8 = (u % (D / 8)) * 8;
-        vv[x] = ld16(Vg + min(k0 + row, L - 1) * rs + c8);
+        const int row = min(u / (D / 8), lim - 1), c8 = (u % (D / 8)) * 8;
+        vv[x] = ld16(Vb + row * rs + c8);
       }
     }
   };
@@ -201,11 +211,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnArgs a) {
         sacc = mfma32(ld16(&Ks[off]), qreg[s], sacc);
         pacc = mfma32(ld16(&Vs[off]), doreg[s], pacc);
       }
+      pacc = mfma32(a_one, b_negd, pacc);  // pacc = dP - D
       float dsv[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float p = fast_exp2(fmaf(sacc[i], c, -lse2));
-        dsv[i] = p * (pacc[i] - Dq);
+        dsv[i] = p * pacc[i];
       }
       if (lim < C::BN) {  // keys past the end: dS = 0
 #pragma unroll
@@ -335,24 +346,26 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(AttnArgs a) {
   // Rows past the end of the sequence are loaded as copies of its last row
   // (finite, in bounds); their LSE is set to +inf so that P = 0.
   auto issue = [&](int qb) {
-    const int q0 = qb * C::BQ;
+    const int q0 = qb * C::BQ, lim = L - q0;
+    const uint16_t* __restrict__ Qb = Qg + (int64_t)q0 * rs;
+    const uint16_t* __restrict__ Ob = dOg + (int64_t)q0 * rs;
+    const float2* __restrict__ Rb = a.rope + q0 * (D / 2);
 #pragma unroll
     for (int x = 0; x < C::QU; ++x) {
       const int u = tid + 256 * x;
       if (C::Q_UNITS % 256 == 0 || u < C::Q_UNITS) {
-        const int row = u / (D / 16), j0 = (u % (D / 16)) * 8;
-        const int qq = min(q0 + row, L - 1);
-        ql[x] = ld16(Qg + qq * rs + j0);
-        qh[x] = ld16(Qg + qq * rs + j0 + D / 2);
-        if (ROPE) load_cs8(a.rope, qq * (D / 2) + j0, qcs[x]);
+        const int row = min(u / (D / 16), lim - 1), j0 = (u % (D / 16)) * 8;
+        ql[x] = ld16(Qb + row * rs + j0);
+        qh[x] = ld16(Qb + row * rs + j0 + D / 2);
+        if (ROPE) load_cs8(Rb, row * (D / 2) + j0, qcs[x]);
       }
     }
 #pragma unroll
     for (int x = 0; x < C::OU; ++x) {
       const int u = tid + 256 * x;
       if (C::O_UNITS % 256 == 0 || u < C::O_UNITS) {
-        const int row = u / (D / 8), c8 = (u % (D / 8)) * 8;
-        ov[x] = ld16(dOg + min(q0 + row, L - 1) * rs + c8);
+        const int row = min(u / (D / 8), lim - 1), c8 = (u % (D / 8)) * 8;
+        ov[x] = ld16(Ob + row * rs + c8);
       }
     }
     if (tid < C::BQ) {

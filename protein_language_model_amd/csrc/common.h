@@ -153,6 +153,15 @@ __device__ __forceinline__ u32x4 ld_tr8(const uint16_t* T, int pitch, int k0, in
   return out;
 }
 
+// -x as a pair of bf16 values (hi, lo) with hi + lo = -x to about 2^-17
+// relative, packed low half first: one MFMA k-slot pair against (1, 1)
+// subtracts x from an fp32 accumulator.
+__device__ __forceinline__ uint32_t neg_bf16_pair(float x) {
+  const float hi = __uint_as_float(pack_bf16(-x, 0.f) << 16);
+  return pack_bf16(hi, -x - hi);
+}
+constexpr uint32_t kBf16OnePair = 0x3f803f80u;  // (1.0, 1.0) in bf16
+
 // sum += x.lo + x.hi for a packed bf16 pair (v_dot2c_f32_bf16 against (1, 1)).
 __device__ __forceinline__ float add_bf16x2(uint32_t x, float sum) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x),

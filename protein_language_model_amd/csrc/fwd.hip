@@ -52,7 +52,7 @@ struct FwdCfg {
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
 template <int D, bool ROPE>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, D == 128 ? 2 : 3) void fwd_kernel(AttnArgs a) {
   using C = FwdCfg<D>;
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS];
 
@@ -103,24 +103,27 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a) {
   // Rows past the end of the sequence are loaded as copies of its last row
   // (finite values, always in bounds); the softmax gives them P = 0.
   auto issue = [&](int kb) {
-    const int k0 = kb * C::BN;
+    const int k0 = kb * C::BN, lim = L - k0;
+    // uniform block bases (scalar registers) + per-lane 32-bit row offsets
+    const uint16_t* __restrict__ Kb = Kg + (int64_t)k0 * rs;
+    const uint16_t* __restrict__ Vb = Vg + (int64_t)k0 * rs;
+    const float2* __restrict__ Rb = a.rope + k0 * (D / 2);
 #pragma unroll
     for (int x = 0; x < C::KU; ++x) {
       const int u = tid + 256 * x;
       if (C::K_UNITS % 256 == 0 || u < C::K_UNITS) {
-        const int row = u / (D / 16), j0 = (u % (D / 16)) * 8;
-        const int key = min(k0 + row, L - 1);
-        kl[x] = ld16(Kg + key * rs + j0);
-        kh[x] = ld16(Kg + key * rs + j0 + D / 2);
-        if (ROPE) load_cs8(a.rope, key * (D / 2) + j0, kcs[x]);
+        const int row = min(u / (D / 16), lim - 1), j0 = (u % (D / 16)) * 8;
+        kl[x] = ld16(Kb + row * rs + j0);
+        kh[x] = ld16(Kb + row * rs + j0 + D / 2);
+        if (ROPE) load_cs8(Rb, row * (D / 2) + j0, kcs[x]);
       }
     }
 #pragma unroll
     for (int x = 0; x < C::VU; ++x) {
       const int u = tid + 256 * x;
       if (C::V_UNITS % 256 == 0 || u < C::V_UNITS) {
-        const int row = u / (D / 8), c8 = (u % (D / 8)) * 8;
-        vv[x] = ld16(Vg + min(k0 + row, L - 1) * rs + c8);
+        const int row = min(u / (D / 8), lim - 1), c8 = (u % (D / 8)) * 8;
+        vv[x] = ld16(Vb + row * rs + c8);
       }
     }
   };
