@@ -1,8 +1,9 @@
 """Benchmark of the varlen RoPE attention hot path on one MI355X.
 
 A step is one pass of the whole path over one packed batch held in HBM:
-plan (varlen schedule + rotary table), forward (O, LSE), backward dq pass
-(with D = rowsum(dO*O) and the inverse-rotation finalize) and dk/dv pass.
+plan (varlen schedule + rotary table), rotation of q and k, forward (O, LSE),
+backward dq pass (with D = rowsum(dO*O) and the inverse-rotation finalize)
+and dk/dv pass.
 The default workload is the ESM-2-650M-shaped dense batch: 16 sequences of
 1024 tokens, 20 heads, head dim 64, bf16, RoPE base 10000.
 
@@ -154,34 +155,37 @@ def main():
     cu = torch.from_numpy(inp["cu_seqlens"]).to(dev)
     o = torch.empty_like(q)
     lse = torch.empty((H, T), dtype=torch.float32, device=dev)
+    qr, kr = torch.empty_like(q), torch.empty_like(k)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    drow = torch.empty((H, T), dtype=torch.float32, device=dev)
+    drow = torch.empty((2, H, T), dtype=torch.float32, device=dev)
     plan = torch.empty(E.esm_attn_plan_bytes(B, T, maxL, H, d), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
+    names = ["plan", "rotate", "fwd", "bwd_dq", "bwd_dkv"]
 
     def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+        def mark(j):
+            if ev is not None:
+                ev[j].record(stream)
+        mark(0)
         E.esm_attn_plan(cu, T, maxL, H, d, base, plan=plan)
-        if ev is not None:
-            ev[1].record(stream)
-        E.esm_attn_fwd_planned(q, k, v, B, maxL, plan, scale, base, out=o, lse=lse)
-        if ev is not None:
-            ev[2].record(stream)
-        E.esm_attn_bwd_planned(q, k, v, o, do, lse, B, maxL, plan, scale, base, dq=dq,
+        mark(1)
+        E.esm_attn_rotate_planned(q, k, B, maxL, plan, base, q_rot=qr, k_rot=kr)
+        mark(2)
+        E.esm_attn_fwd_planned(qr, kr, v, B, maxL, plan, scale, out=o, lse=lse)
+        mark(3)
+        E.esm_attn_bwd_planned(qr, kr, v, o, do, lse, B, maxL, plan, scale, base, dq=dq,
                                drow=drow, passes=E.PASS_DQ)
-        if ev is not None:
-            ev[3].record(stream)
-        E.esm_attn_bwd_planned(q, k, v, o, do, lse, B, maxL, plan, scale, base, dk=dk, dv=dv,
+        mark(4)
+        E.esm_attn_bwd_planned(qr, kr, v, o, do, lse, B, maxL, plan, scale, base, dk=dk, dv=dv,
                                drow=drow, passes=E.PASS_DKV)
-        if ev is not None:
-            ev[4].record(stream)
+        mark(5)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+              for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -189,7 +193,6 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    names = ["plan", "fwd", "bwd_dq", "bwd_dkv"]
     per = {n: [] for n in names}
     for ev in events:
         for j, n in enumerate(names):

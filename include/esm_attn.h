@@ -78,7 +78,7 @@
 extern "C" {
 #endif
 
-#define ESM_ATTN_ABI_VERSION 1
+#define ESM_ATTN_ABI_VERSION 2
 
 typedef int32_t esm_attn_status_t;
 #define ESM_ATTN_OK 0
@@ -95,8 +95,9 @@ const char* esm_attn_status_string(esm_attn_status_t status);
 
 /* Workspace bytes that esm_attn_fwd / esm_attn_bwd need for these sizes
  * (a pure host computation; 0 for arguments the calls would reject). The
- * workspace holds the rotary cos/sin table, the work-item schedule and, for
- * the backward, the row sums D = rowsum(dO * O), fp32 [H][T]. */
+ * workspace holds the plan (rotary cos/sin table and work-item schedule), the
+ * rotated q~ and k~ (bf16 [T][H][d] each) and, for the backward, drow
+ * (fp32 [2][H][T]: the row sums D = rowsum(dO * O), then LSE * log2(e)). */
 size_t esm_attn_fwd_workspace_bytes(int32_t batch, int32_t total_tokens,
                                     int32_t max_seqlen, int32_t num_heads,
                                     int32_t head_dim);
@@ -132,18 +133,23 @@ esm_attn_status_t esm_attn_bwd(
     void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---- plan / execute split ------------------------------------------------
- * esm_attn_fwd and esm_attn_bwd each build a plan (the work-item schedule for
- * cu_seqlens and the rotary cos/sin table) in their workspace before their
- * kernels run. A caller that runs the forward and backward of one batch can
- * build the plan once and pass it to both planned calls instead.
+ * esm_attn_fwd and esm_attn_bwd each run three steps on their workspace:
+ *   1. plan   : the work-item schedule for cu_seqlens and the rotary cos/sin
+ *               table (esm_attn_plan);
+ *   2. rotate : q~ = bf16(R(p) q) and k~ = bf16(R(p) k), once per token
+ *               (esm_attn_rotate_planned; skipped when rope_base = 0, where
+ *               q~ = q and k~ = k);
+ *   3. the attention kernels on q~, k~ (esm_attn_fwd_planned,
+ *      esm_attn_bwd_planned).
+ * A caller that runs the forward and backward of one batch can run steps 1
+ * and 2 once and keep q~ and k~ (instead of q and k) for the backward.
  *
- * esm_attn_plan enqueues the two planning kernels; the plan buffer is device
- * memory of esm_attn_plan_bytes() bytes, owned by the caller, valid for the
- * sizes, cu_seqlens contents and rope_base it was built with, and read-only
- * for the planned calls (several may use one plan, on one stream or after
- * proper stream ordering). The planned calls do not read cu_seqlens; they
- * take the same sizes, scale and rope_base (a different rope_base than the
- * plan's gives wrong values, not an error). */
+ * The plan buffer is device memory of esm_attn_plan_bytes() bytes, owned by
+ * the caller, valid for the sizes, cu_seqlens contents and rope_base it was
+ * built with, and read-only for the other planned calls (several may use one
+ * plan, on one stream or after proper stream ordering). The planned calls do
+ * not read cu_seqlens; they take the same sizes (a different rope_base than
+ * the plan's gives wrong values, not an error). */
 size_t esm_attn_plan_bytes(int32_t batch, int32_t total_tokens, int32_t max_seqlen,
                            int32_t num_heads, int32_t head_dim);
 
@@ -152,25 +158,42 @@ esm_attn_status_t esm_attn_plan(const int32_t* cu_seqlens, int32_t batch,
                                 int32_t num_heads, int32_t head_dim, float rope_base,
                                 void* plan, size_t plan_bytes, void* stream);
 
-/* Forward kernel only (esm_attn_fwd minus planning). */
-esm_attn_status_t esm_attn_fwd_planned(
-    const uint16_t* q, const uint16_t* k, const uint16_t* v,
+/* Rotary embedding of q and k (RoFormer's rotation with x_j paired with
+ * x_{j+d/2}, angles p * rope_base^(-2j/d) from the plan's table): every
+ * element pair is turned in float32 (products and sums rounded one by one) and
+ * rounded once to bf16, round to nearest even. Writes q_rot and k_rot, bf16
+ * [T][H][d]; with rope_base = 0 it copies. q_rot and k_rot must not alias
+ * q or k. */
+esm_attn_status_t esm_attn_rotate_planned(
+    const uint16_t* q, const uint16_t* k,
     int32_t batch, int32_t total_tokens, int32_t max_seqlen,
-    int32_t num_heads, int32_t head_dim,
-    float softmax_scale, float rope_base,
+    int32_t num_heads, int32_t head_dim, float rope_base,
+    uint16_t* q_rot, uint16_t* k_rot,
+    const void* plan, size_t plan_bytes, void* stream);
+
+/* Forward on rotated operands: q_rot and k_rot as esm_attn_rotate_planned
+ * wrote them (or q and k themselves without rotary embedding). Writes o and
+ * lse as esm_attn_fwd does. */
+esm_attn_status_t esm_attn_fwd_planned(
+    const uint16_t* q_rot, const uint16_t* k_rot, const uint16_t* v,
+    int32_t batch, int32_t total_tokens, int32_t max_seqlen,
+    int32_t num_heads, int32_t head_dim, float softmax_scale,
     uint16_t* o, float* lse,
     const void* plan, size_t plan_bytes, void* stream);
 
-/* Backward passes only. drow: caller-provided fp32 [H][T] buffer for the row
- * sums D = rowsum(dO * O). passes is a bit mask: ESM_ATTN_PASS_DQ runs the
- * dq pass (writes dq and drow), ESM_ATTN_PASS_DKV the dk/dv pass (reads drow,
- * writes dk and dv); both bits give the full backward. Running the dk/dv pass
- * alone requires a completed dq pass of the same inputs. Pointers a pass does
- * not use may be NULL. */
+/* Backward on rotated operands (q_rot, k_rot as for the forward; dq and dk
+ * are still the gradients with respect to the pre-rotation q and k: the
+ * kernels apply R(p)^T, for which they need rope_base). drow: caller-provided
+ * fp32 [2][H][T] buffer (D = rowsum(dO * O), then LSE * log2(e)). passes is a
+ * bit mask: ESM_ATTN_PASS_DQ runs the dq pass (reads o and lse, writes dq and
+ * drow), ESM_ATTN_PASS_DKV the dk/dv pass (reads drow, writes dk and dv);
+ * both bits give the full backward. Running the dk/dv pass alone requires a
+ * completed dq pass of the same inputs. Pointers a pass does not use may be
+ * NULL. */
 #define ESM_ATTN_PASS_DQ 1
 #define ESM_ATTN_PASS_DKV 2
 esm_attn_status_t esm_attn_bwd_planned(
-    const uint16_t* q, const uint16_t* k, const uint16_t* v,
+    const uint16_t* q_rot, const uint16_t* k_rot, const uint16_t* v,
     const uint16_t* o, const uint16_t* d_o, const float* lse,
     int32_t batch, int32_t total_tokens, int32_t max_seqlen,
     int32_t num_heads, int32_t head_dim,

@@ -17,7 +17,8 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t rope = 0, sorted = 0, chunk = 0, items = 0, drow = 0, total = 0;
+  size_t rope = 0, sorted = 0, chunk = 0, items = 0, plan = 0;  // the plan
+  size_t drow = 0, qrot = 0, krot = 0, total = 0;                // one-shot calls only
   int64_t n_slots = 0;
   int32_t n_chunks = 0;
 };
@@ -37,6 +38,8 @@ esm_attn_status_t check_sizes(int32_t B, int32_t T, int32_t maxL, int32_t H, int
   return ESM_ATTN_OK;
 }
 
+// Plan = rotary table + schedule. The one-shot calls append the rotated q~
+// and k~ ([T][H][d] bf16 each) and, for the backward, drow ([2][H][T] fp32).
 Layout make_layout(int32_t B, int32_t T, int32_t maxL, int32_t H, int32_t d, bool bwd) {
   Layout l;
   l.n_chunks = (int32_t)schedule_num_chunks(B, H);
@@ -51,7 +54,11 @@ Layout make_layout(int32_t B, int32_t T, int32_t maxL, int32_t H, int32_t d, boo
   l.sorted = take((size_t)B * sizeof(int32_t));
   l.chunk = take((size_t)(l.n_chunks + 1) * sizeof(int32_t));
   l.items = take((size_t)(l.n_slots > 0 ? l.n_slots : 1) * sizeof(Item));
-  if (bwd) l.drow = take((size_t)T * H * sizeof(float));
+  l.plan = off;
+  const size_t elems = (size_t)T * H * d;
+  l.qrot = take(elems * sizeof(uint16_t));
+  l.krot = take(elems * sizeof(uint16_t));
+  if (bwd) l.drow = take((size_t)2 * T * H * sizeof(float));
   l.total = off;
   return l;
 }
@@ -128,7 +135,8 @@ size_t esm_attn_bwd_workspace_bytes(int32_t batch, int32_t total_tokens, int32_t
 
 size_t esm_attn_plan_bytes(int32_t batch, int32_t total_tokens, int32_t max_seqlen,
                            int32_t num_heads, int32_t head_dim) {
-  return esm_attn_fwd_workspace_bytes(batch, total_tokens, max_seqlen, num_heads, head_dim);
+  if (check_sizes(batch, total_tokens, max_seqlen, num_heads, head_dim) != ESM_ATTN_OK) return 0;
+  return make_layout(batch, total_tokens, max_seqlen, num_heads, head_dim, false).plan;
 }
 
 esm_attn_status_t esm_attn_plan(const int32_t* cu_seqlens, int32_t batch, int32_t total_tokens,
@@ -141,49 +149,77 @@ esm_attn_status_t esm_attn_plan(const int32_t* cu_seqlens, int32_t batch, int32_
   if (cu_seqlens == nullptr || !aligned16(cu_seqlens) || plan == nullptr || !aligned16(plan))
     return ESM_ATTN_ERR_INVALID_ARGUMENT;
   const Layout l = make_layout(batch, total_tokens, max_seqlen, num_heads, head_dim, false);
-  if (plan_bytes < l.total) return ESM_ATTN_ERR_WORKSPACE_TOO_SMALL;
+  if (plan_bytes < l.plan) return ESM_ATTN_ERR_WORKSPACE_TOO_SMALL;
   return run_prep(cu_seqlens, batch, total_tokens, max_seqlen, num_heads, head_dim, rope_base, l,
                   static_cast<char*>(plan), reinterpret_cast<hipStream_t>(stream));
 }
 
-esm_attn_status_t esm_attn_fwd_planned(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                       int32_t batch, int32_t total_tokens, int32_t max_seqlen,
-                                       int32_t num_heads, int32_t head_dim, float softmax_scale,
-                                       float rope_base, uint16_t* o, float* lse, const void* plan,
-                                       size_t plan_bytes, void* stream) {
+esm_attn_status_t esm_attn_rotate_planned(const uint16_t* q, const uint16_t* k, int32_t batch,
+                                          int32_t total_tokens, int32_t max_seqlen,
+                                          int32_t num_heads, int32_t head_dim, float rope_base,
+                                          uint16_t* q_rot, uint16_t* k_rot, const void* plan,
+                                          size_t plan_bytes, void* stream) {
   esm_attn_status_t s = check_sizes(batch, total_tokens, max_seqlen, num_heads, head_dim);
   if (s != ESM_ATTN_OK) return s;
-  if ((s = check_scalars(softmax_scale, rope_base)) != ESM_ATTN_OK) return s;
+  if ((s = check_scalars(0.f, rope_base)) != ESM_ATTN_OK) return s;
   if (total_tokens == 0) return ESM_ATTN_OK;
-  const void* ptrs[] = {q, k, v, o, lse, plan};
+  const void* ptrs[] = {q, k, q_rot, k_rot, plan};
   for (const void* p : ptrs)
     if (p == nullptr || !aligned16(p)) return ESM_ATTN_ERR_INVALID_ARGUMENT;
   const Layout l = make_layout(batch, total_tokens, max_seqlen, num_heads, head_dim, false);
-  if (plan_bytes < l.total) return ESM_ATTN_ERR_WORKSPACE_TOO_SMALL;
-  if (max_seqlen == 0) return ESM_ATTN_OK;  // every sequence is empty
+  if (plan_bytes < l.plan) return ESM_ATTN_ERR_WORKSPACE_TOO_SMALL;
+  if (max_seqlen == 0) return ESM_ATTN_OK;
   const char* ws = static_cast<const char*>(plan);
-  AttnArgs a = {};
+  RotArgs a = {};
   a.q = q;
   a.k = k;
-  a.v = v;
-  a.out = o;
-  a.lse = lse;
+  a.q_rot = q_rot;
+  a.k_rot = k_rot;
   a.rope = reinterpret_cast<const float2*>(ws + l.rope);
   a.items = reinterpret_cast<const Item*>(ws + l.items);
-  fill_common(&a, total_tokens, num_heads, softmax_scale);
-  if (launch_fwd(head_dim, rope_base != 0.f, a, l.n_slots, reinterpret_cast<hipStream_t>(stream)) !=
-      hipSuccess)
+  a.H = num_heads;
+  if (launch_rotate(head_dim, rope_base != 0.f, a, l.n_slots,
+                    reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
     return ESM_ATTN_ERR_HIP;
   return ESM_ATTN_OK;
 }
 
-esm_attn_status_t esm_attn_bwd_planned(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                       const uint16_t* o, const uint16_t* d_o, const float* lse,
-                                       int32_t batch, int32_t total_tokens, int32_t max_seqlen,
-                                       int32_t num_heads, int32_t head_dim, float softmax_scale,
-                                       float rope_base, uint16_t* dq, uint16_t* dk, uint16_t* dv,
-                                       float* drow, int32_t passes, const void* plan,
-                                       size_t plan_bytes, void* stream) {
+esm_attn_status_t esm_attn_fwd_planned(const uint16_t* q_rot, const uint16_t* k_rot,
+                                       const uint16_t* v, int32_t batch, int32_t total_tokens,
+                                       int32_t max_seqlen, int32_t num_heads, int32_t head_dim,
+                                       float softmax_scale, uint16_t* o, float* lse,
+                                       const void* plan, size_t plan_bytes, void* stream) {
+  esm_attn_status_t s = check_sizes(batch, total_tokens, max_seqlen, num_heads, head_dim);
+  if (s != ESM_ATTN_OK) return s;
+  if ((s = check_scalars(softmax_scale, 0.f)) != ESM_ATTN_OK) return s;
+  if (total_tokens == 0) return ESM_ATTN_OK;
+  const void* ptrs[] = {q_rot, k_rot, v, o, lse, plan};
+  for (const void* p : ptrs)
+    if (p == nullptr || !aligned16(p)) return ESM_ATTN_ERR_INVALID_ARGUMENT;
+  const Layout l = make_layout(batch, total_tokens, max_seqlen, num_heads, head_dim, false);
+  if (plan_bytes < l.plan) return ESM_ATTN_ERR_WORKSPACE_TOO_SMALL;
+  if (max_seqlen == 0) return ESM_ATTN_OK;  // every sequence is empty
+  const char* ws = static_cast<const char*>(plan);
+  AttnArgs a = {};
+  a.q = q_rot;
+  a.k = k_rot;
+  a.v = v;
+  a.out = o;
+  a.lse = lse;
+  a.items = reinterpret_cast<const Item*>(ws + l.items);
+  fill_common(&a, total_tokens, num_heads, softmax_scale);
+  if (launch_fwd(head_dim, a, l.n_slots, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return ESM_ATTN_ERR_HIP;
+  return ESM_ATTN_OK;
+}
+
+esm_attn_status_t esm_attn_bwd_planned(const uint16_t* q_rot, const uint16_t* k_rot,
+                                       const uint16_t* v, const uint16_t* o, const uint16_t* d_o,
+                                       const float* lse, int32_t batch, int32_t total_tokens,
+                                       int32_t max_seqlen, int32_t num_heads, int32_t head_dim,
+                                       float softmax_scale, float rope_base, uint16_t* dq,
+                                       uint16_t* dk, uint16_t* dv, float* drow, int32_t passes,
+                                       const void* plan, size_t plan_bytes, void* stream) {
   esm_attn_status_t s = check_sizes(batch, total_tokens, max_seqlen, num_heads, head_dim);
   if (s != ESM_ATTN_OK) return s;
   if ((s = check_scalars(softmax_scale, rope_base)) != ESM_ATTN_OK) return s;
@@ -191,20 +227,21 @@ esm_attn_status_t esm_attn_bwd_planned(const uint16_t* q, const uint16_t* k, con
     return ESM_ATTN_ERR_INVALID_ARGUMENT;
   if (total_tokens == 0) return ESM_ATTN_OK;
   const bool pdq = passes & ESM_ATTN_PASS_DQ, pdkv = passes & ESM_ATTN_PASS_DKV;
-  const void* common[] = {q, k, v, lse, d_o, drow, plan};
+  const void* common[] = {q_rot, k_rot, v, d_o, drow, plan};
   for (const void* p : common)
     if (p == nullptr || !aligned16(p)) return ESM_ATTN_ERR_INVALID_ARGUMENT;
-  if (pdq && (o == nullptr || !aligned16(o) || dq == nullptr || !aligned16(dq)))
+  if (pdq && (o == nullptr || !aligned16(o) || lse == nullptr || !aligned16(lse) ||
+              dq == nullptr || !aligned16(dq)))
     return ESM_ATTN_ERR_INVALID_ARGUMENT;
   if (pdkv && (dk == nullptr || !aligned16(dk) || dv == nullptr || !aligned16(dv)))
     return ESM_ATTN_ERR_INVALID_ARGUMENT;
   const Layout l = make_layout(batch, total_tokens, max_seqlen, num_heads, head_dim, false);
-  if (plan_bytes < l.total) return ESM_ATTN_ERR_WORKSPACE_TOO_SMALL;
+  if (plan_bytes < l.plan) return ESM_ATTN_ERR_WORKSPACE_TOO_SMALL;
   if (max_seqlen == 0) return ESM_ATTN_OK;
   const char* ws = static_cast<const char*>(plan);
   AttnArgs a = {};
-  a.q = q;
-  a.k = k;
+  a.q = q_rot;
+  a.k = k_rot;
   a.v = v;
   a.o = o;
   a.dout = d_o;
@@ -237,11 +274,19 @@ esm_attn_status_t esm_attn_fwd(const uint16_t* q, const uint16_t* k, const uint1
   const Layout l = make_layout(batch, total_tokens, max_seqlen, num_heads, head_dim, false);
   if (workspace_bytes < l.total) return ESM_ATTN_ERR_WORKSPACE_TOO_SMALL;
   if (max_seqlen == 0) return ESM_ATTN_OK;
+  char* ws = static_cast<char*>(workspace);
+  uint16_t* qr = reinterpret_cast<uint16_t*>(ws + l.qrot);
+  uint16_t* kr = reinterpret_cast<uint16_t*>(ws + l.krot);
+  const bool rope = rope_base != 0.f;
   if ((s = esm_attn_plan(cu_seqlens, batch, total_tokens, max_seqlen, num_heads, head_dim,
-                         rope_base, workspace, workspace_bytes, stream)) != ESM_ATTN_OK)
+                         rope_base, ws, l.plan, stream)) != ESM_ATTN_OK)
     return s;
-  return esm_attn_fwd_planned(q, k, v, batch, total_tokens, max_seqlen, num_heads, head_dim,
-                              softmax_scale, rope_base, o, lse, workspace, workspace_bytes, stream);
+  if (rope && (s = esm_attn_rotate_planned(q, k, batch, total_tokens, max_seqlen, num_heads,
+                                           head_dim, rope_base, qr, kr, ws, l.plan, stream)) !=
+                  ESM_ATTN_OK)
+    return s;
+  return esm_attn_fwd_planned(rope ? qr : q, rope ? kr : k, v, batch, total_tokens, max_seqlen,
+                              num_heads, head_dim, softmax_scale, o, lse, ws, l.plan, stream);
 }
 
 esm_attn_status_t esm_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
@@ -262,13 +307,20 @@ esm_attn_status_t esm_attn_bwd(const uint16_t* q, const uint16_t* k, const uint1
   if (workspace_bytes < l.total) return ESM_ATTN_ERR_WORKSPACE_TOO_SMALL;
   if (max_seqlen == 0) return ESM_ATTN_OK;
   char* ws = static_cast<char*>(workspace);
+  uint16_t* qr = reinterpret_cast<uint16_t*>(ws + l.qrot);
+  uint16_t* kr = reinterpret_cast<uint16_t*>(ws + l.krot);
+  const bool rope = rope_base != 0.f;
   if ((s = esm_attn_plan(cu_seqlens, batch, total_tokens, max_seqlen, num_heads, head_dim,
-                         rope_base, ws, l.drow, stream)) != ESM_ATTN_OK)
+                         rope_base, ws, l.plan, stream)) != ESM_ATTN_OK)
     return s;
-  return esm_attn_bwd_planned(q, k, v, o, d_o, lse, batch, total_tokens, max_seqlen, num_heads,
-                              head_dim, softmax_scale, rope_base, dq, dk, dv,
-                              reinterpret_cast<float*>(ws + l.drow),
-                              ESM_ATTN_PASS_DQ | ESM_ATTN_PASS_DKV, ws, l.drow, stream);
+  if (rope && (s = esm_attn_rotate_planned(q, k, batch, total_tokens, max_seqlen, num_heads,
+                                           head_dim, rope_base, qr, kr, ws, l.plan, stream)) !=
+                  ESM_ATTN_OK)
+    return s;
+  return esm_attn_bwd_planned(rope ? qr : q, rope ? kr : k, v, o, d_o, lse, batch, total_tokens,
+                              max_seqlen, num_heads, head_dim, softmax_scale, rope_base, dq, dk,
+                              dv, reinterpret_cast<float*>(ws + l.drow),
+                              ESM_ATTN_PASS_DQ | ESM_ATTN_PASS_DKV, ws, l.plan, stream);
 }
 
 esm_attn_status_t esm_attn_check_cu_seqlens_host(const int32_t* cu, int32_t batch,

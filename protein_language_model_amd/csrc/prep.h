@@ -22,10 +22,25 @@ struct PrepArgs {
 
 hipError_t launch_prep(const PrepArgs& a, hipStream_t stream);
 
-// Everything the attention kernels read. Pointers to bf16 data are uint16_t.
-struct AttnArgs {
+// Rotation pass: q_rot = bf16(R(p) q), k_rot = bf16(R(p) k), or copies when
+// rope is null.
+struct RotArgs {
   const uint16_t* q;
   const uint16_t* k;
+  uint16_t* q_rot;
+  uint16_t* k_rot;
+  const float2* rope;   // [max_seqlen][d/2]
+  const Item* items;
+  int32_t H;
+};
+
+hipError_t launch_rotate(int head_dim, bool rope, const RotArgs& a, int64_t n_slots,
+                         hipStream_t stream);
+
+// Everything the attention kernels read. Pointers to bf16 data are uint16_t.
+struct AttnArgs {
+  const uint16_t* q;    // rotated q~
+  const uint16_t* k;    // rotated k~
   const uint16_t* v;
   const uint16_t* o;    // backward: forward output
   const uint16_t* dout; // backward: dO
@@ -35,7 +50,7 @@ struct AttnArgs {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
-  float* drow;          // backward: D = rowsum(dO * O), [H][T]
+  float* drow;          // backward: [2][H][T]: D = rowsum(dO * O), then LSE * log2(e)
   const float2* rope;   // [max_seqlen][d/2]
   const Item* items;
   int32_t T, H;
@@ -45,8 +60,7 @@ struct AttnArgs {
   float scale_abs;
 };
 
-hipError_t launch_fwd(int head_dim, bool rope, const AttnArgs& a, int64_t n_slots,
-                      hipStream_t stream);
+hipError_t launch_fwd(int head_dim, const AttnArgs& a, int64_t n_slots, hipStream_t stream);
 hipError_t launch_bwd(int head_dim, bool rope, const AttnArgs& a, int64_t n_slots, bool dq_pass,
                       bool dkv_pass, hipStream_t stream);
 

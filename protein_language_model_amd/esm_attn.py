@@ -10,8 +10,10 @@ Functions keep the C names:
       -> (o, lse)
   esm_attn_bwd(q, k, v, o, d_o, lse, cu_seqlens, max_seqlen, softmax_scale,
                rope_base) -> (dq, dk, dv)
-plus the workspace queries, esm_attn_check_cu_seqlens_host,
-esm_attn_schedule_host, and `attention`, an autograd wrapper over the two.
+the planned steps (esm_attn_plan, esm_attn_rotate_planned,
+esm_attn_fwd_planned, esm_attn_bwd_planned), the workspace queries,
+esm_attn_check_cu_seqlens_host, esm_attn_schedule_host, and `attention`, an
+autograd wrapper over the planned steps.
 """
 
 import ctypes
@@ -35,6 +37,7 @@ EXPORTED = (
     "esm_attn_bwd",
     "esm_attn_plan_bytes",
     "esm_attn_plan",
+    "esm_attn_rotate_planned",
     "esm_attn_fwd_planned",
     "esm_attn_bwd_planned",
     "esm_attn_check_cu_seqlens_host",
@@ -85,9 +88,12 @@ def lib():
                                vp, vp, vp, vp, u64, vp]
     L.esm_attn_plan.restype = i32
     L.esm_attn_plan.argtypes = [vp, i32, i32, i32, i32, i32, f32, vp, u64, vp]
+    L.esm_attn_rotate_planned.restype = i32
+    L.esm_attn_rotate_planned.argtypes = [vp, vp, i32, i32, i32, i32, i32, f32, vp, vp, vp, u64,
+                                          vp]
     L.esm_attn_fwd_planned.restype = i32
-    L.esm_attn_fwd_planned.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, f32, f32, vp, vp,
-                                       vp, u64, vp]
+    L.esm_attn_fwd_planned.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, f32, vp, vp, vp, u64,
+                                       vp]
     L.esm_attn_bwd_planned.restype = i32
     L.esm_attn_bwd_planned.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32,
                                        f32, vp, vp, vp, vp, i32, vp, u64, vp]
@@ -207,34 +213,50 @@ def esm_attn_plan(cu_seqlens, total_tokens, max_seqlen, num_heads, head_dim,
     return plan
 
 
-def esm_attn_fwd_planned(q, k, v, batch, max_seqlen, plan, softmax_scale=None,
-                         rope_base=10000.0, out=None, lse=None, stream=None):
-    T, H, d = _check_qkv(q, k, v)
+def esm_attn_rotate_planned(q, k, batch, max_seqlen, plan, rope_base=10000.0, q_rot=None,
+                            k_rot=None, stream=None):
+    """q~ = bf16(R(p) q), k~ = bf16(R(p) k) with the plan's rotary table;
+    returns (q_rot, k_rot)."""
+    T, H, d = _check_qkv(q, k)
+    q_rot = torch.empty_like(q) if q_rot is None else q_rot
+    k_rot = torch.empty_like(k) if k_rot is None else k_rot
+    _check(lib().esm_attn_rotate_planned(_ptr(q), _ptr(k), int(batch), T, int(max_seqlen), H, d,
+                                         float(rope_base), _ptr(q_rot), _ptr(k_rot), _ptr(plan),
+                                         plan.numel(), _stream(stream)))
+    return q_rot, k_rot
+
+
+def esm_attn_fwd_planned(q_rot, k_rot, v, batch, max_seqlen, plan, softmax_scale=None,
+                         out=None, lse=None, stream=None):
+    """Forward on rotated q~, k~ (esm_attn_rotate_planned's outputs)."""
+    T, H, d = _check_qkv(q_rot, k_rot, v)
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty_like(v)
     if lse is None:
-        lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
-    _check(lib().esm_attn_fwd_planned(_ptr(q), _ptr(k), _ptr(v), int(batch), T, int(max_seqlen),
-                                      H, d, scale, float(rope_base), _ptr(out), _ptr(lse),
+        lse = torch.empty((H, T), dtype=torch.float32, device=v.device)
+    _check(lib().esm_attn_fwd_planned(_ptr(q_rot), _ptr(k_rot), _ptr(v), int(batch), T,
+                                      int(max_seqlen), H, d, scale, _ptr(out), _ptr(lse),
                                       _ptr(plan), plan.numel(), _stream(stream)))
     return out, lse
 
 
-def esm_attn_bwd_planned(q, k, v, o, d_o, lse, batch, max_seqlen, plan, softmax_scale=None,
-                         rope_base=10000.0, dq=None, dk=None, dv=None, drow=None,
-                         passes=PASS_DQ | PASS_DKV, stream=None):
-    T, H, d = _check_qkv(q, k, v, d_o)
+def esm_attn_bwd_planned(q_rot, k_rot, v, o, d_o, lse, batch, max_seqlen, plan,
+                         softmax_scale=None, rope_base=10000.0, dq=None, dk=None, dv=None,
+                         drow=None, passes=PASS_DQ | PASS_DKV, stream=None):
+    """Backward on rotated q~, k~; dq and dk are gradients with respect to the
+    pre-rotation q and k. drow: fp32 [2, H, T] scratch shared by the passes."""
+    T, H, d = _check_qkv(q_rot, k_rot, v, d_o)
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     if drow is None:
-        drow = torch.empty((H, T), dtype=torch.float32, device=q.device)
+        drow = torch.empty((2, H, T), dtype=torch.float32, device=v.device)
     if passes & PASS_DQ and dq is None:
-        dq = torch.empty_like(q)
+        dq = torch.empty_like(q_rot)
     if passes & PASS_DKV:
-        dk = torch.empty_like(k) if dk is None else dk
+        dk = torch.empty_like(k_rot) if dk is None else dk
         dv = torch.empty_like(v) if dv is None else dv
-    _check(lib().esm_attn_bwd_planned(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse),
-                                      int(batch), T, int(max_seqlen), H, d, scale,
+    _check(lib().esm_attn_bwd_planned(_ptr(q_rot), _ptr(k_rot), _ptr(v), _ptr(o), _ptr(d_o),
+                                      _ptr(lse), int(batch), T, int(max_seqlen), H, d, scale,
                                       float(rope_base), _ptr(dq), _ptr(dk), _ptr(dv),
                                       _ptr(drow), int(passes), _ptr(plan), plan.numel(),
                                       _stream(stream)))
@@ -265,25 +287,29 @@ def esm_attn_schedule_host(cu, total_tokens, max_seqlen, num_heads, block_rows=1
 
 
 class _Attention(torch.autograd.Function):
-    """The plan (schedule + rotary table) is built once in forward and reused
-    by backward."""
+    """The plan (schedule + rotary table) and the rotated q~, k~ are made once
+    in forward and kept for backward in place of q and k."""
 
     @staticmethod
     def forward(ctx, q, k, v, cu_seqlens, max_seqlen, scale, rope_base):
         T, H, d = _check_qkv(q, k, v)
         B = cu_seqlens.numel() - 1
         plan = esm_attn_plan(cu_seqlens, T, max_seqlen, H, d, rope_base)
-        o, lse = esm_attn_fwd_planned(q, k, v, B, max_seqlen, plan, scale, rope_base)
-        ctx.save_for_backward(q, k, v, o, lse, plan)
+        if rope_base != 0.0:
+            q_rot, k_rot = esm_attn_rotate_planned(q, k, B, max_seqlen, plan, rope_base)
+        else:
+            q_rot, k_rot = q, k
+        o, lse = esm_attn_fwd_planned(q_rot, k_rot, v, B, max_seqlen, plan, scale)
+        ctx.save_for_backward(q_rot, k_rot, v, o, lse, plan)
         ctx.args = (B, max_seqlen, scale, rope_base)
         return o
 
     @staticmethod
     def backward(ctx, grad):
-        q, k, v, o, lse, plan = ctx.saved_tensors
+        q_rot, k_rot, v, o, lse, plan = ctx.saved_tensors
         B, max_seqlen, scale, rope_base = ctx.args
-        dq, dk, dv, _ = esm_attn_bwd_planned(q, k, v, o, grad.contiguous(), lse, B, max_seqlen,
-                                             plan, scale, rope_base)
+        dq, dk, dv, _ = esm_attn_bwd_planned(q_rot, k_rot, v, o, grad.contiguous(), lse, B,
+                                             max_seqlen, plan, scale, rope_base)
         return dq, dk, dv, None, None, None, None
 
 

@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported():
     for n in names:
         assert hasattr(lib, n), n
     assert set(E.EXPORTED) == set(names)
-    assert E.esm_attn_abi_version() == 1
+    assert E.esm_attn_abi_version() == 2
 
 
 def test_single_hip_runtime_is_mapped():
@@ -47,8 +47,12 @@ def test_status_strings():
 def test_workspace_sizes():
     fwd = E.esm_attn_fwd_workspace_bytes(16, 16384, 1024, 20, 64)
     bwd = E.esm_attn_bwd_workspace_bytes(16, 16384, 1024, 20, 64)
-    assert fwd == E.esm_attn_plan_bytes(16, 16384, 1024, 20, 64)
-    assert bwd >= fwd + 16384 * 20 * 4
+    plan = E.esm_attn_plan_bytes(16, 16384, 1024, 20, 64)
+    qk = 2 * 16384 * 20 * 64 * 2            # rotated q~ and k~, bf16
+    assert fwd >= plan + qk
+    assert bwd >= fwd + 2 * 16384 * 20 * 4  # drow: D and LSE log2(e), fp32
+    assert plan >= 1024 * 32 * 8            # rotary table
+    assert E.esm_attn_plan_bytes(16, 16384, 1024, 20, 48) == 0
     assert E.esm_attn_fwd_workspace_bytes(16, 16384, 1024, 20, 48) == 0   # bad head_dim
     assert E.esm_attn_fwd_workspace_bytes(0, 16, 16, 1, 64) == 0
     assert E.esm_attn_fwd_workspace_bytes(1, 16, 70000, 1, 64) == 0        # max_seqlen
@@ -109,8 +113,21 @@ def test_backward_and_planned_validation():
     assert st == E.ERR_INVALID_ARGUMENT      # dq pass without dq
     st = L.esm_attn_plan(p, 1, 8, 8, 1, 32, -5.0, p, 1 << 30, None)
     assert st == E.ERR_INVALID_ARGUMENT
-    st = L.esm_attn_fwd_planned(p, p, p, 1, 8, 8, 1, 32, 0.1, 1e4, p, p, p, 4, None)
+    st = L.esm_attn_fwd_planned(p, p, p, 1, 8, 8, 1, 32, 0.1, p, p, p, 4, None)
     assert st == E.ERR_WORKSPACE_TOO_SMALL
+    st = L.esm_attn_fwd_planned(p, p, p, 1, 8, 8, 1, 32, float("nan"), p, p, p, 1 << 30, None)
+    assert st == E.ERR_INVALID_ARGUMENT
+    # rotation step
+    st = L.esm_attn_rotate_planned(p, p, 1, 8, 8, 1, 32, 1e4, p, p, p, 4, None)
+    assert st == E.ERR_WORKSPACE_TOO_SMALL
+    st = L.esm_attn_rotate_planned(p, p, 1, 8, 8, 1, 32, -1.0, p, p, p, 1 << 30, None)
+    assert st == E.ERR_INVALID_ARGUMENT
+    st = L.esm_attn_rotate_planned(p, p, 1, 8, 8, 1, 32, 1e4, None, p, p, 1 << 30, None)
+    assert st == E.ERR_INVALID_ARGUMENT
+    st = L.esm_attn_rotate_planned(p, p, 1, 8, 8, 1, 48, 1e4, p, p, p, 1 << 30, None)
+    assert st == E.ERR_UNSUPPORTED
+    assert L.esm_attn_rotate_planned(None, None, 1, 0, 0, 1, 32, 1e4, None, None, None, 0,
+                                     None) == E.OK
 
 
 def test_check_cu_seqlens_host():
