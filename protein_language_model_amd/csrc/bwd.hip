@@ -18,9 +18,9 @@
 //             MFMA for dP - D measured slower than the subtraction.)
 // q~ and k~ come rotated from the rotation pass. The streamed operands (k~
 // and v in the dq pass; q~, dO, LSE and D in the dkv pass) are copied from
-// global memory into swizzled LDS tiles by global_load_lds, double-buffered
-// (the next block's copy is issued right after the barrier that opens the
-// current block). Products that contract over the token axis (K~^T, Q~^T,
+// global memory into swizzled LDS tiles by global_load_lds, in a ring of
+// three LDS stages (the copy of block b + 2 is issued right after the barrier
+// that opens block b). Products that contract over the token axis (K~^T, Q~^T,
 // dO^T) read the same row-major tiles with the LDS transpose load.
 #include "common.h"
 #include "prep.h"
@@ -41,9 +41,12 @@ struct DqCfg {
   static constexpr int NU = BN / 16;
   static constexpr int TILE = BN * D;           // k~ tile, then v tile
   static constexpr int STAGE = 2 * TILE;
+  static constexpr int NSTAGE = 3;              // LDS ring of key blocks
   static constexpr int EPI = BM * (D + 4) * 2;  // fp32 tile, in uint16 units
-  static constexpr int LDS = 2 * STAGE > EPI ? 2 * STAGE : EPI;
+  static constexpr int LDS = NSTAGE * STAGE > EPI ? NSTAGE * STAGE : EPI;
   static constexpr int OCC = 2;
+  using Loader = TilePair<D, BN>;
+  static constexpr int LOADS = Loader::LOADS_PER_WAVE;  // per wave and block
 };
 
 template <int D, bool ROPE>
@@ -54,7 +57,8 @@ __global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(AttnArgs a) 
   const Item it = a.items[blockIdx.x];
   if (it.len <= 0) return;
   const int L = it.len, h = it.head, q0 = it.blk * C::BM;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 31, g = lane >> 5, prow = perm_row(r);
   const int rs = a.H * D;  // row stride; T*H*d < 2^31 is checked on the host
   const int64_t base = (int64_t)it.seq0 * rs + (int64_t)h * D;
@@ -64,13 +68,15 @@ __global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(AttnArgs a) 
   const uint16_t* __restrict__ Og = a.o + base;
   const uint16_t* __restrict__ dOg = a.dout + base;
 
-  auto issue = [&](int kb) {
+  // k~ and v rows of key block kb -> LDS stage `stage`
+  const typename C::Loader loader(w, lane);
+  auto issue = [&](int kb, int stage) {
     const int k0 = kb * C::BN;
-    uint16_t* Ks = lds + (kb & 1) * C::STAGE;
-    load_tile<D, C::BN>(Kg + (int64_t)k0 * rs, rs, L - k0, Ks, w, lane);
-    load_tile<D, C::BN>(Vg + (int64_t)k0 * rs, rs, L - k0, Ks + C::TILE, w, lane);
+    uint16_t* Ks = lds + stage * C::STAGE;
+    loader.load(Kg + (int64_t)k0 * rs, Vg + (int64_t)k0 * rs, rs, L - k0, Ks, Ks + C::TILE, w);
   };
-  issue(0);
+  const int nkb = (L + C::BN - 1) / C::BN;
+  issue(0, 0);
 
   // ---- prologue: q~ and dO (B operands), D = dO . O, LSE (log2 units)
   const int qi = q0 + w * 32 + r;  // this lane's query
@@ -110,19 +116,32 @@ __global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(AttnArgs a) 
     }
   }
 
+  // blocks 1 .. NSTAGE-2 after the prologue's global loads (see the wait below)
+#pragma unroll
+  for (int j = 1; j < C::NSTAGE - 1; ++j)
+    if (j < nkb) issue(j, j);
+
   const float c = a.c;
   const int xk = swz<D>(prow);
+  const TrRows<D> kread(lane);  // transposed reads of the k~ tile
   f32x16 dqacc[C::ND];
 #pragma unroll
   for (int dt = 0; dt < C::ND; ++dt) dqacc[dt] = f32x16{};
 
-  const int nkb = (L + C::BN - 1) / C::BN;
+  int stage = 0, next = C::NSTAGE - 1;
   for (int kb = 0; kb < nkb; ++kb) {
-    wait_vmem();
-    __syncthreads();
-    if (kb + 1 < nkb) issue(kb + 1);
-    const uint16_t* Ks = lds + (kb & 1) * C::STAGE;
+    // block kb's copies are done once at most the next block's are
+    // outstanding; the barrier publishes them and frees stage `next`
+    if (C::NSTAGE == 3 && kb + 1 < nkb)
+      wait_vmem<C::LOADS>();
+    else
+      wait_vmem<0>();
+    block_barrier();
+    if (kb + C::NSTAGE - 1 < nkb) issue(kb + C::NSTAGE - 1, next);
+    const uint16_t* Ks = lds + stage * C::STAGE;
     const uint16_t* Vs = Ks + C::TILE;
+    stage = stage + 1 == C::NSTAGE ? 0 : stage + 1;
+    next = next + 1 == C::NSTAGE ? 0 : next + 1;
     const int lim = L - kb * C::BN;  // valid keys in this block
 
     u32x4 dsreg[C::NU];
@@ -156,11 +175,10 @@ __global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(AttnArgs a) 
     }
 #pragma unroll
     for (int dt = 0; dt < C::ND; ++dt) {
+      u32x4 at[C::NU];
+      kread.template read<C::NU>(lds_addr(Ks), dt, at);
 #pragma unroll
-      for (int u = 0; u < C::NU; ++u) {
-        const u32x4 at = ld_tr_tile<D, (D < 32)>(Ks, 32 * (u >> 1) + 8 * (u & 1), 32 * dt, D);
-        dqacc[dt] = mfma32(at, dsreg[u], dqacc[dt]);
-      }
+      for (int u = 0; u < C::NU; ++u) dqacc[dt] = mfma32(at[u], dsreg[u], dqacc[dt]);
     }
   }
   __syncthreads();  // every wave is done with the tiles
@@ -193,9 +211,12 @@ struct DkvCfg {
   static constexpr int NU = BQ / 16;
   static constexpr int TILE = BQ * D;           // q~ tile, then dO tile
   static constexpr int STAGE = 2 * TILE + 4 * BQ;  // + lse2[BQ], D[BQ] as fp32
+  static constexpr int NSTAGE = 3;              // LDS ring of query blocks
   static constexpr int EPI = BK * (D + 4) * 2;
-  static constexpr int LDS = 2 * STAGE > EPI ? 2 * STAGE : EPI;
+  static constexpr int LDS = NSTAGE * STAGE > EPI ? NSTAGE * STAGE : EPI;
   static constexpr int OCC = 2;
+  using Loader = TilePair<D, BQ>;
+  static constexpr int LOADS = Loader::LOADS_PER_WAVE + 1;  // + a half row of lse2 or D
 };
 
 template <int D, bool ROPE>
@@ -206,7 +227,8 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkv_kernel(AttnArgs a
   const Item it = a.items[blockIdx.x];
   if (it.len <= 0) return;
   const int L = it.len, h = it.head, k0 = it.blk * C::BK;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 31, g = lane >> 5, prow = perm_row(r);
   const int rs = a.H * D;  // row stride; T*H*d < 2^31 is checked on the host
   const int64_t base = (int64_t)it.seq0 * rs + (int64_t)h * D;
@@ -215,19 +237,21 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkv_kernel(AttnArgs a
   const uint16_t* __restrict__ Vg = a.v + base;
   const uint16_t* __restrict__ dOg = a.dout + base;
   const int64_t row0 = (int64_t)h * a.T + it.seq0;
-  const float* __restrict__ Dg = a.drow + row0;
-  const float* __restrict__ Lg = a.drow + (int64_t)a.H * a.T + row0;
+  // waves 0-1 copy halves of the lse2 row, waves 2-3 halves of the D row
+  const float* __restrict__ Fg =
+      a.drow + (w < 2 ? (int64_t)a.H * a.T : (int64_t)0) + row0;
 
-  auto issue = [&](int qb) {
+  // q~, dO, lse2 and D rows of query block qb -> LDS stage `stage`
+  const typename C::Loader loader(w, lane);
+  auto issue = [&](int qb, int stage) {
     const int q0 = qb * C::BQ, lim = L - q0;
-    uint16_t* Qs = lds + (qb & 1) * C::STAGE;
-    float* Fs = reinterpret_cast<float*>(Qs + 2 * C::TILE);
-    load_tile<D, C::BQ>(Qg + (int64_t)q0 * rs, rs, lim, Qs, w, lane);
-    load_tile<D, C::BQ>(dOg + (int64_t)q0 * rs, rs, lim, Qs + C::TILE, w, lane);
-    load_row_f32(Lg + q0, C::BQ, lim, Fs, w, 0, lane);
-    load_row_f32(Dg + q0, C::BQ, lim, Fs + C::BQ, w, 1, lane);
+    uint16_t* Qs = lds + stage * C::STAGE;
+    float* Fs = reinterpret_cast<float*>(Qs + 2 * C::TILE) + (w < 2 ? 0 : C::BQ);
+    loader.load(Qg + (int64_t)q0 * rs, dOg + (int64_t)q0 * rs, rs, lim, Qs, Qs + C::TILE, w);
+    load_half_row_f32(Fg + q0, C::BQ, lim, Fs, w & 1, lane);
   };
-  issue(0);
+  const int nqb = (L + C::BQ - 1) / C::BQ;
+  issue(0, 0);
 
   // ---- prologue: this lane's key k~ and v (B operands). A negative softmax
   // scale is applied as a sign flip of k~ in S (exact); dK~ then takes the
@@ -247,8 +271,14 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkv_kernel(AttnArgs a
     }
   }
 
+  // blocks 1 .. NSTAGE-2 after the prologue's global loads (see the wait below)
+#pragma unroll
+  for (int j = 1; j < C::NSTAGE - 1; ++j)
+    if (j < nqb) issue(j, j);
+
   const float c = a.c;
   const int xq = swz<D>(prow);
+  const TrRows<D> tread(lane);  // transposed reads of the q~ and dO tiles
   f32x16 dvacc[C::ND], dkacc[C::ND];
 #pragma unroll
   for (int dt = 0; dt < C::ND; ++dt) {
@@ -256,13 +286,20 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkv_kernel(AttnArgs a
     dkacc[dt] = f32x16{};
   }
 
-  const int nqb = (L + C::BQ - 1) / C::BQ;
+  int stage = 0, next = C::NSTAGE - 1;
   for (int qb = 0; qb < nqb; ++qb) {
-    wait_vmem();
-    __syncthreads();
-    if (qb + 1 < nqb) issue(qb + 1);
-    const uint16_t* Qs = lds + (qb & 1) * C::STAGE;
+    // block qb's copies are done once at most the next block's are
+    // outstanding; the barrier publishes them and frees stage `next`
+    if (C::NSTAGE == 3 && qb + 1 < nqb)
+      wait_vmem<C::LOADS>();
+    else
+      wait_vmem<0>();
+    block_barrier();
+    if (qb + C::NSTAGE - 1 < nqb) issue(qb + C::NSTAGE - 1, next);
+    const uint16_t* Qs = lds + stage * C::STAGE;
     const uint16_t* Os = Qs + C::TILE;
+    stage = stage + 1 == C::NSTAGE ? 0 : stage + 1;
+    next = next + 1 == C::NSTAGE ? 0 : next + 1;
     const float* Fs = reinterpret_cast<const float*>(Qs + 2 * C::TILE);
     const int lim = L - qb * C::BQ;  // valid queries in this block
 
@@ -313,14 +350,13 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkv_kernel(AttnArgs a
     }
 #pragma unroll
     for (int dt = 0; dt < C::ND; ++dt) {
+      u32x4 ao[C::NU], aq[C::NU];
+      tread.template read<C::NU>(lds_addr(Os), dt, ao);
 #pragma unroll
-      for (int u = 0; u < C::NU; ++u) {
-        const int kk = 32 * (u >> 1) + 8 * (u & 1);
-        const u32x4 ao = ld_tr_tile<D, (D < 32)>(Os, kk, 32 * dt, D);
-        const u32x4 aq = ld_tr_tile<D, (D < 32)>(Qs, kk, 32 * dt, D);
-        dvacc[dt] = mfma32(ao, preg[u], dvacc[dt]);
-        dkacc[dt] = mfma32(aq, dsreg[u], dkacc[dt]);
-      }
+      for (int u = 0; u < C::NU; ++u) dvacc[dt] = mfma32(ao[u], preg[u], dvacc[dt]);
+      tread.template read<C::NU>(lds_addr(Qs), dt, aq);
+#pragma unroll
+      for (int u = 0; u < C::NU; ++u) dkacc[dt] = mfma32(aq[u], dsreg[u], dkacc[dt]);
     }
   }
   __syncthreads();  // every wave is done with the tiles

@@ -6,8 +6,8 @@
 //   global memory into the MFMA B-operand registers, kept for the whole item.
 //   For each block of 64 keys (32 at d = 128) the k~ and v rows are copied
 //   from global memory into swizzled LDS tiles by global_load_lds (no register
-//   staging, no vector instructions), double-buffered: the next block's copy
-//   is issued right after the barrier that opens the current block.
+//   staging, no vector instructions), in a ring of three LDS stages: the copy
+//   of block kb + 2 is issued right after the barrier that opens block kb.
 //   S^T = K~ Q~^T reads k~ rows; O^T += V^T P^T reads the v tile along its
 //   key (row) axis with the LDS transpose load.
 //   Lane (q, g) of a wave holds the scores of query q against 16 keys per
@@ -44,8 +44,10 @@ struct FwdCfg {
   static constexpr int NU = BN / 16;              // k-steps over keys
   static constexpr int TILE = BN * D;             // elements of one k~ or v tile
   static constexpr int STAGE = 2 * TILE;
-  static constexpr int LDS = 2 * STAGE;
+  static constexpr int NSTAGE = 3;                // LDS ring of key blocks
+  static constexpr int LDS = NSTAGE * STAGE;
   static constexpr int OCC = D == 128 ? 2 : 3;    // workgroups per CU
+  using Loader = TilePair<D, BN>;
 };
 
 constexpr float kLazyBound = 65536.0f;  // 2^16: largest block sum of P kept
@@ -58,7 +60,8 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(AttnArgs a) {
   const Item it = a.items[blockIdx.x];
   if (it.len <= 0) return;
   const int L = it.len, h = it.head, q0 = it.blk * C::BM;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 31, g = lane >> 5, prow = perm_row(r);
   const int rs = a.H * D;  // row stride; T*H*d < 2^31 is checked on the host
   const int64_t base = (int64_t)it.seq0 * rs + (int64_t)h * D;
@@ -66,13 +69,15 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(AttnArgs a) {
   const uint16_t* __restrict__ Kg = a.k + base;
   const uint16_t* __restrict__ Vg = a.v + base;
 
-  auto issue = [&](int kb) {
+  // k~ and v rows of key block kb -> LDS stage `stage`
+  const typename C::Loader loader(w, lane);
+  auto issue = [&](int kb, int stage) {
     const int k0 = kb * C::BN;
-    uint16_t* Ks = lds + (kb & 1) * C::STAGE;
-    load_tile<D, C::BN>(Kg + (int64_t)k0 * rs, rs, L - k0, Ks, w, lane);
-    load_tile<D, C::BN>(Vg + (int64_t)k0 * rs, rs, L - k0, Ks + C::TILE, w, lane);
+    uint16_t* Ks = lds + stage * C::STAGE;
+    loader.load(Kg + (int64_t)k0 * rs, Vg + (int64_t)k0 * rs, rs, L - k0, Ks, Ks + C::TILE, w);
   };
-  issue(0);
+  const int nkb = (L + C::BN - 1) / C::BN;
+  issue(0, 0);
 
   // queries: B operands (8 d values per k-step); rows past the end are zero.
   // A negative softmax scale is applied as a sign flip of q~ (exact), so that
@@ -89,40 +94,59 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(AttnArgs a) {
       for (int e = 0; e < 4; ++e) qreg[s][e] ^= qflip;
     }
   }
+  // Blocks 1 .. NSTAGE-2 are issued after the q~ loads, so that the first
+  // wait below (which lets one block's loads stay in flight) covers those.
+#pragma unroll
+  for (int j = 1; j < C::NSTAGE - 1; ++j)
+    if (j < nkb) issue(j, j);
 
   const float c = a.c;
   const int xk = swz<D>(prow);  // swizzle of the lane's k~ rows 32t + prow
+  const TrRows<D> vread(lane);  // transposed reads of the v tile
   float m = 0.f, mc = 0.f, l = 0.f;
   f32x16 oacc[C::ND];
 #pragma unroll
   for (int dt = 0; dt < C::ND; ++dt) oacc[dt] = f32x16{};
 
-  const int nkb = (L + C::BN - 1) / C::BN;
+  int stage = 0;                 // LDS stage of block kb
+  int next = C::NSTAGE - 1;      // LDS stage of block kb + NSTAGE - 1
   for (int kb = 0; kb < nkb; ++kb) {
-    wait_vmem();
-    __syncthreads();
-    if (kb + 1 < nkb) issue(kb + 1);
-    const uint16_t* Ks = lds + (kb & 1) * C::STAGE;
+    // This wave's copies of block kb are done once at most the loads of the
+    // blocks after it (NSTAGE - 2 of them, when they exist) are outstanding;
+    // the barrier then publishes every wave's copies, and also tells that
+    // stage `next` (last read for block kb - 1) is free again.
+    if (C::NSTAGE == 3 && kb + 1 < nkb)
+      wait_vmem<C::Loader::LOADS_PER_WAVE>();
+    else
+      wait_vmem<0>();
+    block_barrier();
+    if (kb + C::NSTAGE - 1 < nkb) issue(kb + C::NSTAGE - 1, next);
+    const uint16_t* Ks = lds + stage * C::STAGE;
     const uint16_t* Vs = Ks + C::TILE;
+    stage = stage + 1 == C::NSTAGE ? 0 : stage + 1;
+    next = next + 1 == C::NSTAGE ? 0 : next + 1;
 
-    // S^T tiles: lane (q = r, g) register i of tile t = key 32t + 16g + i
-    f32x16 sacc[C::NT];
-#pragma unroll
-    for (int t = 0; t < C::NT; ++t) {
-      sacc[t] = f32x16{};
-      const uint16_t* Kr = Ks + (32 * t + prow) * D;
-#pragma unroll
-      for (int s = 0; s < C::NS; ++s)
-        sacc[t] = mfma32(ld16(Kr + 8 * ((2 * s + g) ^ xk)), qreg[s], sacc[t]);
-    }
+    // S^T tiles: lane (q = r, g) register i of tile t = key 32t + 16g + i.
+    // Keys past the end of the sequence get S = -inf, so P = 0.
     const int lim = L - kb * C::BN;  // valid keys in this block
-    if (lim < C::BN) {  // keys past the end: S = -inf, so P = 0
+    f32x16 sacc[C::NT];
+    auto scores = [&]() {
 #pragma unroll
-      for (int t = 0; t < C::NT; ++t)
+      for (int t = 0; t < C::NT; ++t) {
+        sacc[t] = f32x16{};
+        const uint16_t* Kr = Ks + (32 * t + prow) * D;
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          sacc[t][i] = (32 * t + 16 * g + i < lim) ? sacc[t][i] : -INFINITY;
-    }
+        for (int s = 0; s < C::NS; ++s)
+          sacc[t] = mfma32(ld16(Kr + 8 * ((2 * s + g) ^ xk)), qreg[s], sacc[t]);
+      }
+      if (lim < C::BN) {
+#pragma unroll
+        for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            sacc[t][i] = (32 * t + 16 * g + i < lim) ? sacc[t][i] : -INFINITY;
+      }
+    };
     auto block_max = [&]() {
       float mx = sacc[0][0];
 #pragma unroll
@@ -131,22 +155,27 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(AttnArgs a) {
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[t][i]);
       return fmaxf(mx, xor32(mx));
     };
+    // P = exp2(S c - m c) in place of S; returns this lane's sum of P
+    auto exponentiate = [&]() {
+      float sum = 0.f;
+#pragma unroll
+      for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          sacc[t][i] = fast_exp2(fmaf(sacc[t][i], c, -mc));
+          sum += sacc[t][i];
+        }
+      return sum;
+    };
+    scores();
     if (kb == 0) {
       m = block_max();  // block 0 holds key 0, so m is finite
       mc = m * c;
     }
-
-    float p[C::NT][16];
-    float lb = 0.f;
-#pragma unroll
-    for (int t = 0; t < C::NT; ++t)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        p[t][i] = fast_exp2(fmaf(sacc[t][i], c, -mc));
-        lb += p[t][i];
-      }
+    float lb = exponentiate();
     if (wave_any(!(lb <= kLazyBound))) {
-      // rare: raise the reference to the new maximum and redo the block
+      // rare: recompute S, raise the reference to the new maximum, redo P
+      scores();
       const float mnew = fmaxf(m, block_max());
       const float alpha = fast_exp2((m - mnew) * c);
       m = mnew;
@@ -154,14 +183,7 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(AttnArgs a) {
       l *= alpha;
 #pragma unroll
       for (int dt = 0; dt < C::ND; ++dt) oacc[dt] *= alpha;
-      lb = 0.f;
-#pragma unroll
-      for (int t = 0; t < C::NT; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          p[t][i] = fast_exp2(fmaf(sacc[t][i], c, -mc));
-          lb += p[t][i];
-        }
+      lb = exponentiate();
     }
     l += lb;
 
@@ -172,14 +194,13 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(AttnArgs a) {
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          preg[2 * t + hh][e] = pack_bf16(p[t][8 * hh + 2 * e], p[t][8 * hh + 2 * e + 1]);
+          preg[2 * t + hh][e] = pack_bf16(sacc[t][8 * hh + 2 * e], sacc[t][8 * hh + 2 * e + 1]);
 #pragma unroll
     for (int dt = 0; dt < C::ND; ++dt) {
+      u32x4 av[C::NU];
+      vread.template read<C::NU>(lds_addr(Vs), dt, av);
 #pragma unroll
-      for (int u = 0; u < C::NU; ++u) {
-        const u32x4 av = ld_tr_tile<D, (D < 32)>(Vs, 32 * (u >> 1) + 8 * (u & 1), 32 * dt, D);
-        oacc[dt] = mfma32(av, preg[u], oacc[dt]);
-      }
+      for (int u = 0; u < C::NU; ++u) oacc[dt] = mfma32(av[u], preg[u], oacc[dt]);
     }
   }
 

@@ -36,39 +36,75 @@ __device__ __forceinline__ int tile_off(int row, int c) {
 typedef __attribute__((address_space(1))) const void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
 
-// Waits until this wave's outstanding vector-memory operations (which include
-// global_load_lds transfers into LDS) have completed.
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-// Loads rows [0, R) of a tile whose row i is global row G + min(i, lim-1)*rs
-// (rows past the valid range repeat the last valid one, lim >= 1) into the
-// swizzled LDS tile T. The tile is written in 1 KB pieces, one
-// global_load_lds_dwordx4 per wave and piece (lane l fills bytes 16l..16l+15
-// of the piece); wave w of the 4 takes pieces w, w+4, ...
-template <int D, int R>
-__device__ __forceinline__ void load_tile(const uint16_t* __restrict__ G, int rs, int lim,
-                                          uint16_t* T, int w, int lane) {
-  constexpr int NC = D / 8;
-  constexpr int PIECES = R * NC / 64;
-  static_assert(PIECES * 64 == R * NC, "tile must be a whole number of 1 KB pieces");
-#pragma unroll
-  for (int j = 0; j < (PIECES + 3) / 4; ++j) {
-    const int i = w + 4 * j;
-    if (PIECES % 4 == 0 || i < PIECES) {
-      const int p = i * 64 + lane, row = p / NC, pc = p % NC;
-      const int src_row = min(row, lim - 1);
-      const uint16_t* src = G + src_row * rs + 8 * (pc ^ swz<D>(row));
-      __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)(T + i * 512), 16, 0, 0);
-    }
-  }
+// Waits until at most N of this wave's vector-memory operations (which
+// include global_load_lds transfers into LDS) are still outstanding; they
+// complete in issue order. (s_waitcnt vmcnt(N), other counters untouched.)
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
 }
 
-// Loads n <= 64 consecutive floats src[min(i, lim-1)], i < n, into LDS F[0..n)
-// with one global_load_lds_dword by wave w_load (4 bytes per lane).
-__device__ __forceinline__ void load_row_f32(const float* __restrict__ src, int n, int lim,
-                                             float* F, int w, int w_load, int lane) {
-  if (w == w_load && lane < n)
-    __builtin_amdgcn_global_load_lds((gptr_t)(src + min(lane, lim - 1)), (lptr_t)F, 4, 0, 0);
+// Loads two tiles of R rows at once, tile t's row i being global row
+// G_t + min(i, lim-1)*rs (rows past the valid range repeat the last valid
+// one, lim >= 1), into the swizzled LDS tiles T0 and T1. The tiles are
+// written in 1 KB pieces, one global_load_lds_dwordx4 per wave and piece
+// (lane l fills bytes 16l..16l+15 of the piece); wave w takes pieces
+// w, w + 4, w + 8, ... of each tile, so every wave issues the same number of
+// loads, LOADS_PER_WAVE. Lane l of piece i covers row i*64/NC + l/NC, chunk
+// l % NC: the lane's row is rowbase + ROWSTEP * j for its j-th piece of a
+// tile, and as rowbase < ROWSTEP (a power of two) the swizzle of that row is
+// swz(rowbase) ^ swz(ROWSTEP * j). A tile of only 2 pieces (R * D = 1024) is
+// loaded by waves 0-1 (first tile) and 2-3 (second tile).
+template <int D, int R>
+struct TilePair {
+  static constexpr int NC = D / 8;                 // chunks per row
+  static constexpr int PIECES = R * NC / 64;       // per tile
+  static constexpr bool SMALL = PIECES == 2;
+  static constexpr int PER_TILE = SMALL ? 1 : PIECES / 4;  // pieces per wave and tile
+  static constexpr int LOADS_PER_WAVE = SMALL ? 1 : 2 * PER_TILE;
+  static constexpr int ROWSTEP = 4 * 64 / NC;      // rows between a wave's pieces
+  static_assert(PIECES * 64 == R * NC && (SMALL || PIECES % 4 == 0), "tile shape");
+
+  int rowbase, xbase, wp;  // per lane; wp: the wave's first piece in its tile
+  __device__ __forceinline__ TilePair(int w, int lane) {
+    wp = SMALL ? (w & 1) : w;
+    rowbase = wp * (64 / NC) + lane / NC;
+    xbase = 8 * ((lane % NC) ^ swz<D>(rowbase));
+  }
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ G0,
+                                       const uint16_t* __restrict__ G1, int rs, int lim,
+                                       uint16_t* T0, uint16_t* T1, int w) const {
+    if (SMALL) {
+      const bool second = w >= 2;
+      const uint16_t* src = (second ? G1 : G0) + min(rowbase, lim - 1) * rs + xbase;
+      uint16_t* dst = (second ? T1 : T0) + wp * 512;
+      __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)dst, 16, 0, 0);
+      return;
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int j = 0; j < PER_TILE; ++j) {
+        const int row = rowbase + ROWSTEP * j;
+        const int x = xbase ^ (8 * swz<D>(ROWSTEP * j));
+        const uint16_t* src = (t ? G1 : G0) + min(row, lim - 1) * rs + x;
+        uint16_t* dst = (t ? T1 : T0) + (wp + 4 * j) * 512;
+        __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)dst, 16, 0, 0);
+      }
+    }
+  }
+};
+
+// Loads n <= 128 consecutive floats src[min(i, lim-1)], i < n, into LDS
+// F[0..n): wave w takes the part [w_part * n/2, (w_part + 1) * n/2) with one
+// global_load_lds_dword (4 bytes per lane).
+__device__ __forceinline__ void load_half_row_f32(const float* __restrict__ src, int n, int lim,
+                                                  float* F, int w_part, int lane) {
+  const int half = n / 2, i = w_part * half + lane;
+  if (lane < half)
+    __builtin_amdgcn_global_load_lds((gptr_t)(src + min(i, lim - 1)), (lptr_t)(F + w_part * half),
+                                     4, 0, 0);
 }
 
 // MFMA operand along d from a tile: lane (r, g) gets logical chunk c of row
@@ -78,28 +114,105 @@ __device__ __forceinline__ u32x4 ld_row(const uint16_t* T, int row, int c) {
   return ld16(T + tile_off<D>(row, c));
 }
 
-// MFMA operand whose k index runs along the ROWS of the tile (the transposed
-// tile): lane (r = l % 32, g = l / 32) receives T[k0 + 16g + e][col0 +
-// perm_row(r)] for e = 0..7, through two ds_read_b64_tr_b16 (see ld_tr8 in
-// common.h for the lane mapping of that instruction). k0 is a multiple of 8.
-// ZERO_HI: lanes whose perm_row(r) >= ncols get zeros (tiles narrower than 32
-// columns); their source addresses are clamped into the tile.
-template <int D, bool ZERO_HI>
-__device__ __forceinline__ u32x4 ld_tr_tile(const uint16_t* T, int k0, int col0, int ncols) {
-  const int l = threadIdx.x & 63;
-  const int s = l & 15, G = l >> 4, g = l >> 5;
-  int col = perm_row(16 * (G & 1) + 4 * (s & 3));
-  if (ZERO_HI && col >= ncols) col = 0;
-  col += col0;
-  const int row0 = k0 + 16 * g + (s >> 2), row1 = row0 + 4;
-  const uint16_t* p0 = T + tile_off<D>(row0, col >> 3) + (col & 7);
-  const uint16_t* p1 = T + tile_off<D>(row1, col >> 3) + (col & 7);
-  const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p0);
-  const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p1);
-  const uint2 a = __builtin_bit_cast(uint2, v0), b = __builtin_bit_cast(uint2, v1);
-  u32x4 out = {a.x, a.y, b.x, b.y};
-  if (ZERO_HI && perm_row(l & 31) >= ncols) out = u32x4{0u, 0u, 0u, 0u};
-  return out;
+// Byte address in LDS of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
 }
+
+// Workgroup barrier without a memory fence: the kernels order their LDS
+// traffic themselves (wait_vmem for the global_load_lds copies; every LDS
+// read is consumed, hence complete, before the barrier that precedes its
+// stage's next copy). The empty asm statements keep the compiler from moving
+// memory accesses across it.
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// MFMA operands whose k index runs along the ROWS of a tile (the transposed
+// tile), for the row blocks k0(u) = 32 (u / 2) + 8 (u % 2), u < NU, of the
+// 32 columns [32 dt, 32 dt + 32): lane (r = l % 32, g = l / 32) receives
+// T[k0 + 16g + e][32 dt + perm_row(r)], e = 0..7, through two
+// ds_read_b64_tr_b16 (rows k0 + 16g + 0..3 and + 4..7). That instruction
+// works on groups of 16 lanes: lane 4a + b of a group receives element b of
+// the 8-byte pieces addressed by lanes a, a+4, a+8, a+12 of the group. Lane s
+// of group G addresses row 16g + s/4 (+ k0, + 4) at column
+// perm_row(16 (G % 2) + 4 (s % 4)), so lane 4a + b collects four consecutive
+// rows of column perm_row(16 (G % 2) + 4a) + b = perm_row(r).
+// Row k0 + 16g + s/4 + 4h has the disjoint bits of k0, 16g + s/4 and 4h, and
+// swz of the k0 used here is 0, so its swizzle is swz(16g + s/4) ^ swz(4h):
+// each lane needs one base address per (h, dt) and the row block is an
+// immediate offset. The reads are inline assembly because the compiler,
+// unable to tell them apart from the global_load_lds copies still in flight
+// into other stages, would otherwise wait for all those copies first; the
+// asm block waits for its own reads (lgkmcnt(0)) before it ends.
+// ZERO_HI: lanes whose perm_row(r) >= D get zeros (D = 16: tiles narrower
+// than 32 columns); their addresses are clamped into the tile.
+template <int D>
+struct TrRows {
+  static constexpr bool ZERO_HI = D < 32;
+  static constexpr int ND = D >= 32 ? D / 32 : 1;
+  static constexpr int ROWB = 2 * D;  // bytes per tile row
+  uint32_t base[2][ND];               // per lane, bytes within the tile
+  bool hi_zero;
+
+  __device__ __forceinline__ explicit TrRows(int lane) {
+    const int s = lane & 15, G = lane >> 4, g = lane >> 5;
+    int col = perm_row(16 * (G & 1) + 4 * (s & 3));
+    hi_zero = ZERO_HI && perm_row(lane & 31) >= D;
+    if (ZERO_HI && col >= D) col = 0;
+    const int rl = 16 * g + (s >> 2);
+    const int cx = (col >> 3) ^ swz<D>(rl);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt)
+        base[h][dt] = 2 * (rl * D + (col & 7) + 8 * (cx ^ (4 * dt) ^ (h ? swz<D>(4) : 0)));
+  }
+
+  // NU operands (NU = 2 or 4) of d tile dt from the tile at LDS byte address
+  // tile; one asm block, which returns with the data in registers.
+  template <int NU>
+  __device__ __forceinline__ void read(uint32_t tile, int dt, u32x4 (&out)[NU]) const {
+    const uint32_t b0 = tile + base[0][dt], b1 = tile + base[1][dt];
+    u32x2 v[8];
+    if constexpr (NU == 4) {
+      asm volatile(
+          "ds_read_b64_tr_b16 %0, %8 offset:%10\n\t"
+          "ds_read_b64_tr_b16 %1, %9 offset:%11\n\t"
+          "ds_read_b64_tr_b16 %2, %8 offset:%12\n\t"
+          "ds_read_b64_tr_b16 %3, %9 offset:%13\n\t"
+          "ds_read_b64_tr_b16 %4, %8 offset:%14\n\t"
+          "ds_read_b64_tr_b16 %5, %9 offset:%15\n\t"
+          "ds_read_b64_tr_b16 %6, %8 offset:%16\n\t"
+          "ds_read_b64_tr_b16 %7, %9 offset:%17\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
+            "=&v"(v[6]), "=&v"(v[7])
+          : "v"(b0), "v"(b1), "i"(0 * ROWB), "i"(4 * ROWB), "i"(8 * ROWB), "i"(12 * ROWB),
+            "i"(32 * ROWB), "i"(36 * ROWB), "i"(40 * ROWB), "i"(44 * ROWB)
+          : "memory");
+    } else {
+      static_assert(NU == 2, "2 or 4 operands");
+      asm volatile(
+          "ds_read_b64_tr_b16 %0, %4 offset:%6\n\t"
+          "ds_read_b64_tr_b16 %1, %5 offset:%7\n\t"
+          "ds_read_b64_tr_b16 %2, %4 offset:%8\n\t"
+          "ds_read_b64_tr_b16 %3, %5 offset:%9\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+          : "v"(b0), "v"(b1), "i"(0 * ROWB), "i"(4 * ROWB), "i"(8 * ROWB), "i"(12 * ROWB)
+          : "memory");
+    }
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      out[u] = u32x4{v[2 * u].x, v[2 * u].y, v[2 * u + 1].x, v[2 * u + 1].y};
+      if (ZERO_HI && hi_zero) out[u] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+};
 
 }  // namespace esm
