@@ -129,7 +129,10 @@ __global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(AttnArgs a) 
   for (int dt = 0; dt < C::ND; ++dt) dqacc[dt] = f32x16{};
 
   int stage = 0, next = C::NSTAGE - 1;
-  for (int kb = 0; kb < nkb; ++kb) {
+  // One key block; only the last block of a ragged sequence (FULL false)
+  // carries the masking code.
+  auto block = [&](int kb, auto full) {
+    constexpr bool FULL = decltype(full)::value;
     // block kb's copies are done once at most the next block's are
     // outstanding; the barrier publishes them and frees stage `next`
     if (C::NSTAGE == 3 && kb + 1 < nkb)
@@ -162,7 +165,7 @@ __global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(AttnArgs a) 
         const float p = fast_exp2(fmaf(sacc[i], c, -lse2));
         dsv[i] = p * pacc[i];
       }
-      if (lim < C::BN) {  // keys past the end: dS = 0
+      if (!FULL) {  // keys past the end: dS = 0
 #pragma unroll
         for (int i = 0; i < 16; ++i)
           if (32 * t + 16 * g + i >= lim) dsv[i] = 0.f;
@@ -180,7 +183,10 @@ __global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(AttnArgs a) 
 #pragma unroll
       for (int u = 0; u < C::NU; ++u) dqacc[dt] = mfma32(at[u], dsreg[u], dqacc[dt]);
     }
-  }
+  };
+  const int nfull = L / C::BN;
+  for (int kb = 0; kb < nfull; ++kb) block(kb, Full{});
+  if (nfull < nkb) block(nfull, Ragged{});
   __syncthreads();  // every wave is done with the tiles
 
   // ---- epilogue: dq~ (fp32) -> LDS -> inverse rotation -> bf16
@@ -208,13 +214,12 @@ struct DkvCfg {
   static constexpr int NS = D / 16;
   static constexpr int ND = D >= 32 ? D / 32 : 1;
   static constexpr int NT = BQ / 32;
-  static constexpr int NU = BQ / 16;
   static constexpr int TILE = BQ * D;           // q~ tile, then dO tile
   static constexpr int STAGE = 2 * TILE + 4 * BQ;  // + lse2[BQ], D[BQ] as fp32
   static constexpr int NSTAGE = 3;              // LDS ring of query blocks
   static constexpr int EPI = BK * (D + 4) * 2;
   static constexpr int LDS = NSTAGE * STAGE > EPI ? NSTAGE * STAGE : EPI;
-  static constexpr int OCC = 2;
+  static constexpr int OCC = D == 128 ? 2 : 3;
   using Loader = TilePair<D, BQ>;
   static constexpr int LOADS = Loader::LOADS_PER_WAVE + 1;  // + a half row of lse2 or D
 };
@@ -248,7 +253,7 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkv_kernel(AttnArgs a
     uint16_t* Qs = lds + stage * C::STAGE;
     float* Fs = reinterpret_cast<float*>(Qs + 2 * C::TILE) + (w < 2 ? 0 : C::BQ);
     loader.load(Qg + (int64_t)q0 * rs, dOg + (int64_t)q0 * rs, rs, lim, Qs, Qs + C::TILE, w);
-    load_half_row_f32(Fg + q0, C::BQ, lim, Fs, w & 1, lane);
+    load_half_row_f32(Fg + q0, C::BQ, lim, Fs, w & 1);
   };
   const int nqb = (L + C::BQ - 1) / C::BQ;
   issue(0, 0);
@@ -287,7 +292,10 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkv_kernel(AttnArgs a
   }
 
   int stage = 0, next = C::NSTAGE - 1;
-  for (int qb = 0; qb < nqb; ++qb) {
+  // One query block; only the last block of a ragged sequence (FULL false)
+  // carries the masking code.
+  auto block = [&](int qb, auto full) {
+    constexpr bool FULL = decltype(full)::value;
     // block qb's copies are done once at most the next block's are
     // outstanding; the barrier publishes them and frees stage `next`
     if (C::NSTAGE == 3 && qb + 1 < nqb)
@@ -303,7 +311,8 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkv_kernel(AttnArgs a
     const float* Fs = reinterpret_cast<const float*>(Qs + 2 * C::TILE);
     const int lim = L - qb * C::BQ;  // valid queries in this block
 
-    u32x4 preg[C::NU], dsreg[C::NU];
+    // One 32-query tile at a time: S and dP, then P and dS, then the tile's
+    // dV / dK products (keeps one tile's P and dS live, not the block's).
 #pragma unroll
     for (int t = 0; t < C::NT; ++t) {
       f32x16 sacc = f32x16{}, pacc = f32x16{};
@@ -314,51 +323,51 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkv_kernel(AttnArgs a
         sacc = mfma32(ld16(Qs + off), kreg[s], sacc);
         pacc = mfma32(ld16(Os + off), vreg[s], pacc);
       }
-      // queries 32t + 16g + i, i = 0..15
-      float lse2[16], dd[16];
+      // queries 32t + 16g + i, i = 0..15; P and dS overwrite S and dP
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const u32x4 x = ld16(&Fs[32 * t + 16 * g + 4 * j]);
         const u32x4 y = ld16(&Fs[C::BQ + 32 * t + 16 * g + 4 * j]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          lse2[4 * j + e] = __uint_as_float(x[e]);
-          dd[4 * j + e] = __uint_as_float(y[e]);
+          const int i = 4 * j + e;
+          sacc[i] = fast_exp2(fmaf(sacc[i], c, -__uint_as_float(x[e])));
+          pacc[i] = sacc[i] * (pacc[i] - __uint_as_float(y[e]));
         }
       }
-      float pv[16], dsv[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        pv[i] = fast_exp2(fmaf(sacc[i], c, -lse2[i]));
-        dsv[i] = pv[i] * (pacc[i] - dd[i]);
-      }
-      if (lim < C::BQ) {  // queries past the end (copies of the last row): P = dS = 0
+      if (!FULL) {  // queries past the end (copies of the last row): P = dS = 0
 #pragma unroll
         for (int i = 0; i < 16; ++i)
           if (32 * t + 16 * g + i >= lim) {
-            pv[i] = 0.f;
-            dsv[i] = 0.f;
+            sacc[i] = 0.f;
+            pacc[i] = 0.f;
           }
       }
+      u32x4 preg[2], dsreg[2];
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          preg[2 * t + hh][e] = pack_bf16(pv[8 * hh + 2 * e], pv[8 * hh + 2 * e + 1]);
-          dsreg[2 * t + hh][e] = pack_bf16(dsv[8 * hh + 2 * e], dsv[8 * hh + 2 * e + 1]);
+          preg[hh][e] = pack_bf16(sacc[8 * hh + 2 * e], sacc[8 * hh + 2 * e + 1]);
+          dsreg[hh][e] = pack_bf16(pacc[8 * hh + 2 * e], pacc[8 * hh + 2 * e + 1]);
         }
+      // rows 32t .. 32t + 31 of the dO and q~ tiles, read along the rows
+      const uint32_t orow = lds_addr(Os) + 32 * t * 2 * D, qrow = lds_addr(Qs) + 32 * t * 2 * D;
+#pragma unroll
+      for (int dt = 0; dt < C::ND; ++dt) {
+        u32x4 ao[2], aq[2];
+        tread.template read<2>(orow, dt, ao);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) dvacc[dt] = mfma32(ao[u], preg[u], dvacc[dt]);
+        tread.template read<2>(qrow, dt, aq);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) dkacc[dt] = mfma32(aq[u], dsreg[u], dkacc[dt]);
+      }
     }
-#pragma unroll
-    for (int dt = 0; dt < C::ND; ++dt) {
-      u32x4 ao[C::NU], aq[C::NU];
-      tread.template read<C::NU>(lds_addr(Os), dt, ao);
-#pragma unroll
-      for (int u = 0; u < C::NU; ++u) dvacc[dt] = mfma32(ao[u], preg[u], dvacc[dt]);
-      tread.template read<C::NU>(lds_addr(Qs), dt, aq);
-#pragma unroll
-      for (int u = 0; u < C::NU; ++u) dkacc[dt] = mfma32(aq[u], dsreg[u], dkacc[dt]);
-    }
-  }
+  };
+  const int nfull = L / C::BQ;
+  for (int qb = 0; qb < nfull; ++qb) block(qb, Full{});
+  if (nfull < nqb) block(nfull, Ragged{});
   __syncthreads();  // every wave is done with the tiles
 
   // ---- epilogue: dk = R(-p) scale dK~, dv

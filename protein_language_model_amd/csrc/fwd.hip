@@ -110,7 +110,10 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(AttnArgs a) {
 
   int stage = 0;                 // LDS stage of block kb
   int next = C::NSTAGE - 1;      // LDS stage of block kb + NSTAGE - 1
-  for (int kb = 0; kb < nkb; ++kb) {
+  // One key block; FULL blocks have no key past the end of the sequence, so
+  // only the last block of a ragged sequence carries the masking code.
+  auto block = [&](int kb, auto full) {
+    constexpr bool FULL = decltype(full)::value;
     // This wave's copies of block kb are done once at most the loads of the
     // blocks after it (NSTAGE - 2 of them, when they exist) are outstanding;
     // the barrier then publishes every wave's copies, and also tells that
@@ -139,7 +142,7 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(AttnArgs a) {
         for (int s = 0; s < C::NS; ++s)
           sacc[t] = mfma32(ld16(Kr + 8 * ((2 * s + g) ^ xk)), qreg[s], sacc[t]);
       }
-      if (lim < C::BN) {
+      if (!FULL) {
 #pragma unroll
         for (int t = 0; t < C::NT; ++t)
 #pragma unroll
@@ -202,7 +205,10 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(AttnArgs a) {
 #pragma unroll
       for (int u = 0; u < C::NU; ++u) oacc[dt] = mfma32(av[u], preg[u], oacc[dt]);
     }
-  }
+  };
+  const int nfull = L / C::BN;
+  for (int kb = 0; kb < nfull; ++kb) block(kb, Full{});
+  if (nfull < nkb) block(nfull, Ragged{});
 
   // ---- epilogue
   l += xor32(l);

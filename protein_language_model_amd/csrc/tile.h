@@ -33,6 +33,15 @@ __device__ __forceinline__ int tile_off(int row, int c) {
   return row * D + 8 * (c ^ swz<D>(row));
 }
 
+// Lane index computed where it is used: the asm keeps the compiler from
+// hoisting it (and values derived from it) out of a loop, where they would
+// stay live, or be spilled, across the whole loop.
+__device__ __forceinline__ int lane_id_here() {
+  int v;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(v));
+  return v;
+}
+
 typedef __attribute__((address_space(1))) const void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
 
@@ -66,18 +75,21 @@ struct TilePair {
   static constexpr int ROWSTEP = 4 * 64 / NC;      // rows between a wave's pieces
   static_assert(PIECES * 64 == R * NC && (SMALL || PIECES % 4 == 0), "tile shape");
 
-  int rowbase, xbase, wp;  // per lane; wp: the wave's first piece in its tile
-  __device__ __forceinline__ TilePair(int w, int lane) {
-    wp = SMALL ? (w & 1) : w;
-    rowbase = wp * (64 / NC) + lane / NC;
-    xbase = 8 * ((lane % NC) ^ swz<D>(rowbase));
-  }
+  // Per-lane values are recomputed at each call (a few instructions) rather
+  // than kept live across the kernels' main loops.
+  __device__ __forceinline__ TilePair(int, int) {}
   __device__ __forceinline__ void load(const uint16_t* __restrict__ G0,
                                        const uint16_t* __restrict__ G1, int rs, int lim,
                                        uint16_t* T0, uint16_t* T1, int w) const {
+    const int wp = SMALL ? (w & 1) : w;
+    const int lane = lane_id_here();
+    const int rowbase = wp * (64 / NC) + lane / NC;
+    const int xbase = 8 * ((lane % NC) ^ swz<D>(rowbase));
+    // uniform 64-bit base + 32-bit per-lane byte offset (the saddr form)
     if (SMALL) {
       const bool second = w >= 2;
-      const uint16_t* src = (second ? G1 : G0) + min(rowbase, lim - 1) * rs + xbase;
+      const uint32_t off = 2u * (uint32_t)(min(rowbase, lim - 1) * rs + xbase);
+      const char* src = reinterpret_cast<const char*>(second ? G1 : G0) + off;
       uint16_t* dst = (second ? T1 : T0) + wp * 512;
       __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)dst, 16, 0, 0);
       return;
@@ -88,7 +100,8 @@ struct TilePair {
       for (int j = 0; j < PER_TILE; ++j) {
         const int row = rowbase + ROWSTEP * j;
         const int x = xbase ^ (8 * swz<D>(ROWSTEP * j));
-        const uint16_t* src = (t ? G1 : G0) + min(row, lim - 1) * rs + x;
+        const uint32_t off = 2u * (uint32_t)(min(row, lim - 1) * rs + x);
+        const char* src = reinterpret_cast<const char*>(t ? G1 : G0) + off;
         uint16_t* dst = (t ? T1 : T0) + (wp + 4 * j) * 512;
         __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)dst, 16, 0, 0);
       }
@@ -100,11 +113,13 @@ struct TilePair {
 // F[0..n): wave w takes the part [w_part * n/2, (w_part + 1) * n/2) with one
 // global_load_lds_dword (4 bytes per lane).
 __device__ __forceinline__ void load_half_row_f32(const float* __restrict__ src, int n, int lim,
-                                                  float* F, int w_part, int lane) {
+                                                  float* F, int w_part) {
+  const int lane = lane_id_here();
   const int half = n / 2, i = w_part * half + lane;
-  if (lane < half)
-    __builtin_amdgcn_global_load_lds((gptr_t)(src + min(i, lim - 1)), (lptr_t)(F + w_part * half),
-                                     4, 0, 0);
+  if (lane < half) {
+    const char* p = reinterpret_cast<const char*>(src) + 4u * (uint32_t)min(i, lim - 1);
+    __builtin_amdgcn_global_load_lds((gptr_t)p, (lptr_t)(F + w_part * half), 4, 0, 0);
+  }
 }
 
 // MFMA operand along d from a tile: lane (r, g) gets logical chunk c of row
