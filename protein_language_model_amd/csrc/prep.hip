@@ -6,24 +6,62 @@
 
 namespace esm {
 
+// Inclusive prefix sum over the 1024 threads of the workgroup: in-register
+// within each wave, then over the 16 wave totals. wsum: 16 ints of LDS.
+// Every thread must call it; it ends with a barrier.
+__device__ __forceinline__ int32_t block_inclusive_scan(int32_t v, int32_t* wsum) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t t = __shfl_up(v, off);
+    if (lane >= off) v += t;
+  }
+  if (lane == 63) wsum[wid] = v;
+  __syncthreads();
+  if (wid == 0) {
+    int32_t x = lane < 16 ? wsum[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      const int32_t t = __shfl_up(x, off);
+      if (lane >= off) x += t;
+    }
+    if (lane < 16) wsum[lane] = x;
+  }
+  __syncthreads();
+  if (wid > 0) v += wsum[wid - 1];
+  __syncthreads();  // wsum may be reused by the next call
+  return v;
+}
+
+constexpr int kPlanCache = 4096;  // batches up to this size keep cu and the order in LDS
+
 // One workgroup of 1024 threads. Sorts sequences by item count, longest first
 // (counting sort over item counts; order inside a count is arbitrary and
-// irrelevant to the results), then writes the chunk bases.
+// irrelevant to the results), then writes the chunk bases. For batches of up
+// to kPlanCache sequences cu_seqlens and the sorted order live in LDS, so the
+// only global-memory round trips are the first read and the final writes.
 __global__ __launch_bounds__(1024) void schedule_plan_kernel(
     const int32_t* __restrict__ cu, int32_t B, int32_t T, int32_t H, int32_t max_seqlen,
     int32_t block, int32_t n_buckets, int32_t* __restrict__ sorted,
     int32_t* __restrict__ chunk_base, int32_t n_chunks) {
   __shared__ int32_t hist[kMaxBuckets];
   __shared__ int32_t start[kMaxBuckets];
-  __shared__ int32_t scan[1024];
+  __shared__ int32_t cu_s[kPlanCache + 1];
+  __shared__ int32_t sorted_s[kPlanCache];
+  __shared__ int32_t wsum[16];
   __shared__ int32_t carry;
   const int tid = threadIdx.x;
+  const bool cached = B <= kPlanCache;
+  if (cached)
+    for (int i = tid; i <= B; i += 1024) cu_s[i] = cu[i];
+  const int32_t* cuv = cached ? cu_s : cu;
+  int32_t* srt = cached ? sorted_s : sorted;
 
   for (int i = tid; i < n_buckets; i += 1024) hist[i] = 0;
   __syncthreads();
   for (int b = tid; b < B; b += 1024) {
     int32_t s, L;
-    seq_bounds(cu, b, T, max_seqlen, &s, &L);
+    seq_bounds(cuv, b, T, max_seqlen, &s, &L);
     atomicAdd(&hist[(L + block - 1) / block], 1);
   }
   __syncthreads();
@@ -37,15 +75,7 @@ __global__ __launch_bounds__(1024) void schedule_plan_kernel(
       const int k = n_buckets - 1 - (4 * tid + j);
       if (k >= 0) own += hist[k];
     }
-    scan[tid] = own;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-      const int32_t v = tid >= off ? scan[tid - off] : 0;
-      __syncthreads();
-      scan[tid] += v;
-      __syncthreads();
-    }
-    int32_t run = scan[tid] - own;
+    int32_t run = block_inclusive_scan(own, wsum) - own;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int k = n_buckets - 1 - (4 * tid + j);
@@ -60,12 +90,14 @@ __global__ __launch_bounds__(1024) void schedule_plan_kernel(
   __syncthreads();
   for (int b = tid; b < B; b += 1024) {
     int32_t s, L;
-    seq_bounds(cu, b, T, max_seqlen, &s, &L);
+    seq_bounds(cuv, b, T, max_seqlen, &s, &L);
     const int k = (L + block - 1) / block;
-    sorted[start[k] + atomicAdd(&hist[k], 1)] = b;
+    srt[start[k] + atomicAdd(&hist[k], 1)] = b;
   }
-  __threadfence();
+  if (!cached) __threadfence();
   __syncthreads();
+  if (cached)
+    for (int i = tid; i < B; i += 1024) sorted[i] = sorted_s[i];
 
   // chunk heights -> exclusive prefix (chunk_base), 1024 chunks per round
   if (tid == 0) carry = 0;
@@ -79,22 +111,16 @@ __global__ __launch_bounds__(1024) void schedule_plan_kernel(
       const int64_t g1 = (g0 + 8 < groups ? g0 + 8 : groups) - 1;
       for (int64_t s = g0 / H; s <= g1 / H; ++s) {
         int32_t st, L;
-        seq_bounds(cu, sorted[s], T, max_seqlen, &st, &L);
+        seq_bounds(cuv, srt[s], T, max_seqlen, &st, &L);
         const int32_t n = (L + block - 1) / block;
         height = n > height ? n : height;
       }
     }
-    scan[tid] = 8 * height;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-      const int32_t v = tid >= off ? scan[tid - off] : 0;
-      __syncthreads();
-      scan[tid] += v;
-      __syncthreads();
-    }
-    if (c < n_chunks) chunk_base[c] = carry + scan[tid] - 8 * height;
-    __syncthreads();
-    if (tid == 1023) carry += scan[1023];
+    const int32_t incl = block_inclusive_scan(8 * height, wsum);
+    const int32_t cbase = carry;
+    if (c < n_chunks) chunk_base[c] = cbase + incl - 8 * height;
+    __syncthreads();  // every thread has read carry
+    if (tid == 1023) carry = cbase + incl;
     __syncthreads();
   }
   if (tid == 0) chunk_base[n_chunks] = carry;

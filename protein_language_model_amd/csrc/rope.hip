@@ -13,50 +13,76 @@
 
 namespace esm {
 
-// One workgroup per schedule slot: rows [blk * 128, blk * 128 + 128) of one
-// (sequence, head), both tensors.
+constexpr int kRotSplit = 2;  // workgroups per 128-row item
+
+// Workgroup (x, y) rotates rows [blk * 128 + y * RR, blk * 128 + (y + 1) * RR)
+// (RR = 128 / kRotSplit) of the (sequence, head) of schedule slot x, q and k:
+// one 8-pair chunk (16 bytes of the low half, 16 of the high half) per
+// thread and tensor, all loads issued before any arithmetic. Many small
+// workgroups keep enough loads in flight to stream at close to copy speed
+// (grouping several heads per workgroup to share the cos/sin loads measured
+// slower: fewer loads in flight).
 template <int D, bool ROPE>
 __global__ __launch_bounds__(256) void rotate_kernel(RotArgs a) {
   const Item it = a.items[blockIdx.x];
   if (it.len <= 0) return;
+  constexpr int UPR = D / 16;                        // 8-pair chunks per row
+  constexpr int RR = kItemRows / kRotSplit;          // rows per workgroup
+  constexpr int NU = (RR * UPR + 255) / 256;         // units per thread
   const int rs = a.H * D;
+  const int r0 = it.blk * kItemRows + blockIdx.y * RR;
+  const int n = min(RR, it.len - r0) * UPR;          // may be <= 0
   const int64_t base = (int64_t)it.seq0 * rs + (int64_t)it.head * D;
-  const int r0 = it.blk * kItemRows;
-  const int rows = min(kItemRows, it.len - r0);
-  for (int u = threadIdx.x; u < rows * (D / 16); u += 256) {
-    const int row = u / (D / 16), j0 = (u % (D / 16)) * 8, pos = r0 + row;
-    const int64_t off = base + (int64_t)pos * rs + j0;
-    const u32x4 ql = ld16(a.q + off), qh = ld16(a.q + off + D / 2);
-    const u32x4 kl = ld16(a.k + off), kh = ld16(a.k + off + D / 2);
-    if (ROPE) {
-      float2 cs[8];
-      load_cs8(a.rope, pos * (D / 2) + j0, cs);
-      float lo[8], hi[8];
-      unpack8(ql, lo);
-      unpack8(qh, hi);
-      rotate8<false, false>(lo, hi, cs);
-      st16(a.q_rot + off, pack8(lo));
-      st16(a.q_rot + off + D / 2, pack8(hi));
-      unpack8(kl, lo);
-      unpack8(kh, hi);
-      rotate8<false, false>(lo, hi, cs);
-      st16(a.k_rot + off, pack8(lo));
-      st16(a.k_rot + off + D / 2, pack8(hi));
-    } else {
-      st16(a.q_rot + off, ql);
-      st16(a.q_rot + off + D / 2, qh);
-      st16(a.k_rot + off, kl);
-      st16(a.k_rot + off + D / 2, kh);
+  u32x4 ql[NU], qh[NU], kl[NU], kh[NU];
+  float2 cs[NU][8];
+#pragma unroll
+  for (int x = 0; x < NU; ++x) {
+    const int u = threadIdx.x + 256 * x;
+    if (u < n) {
+      const int row = u / UPR, j0 = (u % UPR) * 8, pos = r0 + row;
+      const int64_t off = base + (int64_t)pos * rs + j0;
+      ql[x] = ld16(a.q + off);
+      qh[x] = ld16(a.q + off + D / 2);
+      kl[x] = ld16(a.k + off);
+      kh[x] = ld16(a.k + off + D / 2);
+      if (ROPE) load_cs8(a.rope, pos * (D / 2) + j0, cs[x]);
+    }
+  }
+#pragma unroll
+  for (int x = 0; x < NU; ++x) {
+    const int u = threadIdx.x + 256 * x;
+    if (u < n) {
+      const int row = u / UPR, j0 = (u % UPR) * 8, pos = r0 + row;
+      const int64_t off = base + (int64_t)pos * rs + j0;
+      u32x4 q0 = ql[x], q1 = qh[x], k0 = kl[x], k1 = kh[x];
+      if (ROPE) {
+        float lo[8], hi[8];
+        unpack8(q0, lo);
+        unpack8(q1, hi);
+        rotate8<false, false>(lo, hi, cs[x]);
+        q0 = pack8(lo);
+        q1 = pack8(hi);
+        unpack8(k0, lo);
+        unpack8(k1, hi);
+        rotate8<false, false>(lo, hi, cs[x]);
+        k0 = pack8(lo);
+        k1 = pack8(hi);
+      }
+      st16(a.q_rot + off, q0);
+      st16(a.q_rot + off + D / 2, q1);
+      st16(a.k_rot + off, k0);
+      st16(a.k_rot + off + D / 2, k1);
     }
   }
 }
 
 template <int D>
 static hipError_t launch_rotate_d(bool rope, const RotArgs& a, int64_t n_slots, hipStream_t st) {
+  const dim3 grid((unsigned)n_slots, kRotSplit);
   if (rope)
-    rotate_kernel<D, true><<<(unsigned)n_slots, 256, 0, st>>>(a);
+    rotate_kernel<D, true><<<grid, 256, 0, st>>>(a);
   else
-    rotate_kernel<D, false><<<(unsigned)n_slots, 256, 0, st>>>(a);
+    rotate_kernel<D, false><<<grid, 256, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -161,6 +161,42 @@ def test_non_default_stream(device):
     np.testing.assert_array_equal(bf16_f64(o), ref["o"])
 
 
+def test_planned_path_matches_one_shot(device):
+    """The split path the benchmark times (plan, rotation, forward, dq pass,
+    dk/dv pass) gives bitwise the outputs of the one-shot calls."""
+    inp = _case("esm2_650m", lengths=[300, 1, 129, 64], H=3)
+    T, H, d, B = inp["T"], inp["H"], inp["d"], len(inp["lengths"])
+    maxL = max(inp["lengths"])
+    q, k, v, do = (to_dev(inp[x], device) for x in ("q", "k", "v", "do"))
+    cu = torch.from_numpy(inp["cu_seqlens"]).to(device)
+    ref = run_gpu(inp, device)
+    plan = E.esm_attn_plan(cu, T, maxL, H, d, inp["rope_base"])
+    qr, kr = E.esm_attn_rotate_planned(q, k, B, maxL, plan, inp["rope_base"])
+    o, lse = E.esm_attn_fwd_planned(qr, kr, v, B, maxL, plan, inp["scale"])
+    drow = torch.empty((2, H, T), dtype=torch.float32, device=device)
+    dq, _, _, _ = E.esm_attn_bwd_planned(qr, kr, v, o, do, lse, B, maxL, plan, inp["scale"],
+                                         inp["rope_base"], drow=drow, passes=E.PASS_DQ)
+    _, dk, dv, _ = E.esm_attn_bwd_planned(qr, kr, v, o, do, lse, B, maxL, plan, inp["scale"],
+                                          inp["rope_base"], drow=drow, passes=E.PASS_DKV)
+    torch.cuda.synchronize()
+    for name, t in (("o", o), ("dq", dq), ("dk", dk), ("dv", dv)):
+        np.testing.assert_array_equal(bf16_f64(t), ref[name], err_msg=name)
+    np.testing.assert_array_equal(lse.cpu().numpy().astype(np.float64), ref["lse"])
+
+
+def test_many_short_sequences(device):
+    """More sequences than the planning kernel keeps in LDS (4096): the
+    schedule then works from global memory."""
+    rng = np.random.default_rng(11)
+    lengths = [int(x) for x in rng.integers(0, 6, size=5000)]
+    inp = _case("esm2_8m", lengths=lengths, H=1)
+    say("case many short", len(lengths), inp["T"])
+    gpu = run_gpu(inp, device)
+    for key in ("o", "lse", "dq", "dk", "dv"):
+        assert np.isfinite(gpu[key]).all(), key
+    compare(gpu, inp, seqs=list(range(0, 5000, 97)) + [4999], label="many short")
+
+
 # ---------------------------------------------------------------- full sizes
 
 FULL = [
