@@ -9,11 +9,10 @@ The default workload is the ESM-2-650M-shaped dense batch: 16 sequences of
 
 Prints ONE JSON line. `value` is counted TFLOP/s of forward + backward
 (forward 4*sum(L^2)*H*d, backward 2.5x that) over the wall clock of the
-timed steps; `kernels_us` are per-call event times inside the steps;
-`roofline` describes the dominant kernel, its launch duration timed with
-events on the stream it is launched on over back-to-back launches of that
-call alone; `cpu_baseline` times the float64 oracle on a bounded sample on
-the host.
+timed steps; `kernels_us` are per-call times from events recorded around
+each call inside the timed steps, on the stream the kernels are launched on;
+`roofline` describes the dominant kernel with that average launch time;
+`cpu_baseline` times the float64 oracle on a bounded sample on the host.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload esm2_650m]
                     [--no-cpu-baseline] [--cpu-seconds 15]
@@ -203,30 +202,6 @@ def main():
     avg = {n: float(np.mean(x)) for n, x in per.items()}
     step_ms = wall / args.steps * 1e3
 
-    # Launch duration of each kernel for the roofline: N back-to-back launches
-    # of that call alone between two events on the launch stream (per-launch
-    # gaps amortised, as in a kernel trace); inputs are the last step's.
-    single = {
-        "rotate": lambda: E.esm_attn_rotate_planned(q, k, B, maxL, plan, base, q_rot=qr, k_rot=kr),
-        "fwd": lambda: E.esm_attn_fwd_planned(qr, kr, v, B, maxL, plan, scale, out=o, lse=lse),
-        "bwd_dq": lambda: E.esm_attn_bwd_planned(qr, kr, v, o, do, lse, B, maxL, plan, scale, base,
-                                                 dq=dq, drow=drow, passes=E.PASS_DQ),
-        "bwd_dkv": lambda: E.esm_attn_bwd_planned(qr, kr, v, o, do, lse, B, maxL, plan, scale,
-                                                  base, dk=dk, dv=dv, drow=drow,
-                                                  passes=E.PASS_DKV),
-    }
-    launch_us = {}
-    for n, fn in single.items():
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps = max(args.steps, 5)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(reps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        launch_us[n] = e0.elapsed_time(e1) * 1e3 / reps
-
     fwd_f, bwd_f = W.counted_flops(inp["lengths"], H, d)
     total_f = fwd_f + bwd_f
     tflops = total_f / (step_ms * 1e-3) / 1e12
@@ -235,8 +210,8 @@ def main():
     kernel_flops = {"fwd": 4 * s2 * H * d,            # S = QK^T, O = PV
                     "bwd_dq": 6 * s2 * H * d,         # S, dP = dO V^T, dQ = dS K
                     "bwd_dkv": 8 * s2 * H * d}        # S, dP, dV = P^T dO, dK = dS^T Q
-    dom = max(kernel_flops, key=lambda n: launch_us[n])
-    achieved = kernel_flops[dom] / (launch_us[dom] * 1e-6) / 1e12
+    dom = max(kernel_flops, key=lambda n: avg[n])
+    achieved = kernel_flops[dom] / (avg[dom] * 1e-6) / 1e12
     kernel_symbol = {"fwd": "fwd_kernel<%d" % d, "bwd_dq": "bwd_dq_kernel<%d" % d,
                      "bwd_dkv": "bwd_dkv_kernel<%d" % d}[dom]
     traffic = measured_traffic(args.workload, kernel_symbol)
@@ -261,14 +236,13 @@ def main():
         "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
         "tokens_per_s": round(T / (step_ms * 1e-3), 1),
         "kernels_us": {n: round(x, 2) for n, x in avg.items()},
-        "kernel_launch_us": {n: round(x, 2) for n, x in launch_us.items()},
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": None if traffic is None else round(traffic["bytes"]),
                      "traffic_detail": traffic,
                      "algorithmic_flops": kernel_flops[dom],
-                     "avg_launch_us": round(launch_us[dom], 2)},
+                     "avg_launch_us": round(avg[dom], 2)},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
