@@ -220,6 +220,7 @@ struct DkvCfg {
   static constexpr int EPI = BK * (D + 4) * 2;
   static constexpr int LDS = NSTAGE * STAGE > EPI ? NSTAGE * STAGE : EPI;
   static constexpr int OCC = D == 128 ? 2 : 3;
+  static constexpr bool FOLD_D = D <= 64;          // dP - D folded into an MFMA
   using Loader = TilePair<D, BQ>;
   static constexpr int LOADS = Loader::LOADS_PER_WAVE + 1;  // + a half row of lse2 or D
 };
@@ -323,16 +324,26 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkv_kernel(AttnArgs a
         sacc = mfma32(ld16(Qs + off), kreg[s], sacc);
         pacc = mfma32(ld16(Os + off), vreg[s], pacc);
       }
+      // dP - D on the matrix core (d <= 64; at d = 128 the extra operands
+      // would spill): one more k-step whose A column pair holds -D of the
+      // query row as a bf16 hi + lo split and whose B pair is (1, 1), so
+      // every key column gets -D added in fp32
+      if (C::FOLD_D) {
+        const u32x4 a_negd = {g == 0 ? neg_bf16_pair(Fs[C::BQ + 32 * t + prow]) : 0u, 0u, 0u, 0u};
+        const u32x4 b_one = {g == 0 ? kBf16OnePair : 0u, 0u, 0u, 0u};
+        pacc = mfma32(a_negd, b_one, pacc);
+      }
       // queries 32t + 16g + i, i = 0..15; P and dS overwrite S and dP
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const u32x4 x = ld16(&Fs[32 * t + 16 * g + 4 * j]);
-        const u32x4 y = ld16(&Fs[C::BQ + 32 * t + 16 * g + 4 * j]);
+        u32x4 y = zero4();
+        if (!C::FOLD_D) y = ld16(&Fs[C::BQ + 32 * t + 16 * g + 4 * j]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * j + e;
           sacc[i] = fast_exp2(fmaf(sacc[i], c, -__uint_as_float(x[e])));
-          pacc[i] = sacc[i] * (pacc[i] - __uint_as_float(y[e]));
+          pacc[i] = sacc[i] * (C::FOLD_D ? pacc[i] : pacc[i] - __uint_as_float(y[e]));
         }
       }
       if (!FULL) {  // queries past the end (copies of the last row): P = dS = 0
