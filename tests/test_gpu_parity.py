@@ -184,6 +184,36 @@ def test_planned_path_matches_one_shot(device):
     np.testing.assert_array_equal(lse.cpu().numpy().astype(np.float64), ref["lse"])
 
 
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+def test_repeated_calls_on_one_plan(device, d):
+    """Calls repeated on one plan give bitwise the same outputs, equal to the
+    one-shot calls and, on sampled slices, to the oracle."""
+    name = {16: "esm2_8m", 32: "esm2_150m", 64: "esm2_650m", 128: "esm2_15b"}[d]
+    lengths = [300, 256, 40, 200, 1100, 64, 1] * 3
+    inp = _case(name, lengths=lengths, H=24)
+    T, H, B = inp["T"], inp["H"], len(inp["lengths"])
+    maxL = max(inp["lengths"])
+    say("case repeated", d, "T", T, "H", H)
+    gpu = run_gpu(inp, device)
+    compare(gpu, inp, seqs=[0, 4, 6, 20], heads=[0, 23], label="repeated d%d" % d)
+    q, k, v, do = (to_dev(inp[x], device) for x in ("q", "k", "v", "do"))
+    cu = torch.from_numpy(inp["cu_seqlens"]).to(device)
+    plan = E.esm_attn_plan(cu, T, maxL, H, d, inp["rope_base"])
+    qr, kr = E.esm_attn_rotate_planned(q, k, B, maxL, plan, inp["rope_base"])
+    outs = []
+    for _ in range(3):
+        o, lse = E.esm_attn_fwd_planned(qr, kr, v, B, maxL, plan, inp["scale"])
+        dq, dk, dv, _ = E.esm_attn_bwd_planned(qr, kr, v, o, do, lse, B, maxL, plan,
+                                               inp["scale"], inp["rope_base"])
+        outs.append([bf16_f64(t) for t in (o, dq, dk, dv)] + [lse.cpu().numpy()])
+    torch.cuda.synchronize()
+    for rep in outs[1:]:
+        for a, b in zip(outs[0], rep):
+            np.testing.assert_array_equal(a, b)
+    for n, a in zip(("o", "dq", "dk", "dv"), outs[0]):
+        np.testing.assert_array_equal(a, gpu[n], err_msg=n)
+
+
 def test_many_short_sequences(device):
     """More sequences than the planning kernel keeps in LDS (4096): the
     schedule then works from global memory."""
