@@ -68,12 +68,18 @@ __global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(AttnArgs a) 
   const uint16_t* __restrict__ Og = a.o + base;
   const uint16_t* __restrict__ dOg = a.dout + base;
 
-  // k~ and v rows of key block kb -> LDS stage `stage`
+  // k~ and v rows of key block kb -> LDS stage `stage` (offsets kept in
+  // registers for blocks with every key present)
   const typename C::Loader loader(w, lane);
+  const typename C::Loader::Offsets koff = loader.offsets(rs, w);
   auto issue = [&](int kb, int stage) {
     const int k0 = kb * C::BN;
     uint16_t* Ks = lds + stage * C::STAGE;
-    loader.load(Kg + (int64_t)k0 * rs, Vg + (int64_t)k0 * rs, rs, L - k0, Ks, Ks + C::TILE, w);
+    if (k0 + C::BN <= L)
+      loader.load_full(Kg + (int64_t)k0 * rs, Vg + (int64_t)k0 * rs, koff, Ks, Ks + C::TILE, w);
+    else
+      loader.template load<1>(Kg + (int64_t)k0 * rs, Vg + (int64_t)k0 * rs, rs, L - k0, Ks,
+                              Ks + C::TILE, w);
   };
   const int nkb = (L + C::BN - 1) / C::BN;
   issue(0, 0);

@@ -22,8 +22,10 @@
 // block. So every P ever used is at most 2^16, l and O stay far from fp32
 // overflow, and the common block costs one fma, one exp2, one add per score
 // and one conversion per two scores. P is rounded once to bf16 for the MFMA;
-// l sums the fp32 values. Keys past the end of the sequence get S = -inf,
-// so P = 0. Epilogue: O = acc / l -> bf16; LSE = (m c + log2 l) ln 2.
+// l sums the fp32 values (summing the bf16 values instead, with dot2, would
+// carry their rounding, up to 2^-8 relative, into the LSE). Keys past the end
+// of the sequence get S = -inf, so P = 0. Epilogue: O = acc / l -> bf16;
+// LSE = (m c + log2 l) ln 2.
 //
 // Tiled attention keeps the L x L matrices on chip (BioNeMo blog, section 2.3
 // describes the idea for another GPU); this kernel is laid out for the 64-wide
@@ -69,12 +71,18 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(AttnArgs a) {
   const uint16_t* __restrict__ Kg = a.k + base;
   const uint16_t* __restrict__ Vg = a.v + base;
 
-  // k~ and v rows of key block kb -> LDS stage `stage`
+  // k~ and v rows of key block kb -> LDS stage `stage` (offsets kept in
+  // registers for blocks with every key present)
   const typename C::Loader loader(w, lane);
+  const typename C::Loader::Offsets koff = loader.offsets(rs, w);
   auto issue = [&](int kb, int stage) {
     const int k0 = kb * C::BN;
     uint16_t* Ks = lds + stage * C::STAGE;
-    loader.load(Kg + (int64_t)k0 * rs, Vg + (int64_t)k0 * rs, rs, L - k0, Ks, Ks + C::TILE, w);
+    if (k0 + C::BN <= L)
+      loader.load_full(Kg + (int64_t)k0 * rs, Vg + (int64_t)k0 * rs, koff, Ks, Ks + C::TILE, w);
+    else
+      loader.template load<1>(Kg + (int64_t)k0 * rs, Vg + (int64_t)k0 * rs, rs, L - k0, Ks,
+                              Ks + C::TILE, w);
   };
   const int nkb = (L + C::BN - 1) / C::BN;
   issue(0, 0);

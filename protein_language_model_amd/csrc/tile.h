@@ -75,9 +75,60 @@ struct TilePair {
   static constexpr int ROWSTEP = 4 * 64 / NC;      // rows between a wave's pieces
   static_assert(PIECES * 64 == R * NC && (SMALL || PIECES % 4 == 0), "tile shape");
 
-  // Per-lane values are recomputed at each call (a few instructions) rather
-  // than kept live across the kernels' main loops.
+  // Per-lane byte offsets of the copies of a block whose rows all exist (no
+  // clamp): computed once per item, so that copies of such blocks take no
+  // vector instructions. Row rowbase + ROWSTEP j, chunk xbase ^ swz(ROWSTEP j).
+  struct Offsets {
+    uint32_t v[PER_TILE];
+  };
+  __device__ __forceinline__ Offsets offsets(int rs, int w) const {
+    const int wp = SMALL ? (w & 1) : w;
+    const int lane = __lane_id();
+    const int rowbase = wp * (64 / NC) + lane / NC;
+    const int xbase = 8 * ((lane % NC) ^ swz<D>(rowbase));
+    Offsets o;
+#pragma unroll
+    for (int j = 0; j < PER_TILE; ++j)
+      o.v[j] = 2u * (uint32_t)((rowbase + ROWSTEP * j) * rs + (xbase ^ (8 * swz<D>(ROWSTEP * j))));
+    return o;
+  }
+  // The copies of a block with every row present, from offsets().
+  __device__ __forceinline__ void load_full(const uint16_t* __restrict__ G0,
+                                            const uint16_t* __restrict__ G1, const Offsets& o,
+                                            uint16_t* T0, uint16_t* T1, int w) const {
+    const int wp = SMALL ? (w & 1) : w;
+    // (the empty asm hands each offset over as a fresh 32-bit value, so that
+    // the copy takes the saddr form: uniform base + 32-bit lane offset)
+    uint32_t v[PER_TILE];
+#pragma unroll
+    for (int j = 0; j < PER_TILE; ++j) {
+      v[j] = o.v[j];
+      asm volatile("" : "+v"(v[j]));
+    }
+    if (SMALL) {
+      const bool second = w >= 2;
+      const char* src = reinterpret_cast<const char*>(second ? G1 : G0) + v[0];
+      __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)((second ? T1 : T0) + wp * 512), 16,
+                                       0, 0);
+      return;
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int j = 0; j < PER_TILE; ++j) {
+        const char* src = reinterpret_cast<const char*>(t ? G1 : G0) + v[j];
+        __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)((t ? T1 : T0) + (wp + 4 * j) * 512),
+                                         16, 0, 0);
+      }
+  }
+
+  // Per-lane values of load() are recomputed at each call (a few
+  // instructions) rather than kept live across the kernels' main loops.
   __device__ __forceinline__ TilePair(int, int) {}
+  // AUX: cache-policy bits of the copies (1 = sc0). A kernel that also
+  // copies with load_full passes 1 here: the two call sites then cannot be
+  // merged into one copy from a selected 64-bit address.
+  template <int AUX = 0>
   __device__ __forceinline__ void load(const uint16_t* __restrict__ G0,
                                        const uint16_t* __restrict__ G1, int rs, int lim,
                                        uint16_t* T0, uint16_t* T1, int w) const {
@@ -91,7 +142,7 @@ struct TilePair {
       const uint32_t off = 2u * (uint32_t)(min(rowbase, lim - 1) * rs + xbase);
       const char* src = reinterpret_cast<const char*>(second ? G1 : G0) + off;
       uint16_t* dst = (second ? T1 : T0) + wp * 512;
-      __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)dst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)dst, 16, 0, AUX);
       return;
     }
 #pragma unroll
@@ -103,7 +154,7 @@ struct TilePair {
         const uint32_t off = 2u * (uint32_t)(min(row, lim - 1) * rs + x);
         const char* src = reinterpret_cast<const char*>(t ? G1 : G0) + off;
         uint16_t* dst = (t ? T1 : T0) + (wp + 4 * j) * 512;
-        __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)dst, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)dst, 16, 0, AUX);
       }
     }
   }
