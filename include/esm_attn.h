@@ -37,6 +37,12 @@
  *   lse                         : float, [H][T], natural log
  *   cu_seqlens                  : int32_t, [batch + 1], DEVICE memory
  *   head_dim d                  : 16, 32, 64 or 128
+ *   The planned calls also take token row strides (elements between the
+ *   starts of consecutive tokens' rows; H*d for the packed layout above): a
+ *   fused projection's output [T][3][H][d] is used in place as q, k, v with
+ *   stride 3*H*d, and dq, dk, dv can be written into one [T][3][H][d]
+ *   gradient the same way. A stride must be >= H*d, a multiple of 8, and
+ *   total_tokens * stride < 2^31 (else ESM_ATTN_ERR_UNSUPPORTED).
  *
  * Ownership and execution
  *   The caller allocates every buffer (inputs, outputs, workspace); the library
@@ -78,7 +84,7 @@
 extern "C" {
 #endif
 
-#define ESM_ATTN_ABI_VERSION 2
+#define ESM_ATTN_ABI_VERSION 3
 
 typedef int32_t esm_attn_status_t;
 #define ESM_ATTN_OK 0
@@ -142,7 +148,11 @@ esm_attn_status_t esm_attn_bwd(
  *   3. the attention kernels on q~, k~ (esm_attn_fwd_planned,
  *      esm_attn_bwd_planned).
  * A caller that runs the forward and backward of one batch can run steps 1
- * and 2 once and keep q~ and k~ (instead of q and k) for the backward.
+ * and 2 once and keep q~ and k~ (instead of q and k) for the backward. The
+ * plan depends only on cu_seqlens, the sizes and rope_base, so one plan
+ * serves every layer of a model for that batch (the rotary table is shared
+ * across layers); a fused layer rotates q and k in place inside its
+ * [T][3][H][d] projection output and keeps that buffer for its backward.
  *
  * The plan buffer is device memory of esm_attn_plan_bytes() bytes, owned by
  * the caller, valid for the sizes, cu_seqlens contents and rope_base it was
@@ -161,29 +171,38 @@ esm_attn_status_t esm_attn_plan(const int32_t* cu_seqlens, int32_t batch,
 /* Rotary embedding of q and k (RoFormer's rotation with x_j paired with
  * x_{j+d/2}, angles p * rope_base^(-2j/d) from the plan's table): every
  * element pair is turned in float32 (products and sums rounded one by one) and
- * rounded once to bf16, round to nearest even. Writes q_rot and k_rot, bf16
- * [T][H][d]; with rope_base = 0 it copies. q_rot and k_rot must not alias
- * q or k. */
+ * rounded once to bf16, round to nearest even. Reads q and k with token row
+ * stride in_row_stride and writes q_rot and k_rot, bf16, with stride
+ * out_row_stride; with rope_base = 0 it copies. In place is allowed:
+ * q_rot == q and k_rot == k with equal strides (a fused layer rotates q and
+ * k inside its [T][3][H][d] projection output); q_rot == q without
+ * k_rot == k, or in place with different strides, is
+ * ESM_ATTN_ERR_INVALID_ARGUMENT. Otherwise outputs must not overlap inputs. */
 esm_attn_status_t esm_attn_rotate_planned(
-    const uint16_t* q, const uint16_t* k,
+    const uint16_t* q, const uint16_t* k, int32_t in_row_stride,
     int32_t batch, int32_t total_tokens, int32_t max_seqlen,
     int32_t num_heads, int32_t head_dim, float rope_base,
-    uint16_t* q_rot, uint16_t* k_rot,
+    uint16_t* q_rot, uint16_t* k_rot, int32_t out_row_stride,
     const void* plan, size_t plan_bytes, void* stream);
 
 /* Forward on rotated operands: q_rot and k_rot as esm_attn_rotate_planned
- * wrote them (or q and k themselves without rotary embedding). Writes o and
- * lse as esm_attn_fwd does. */
+ * wrote them (or q and k themselves without rotary embedding), and v, all
+ * with token row stride qkv_row_stride (they may interleave in one fused
+ * buffer). Writes o ([T][H][d], packed) and lse as esm_attn_fwd does. */
 esm_attn_status_t esm_attn_fwd_planned(
     const uint16_t* q_rot, const uint16_t* k_rot, const uint16_t* v,
+    int32_t qkv_row_stride,
     int32_t batch, int32_t total_tokens, int32_t max_seqlen,
     int32_t num_heads, int32_t head_dim, float softmax_scale,
     uint16_t* o, float* lse,
     const void* plan, size_t plan_bytes, void* stream);
 
-/* Backward on rotated operands (q_rot, k_rot as for the forward; dq and dk
- * are still the gradients with respect to the pre-rotation q and k: the
- * kernels apply R(p)^T, for which they need rope_base). drow: caller-provided
+/* Backward on rotated operands (q_rot, k_rot, v and their stride as for the
+ * forward; o and d_o packed [T][H][d]); dq and dk are still the gradients
+ * with respect to the pre-rotation q and k: the kernels apply R(p)^T, for
+ * which they need rope_base. dq, dk, dv are written with token row stride
+ * grad_row_stride (they may interleave in one [T][3][H][d] gradient; they
+ * must not overlap any input). drow: caller-provided
  * fp32 [2][H][T] buffer (D = rowsum(dO * O), then LSE * log2(e)). passes is a
  * bit mask: ESM_ATTN_PASS_DQ runs the dq pass (reads o and lse, writes dq and
  * drow), ESM_ATTN_PASS_DKV the dk/dv pass (reads drow, writes dk and dv);
@@ -194,11 +213,13 @@ esm_attn_status_t esm_attn_fwd_planned(
 #define ESM_ATTN_PASS_DKV 2
 esm_attn_status_t esm_attn_bwd_planned(
     const uint16_t* q_rot, const uint16_t* k_rot, const uint16_t* v,
+    int32_t qkv_row_stride,
     const uint16_t* o, const uint16_t* d_o, const float* lse,
     int32_t batch, int32_t total_tokens, int32_t max_seqlen,
     int32_t num_heads, int32_t head_dim,
     float softmax_scale, float rope_base,
-    uint16_t* dq, uint16_t* dk, uint16_t* dv, float* drow, int32_t passes,
+    uint16_t* dq, uint16_t* dk, uint16_t* dv, int32_t grad_row_stride,
+    float* drow, int32_t passes,
     const void* plan, size_t plan_bytes, void* stream);
 
 /* Host-only check of a HOST copy of cu_seqlens: cu[0] = 0, nondecreasing,

@@ -65,6 +65,14 @@ Layout make_layout(int32_t B, int32_t T, int32_t maxL, int32_t H, int32_t d, boo
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// A token row stride: at least H*d elements, rows 16-byte aligned, and every
+// element offset below 2^31 (the kernels address rows with 32-bit offsets).
+esm_attn_status_t check_stride(int32_t ld, int32_t T, int32_t H, int32_t d) {
+  if (ld < H * d || ld % 8 != 0) return ESM_ATTN_ERR_INVALID_ARGUMENT;
+  if ((int64_t)T * ld >= ((int64_t)1 << 31)) return ESM_ATTN_ERR_UNSUPPORTED;
+  return ESM_ATTN_OK;
+}
+
 esm_attn_status_t check_scalars(float scale, float rope_base) {
   if (!isfinite(scale)) return ESM_ATTN_ERR_INVALID_ARGUMENT;
   if (!isfinite(rope_base) || rope_base < 0.f) return ESM_ATTN_ERR_INVALID_ARGUMENT;
@@ -154,14 +162,22 @@ esm_attn_status_t esm_attn_plan(const int32_t* cu_seqlens, int32_t batch, int32_
                   static_cast<char*>(plan), reinterpret_cast<hipStream_t>(stream));
 }
 
-esm_attn_status_t esm_attn_rotate_planned(const uint16_t* q, const uint16_t* k, int32_t batch,
+esm_attn_status_t esm_attn_rotate_planned(const uint16_t* q, const uint16_t* k,
+                                          int32_t in_row_stride, int32_t batch,
                                           int32_t total_tokens, int32_t max_seqlen,
                                           int32_t num_heads, int32_t head_dim, float rope_base,
-                                          uint16_t* q_rot, uint16_t* k_rot, const void* plan,
+                                          uint16_t* q_rot, uint16_t* k_rot,
+                                          int32_t out_row_stride, const void* plan,
                                           size_t plan_bytes, void* stream) {
   esm_attn_status_t s = check_sizes(batch, total_tokens, max_seqlen, num_heads, head_dim);
   if (s != ESM_ATTN_OK) return s;
   if ((s = check_scalars(0.f, rope_base)) != ESM_ATTN_OK) return s;
+  if ((s = check_stride(in_row_stride, total_tokens, num_heads, head_dim)) != ESM_ATTN_OK ||
+      (s = check_stride(out_row_stride, total_tokens, num_heads, head_dim)) != ESM_ATTN_OK)
+    return s;
+  // in place: both outputs on their inputs, with the same stride
+  const bool qin = q_rot == q, kin = k_rot == k;
+  if (qin != kin || (qin && in_row_stride != out_row_stride)) return ESM_ATTN_ERR_INVALID_ARGUMENT;
   if (total_tokens == 0) return ESM_ATTN_OK;
   const void* ptrs[] = {q, k, q_rot, k_rot, plan};
   for (const void* p : ptrs)
@@ -175,6 +191,8 @@ esm_attn_status_t esm_attn_rotate_planned(const uint16_t* q, const uint16_t* k, 
   a.k = k;
   a.q_rot = q_rot;
   a.k_rot = k_rot;
+  a.ld_in = in_row_stride;
+  a.ld_out = out_row_stride;
   a.rope = reinterpret_cast<const float2*>(ws + l.rope);
   a.items = reinterpret_cast<const Item*>(ws + l.items);
   a.H = num_heads;
@@ -185,13 +203,16 @@ esm_attn_status_t esm_attn_rotate_planned(const uint16_t* q, const uint16_t* k, 
 }
 
 esm_attn_status_t esm_attn_fwd_planned(const uint16_t* q_rot, const uint16_t* k_rot,
-                                       const uint16_t* v, int32_t batch, int32_t total_tokens,
-                                       int32_t max_seqlen, int32_t num_heads, int32_t head_dim,
-                                       float softmax_scale, uint16_t* o, float* lse,
-                                       const void* plan, size_t plan_bytes, void* stream) {
+                                       const uint16_t* v, int32_t qkv_row_stride, int32_t batch,
+                                       int32_t total_tokens, int32_t max_seqlen,
+                                       int32_t num_heads, int32_t head_dim, float softmax_scale,
+                                       uint16_t* o, float* lse, const void* plan,
+                                       size_t plan_bytes, void* stream) {
   esm_attn_status_t s = check_sizes(batch, total_tokens, max_seqlen, num_heads, head_dim);
   if (s != ESM_ATTN_OK) return s;
   if ((s = check_scalars(softmax_scale, 0.f)) != ESM_ATTN_OK) return s;
+  if ((s = check_stride(qkv_row_stride, total_tokens, num_heads, head_dim)) != ESM_ATTN_OK)
+    return s;
   if (total_tokens == 0) return ESM_ATTN_OK;
   const void* ptrs[] = {q_rot, k_rot, v, o, lse, plan};
   for (const void* p : ptrs)
@@ -207,6 +228,7 @@ esm_attn_status_t esm_attn_fwd_planned(const uint16_t* q_rot, const uint16_t* k_
   a.out = o;
   a.lse = lse;
   a.items = reinterpret_cast<const Item*>(ws + l.items);
+  a.ld_qkv = qkv_row_stride;
   fill_common(&a, total_tokens, num_heads, softmax_scale);
   if (launch_fwd(head_dim, a, l.n_slots, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
     return ESM_ATTN_ERR_HIP;
@@ -214,15 +236,19 @@ esm_attn_status_t esm_attn_fwd_planned(const uint16_t* q_rot, const uint16_t* k_
 }
 
 esm_attn_status_t esm_attn_bwd_planned(const uint16_t* q_rot, const uint16_t* k_rot,
-                                       const uint16_t* v, const uint16_t* o, const uint16_t* d_o,
-                                       const float* lse, int32_t batch, int32_t total_tokens,
-                                       int32_t max_seqlen, int32_t num_heads, int32_t head_dim,
-                                       float softmax_scale, float rope_base, uint16_t* dq,
-                                       uint16_t* dk, uint16_t* dv, float* drow, int32_t passes,
+                                       const uint16_t* v, int32_t qkv_row_stride,
+                                       const uint16_t* o, const uint16_t* d_o, const float* lse,
+                                       int32_t batch, int32_t total_tokens, int32_t max_seqlen,
+                                       int32_t num_heads, int32_t head_dim, float softmax_scale,
+                                       float rope_base, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+                                       int32_t grad_row_stride, float* drow, int32_t passes,
                                        const void* plan, size_t plan_bytes, void* stream) {
   esm_attn_status_t s = check_sizes(batch, total_tokens, max_seqlen, num_heads, head_dim);
   if (s != ESM_ATTN_OK) return s;
   if ((s = check_scalars(softmax_scale, rope_base)) != ESM_ATTN_OK) return s;
+  if ((s = check_stride(qkv_row_stride, total_tokens, num_heads, head_dim)) != ESM_ATTN_OK ||
+      (s = check_stride(grad_row_stride, total_tokens, num_heads, head_dim)) != ESM_ATTN_OK)
+    return s;
   if (passes < 1 || passes > (ESM_ATTN_PASS_DQ | ESM_ATTN_PASS_DKV))
     return ESM_ATTN_ERR_INVALID_ARGUMENT;
   if (total_tokens == 0) return ESM_ATTN_OK;
@@ -252,6 +278,8 @@ esm_attn_status_t esm_attn_bwd_planned(const uint16_t* q_rot, const uint16_t* k_
   a.drow = drow;
   a.rope = reinterpret_cast<const float2*>(ws + l.rope);
   a.items = reinterpret_cast<const Item*>(ws + l.items);
+  a.ld_qkv = qkv_row_stride;
+  a.ld_grad = grad_row_stride;
   fill_common(&a, total_tokens, num_heads, softmax_scale);
   if (launch_bwd(head_dim, rope_base != 0.f, a, l.n_slots, pdq, pdkv,
                  reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
@@ -281,12 +309,14 @@ esm_attn_status_t esm_attn_fwd(const uint16_t* q, const uint16_t* k, const uint1
   if ((s = esm_attn_plan(cu_seqlens, batch, total_tokens, max_seqlen, num_heads, head_dim,
                          rope_base, ws, l.plan, stream)) != ESM_ATTN_OK)
     return s;
-  if (rope && (s = esm_attn_rotate_planned(q, k, batch, total_tokens, max_seqlen, num_heads,
-                                           head_dim, rope_base, qr, kr, ws, l.plan, stream)) !=
-                  ESM_ATTN_OK)
+  const int32_t ld = num_heads * head_dim;
+  if (rope && (s = esm_attn_rotate_planned(q, k, ld, batch, total_tokens, max_seqlen, num_heads,
+                                           head_dim, rope_base, qr, kr, ld, ws, l.plan,
+                                           stream)) != ESM_ATTN_OK)
     return s;
-  return esm_attn_fwd_planned(rope ? qr : q, rope ? kr : k, v, batch, total_tokens, max_seqlen,
-                              num_heads, head_dim, softmax_scale, o, lse, ws, l.plan, stream);
+  return esm_attn_fwd_planned(rope ? qr : q, rope ? kr : k, v, ld, batch, total_tokens,
+                              max_seqlen, num_heads, head_dim, softmax_scale, o, lse, ws, l.plan,
+                              stream);
 }
 
 esm_attn_status_t esm_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
@@ -313,13 +343,14 @@ esm_attn_status_t esm_attn_bwd(const uint16_t* q, const uint16_t* k, const uint1
   if ((s = esm_attn_plan(cu_seqlens, batch, total_tokens, max_seqlen, num_heads, head_dim,
                          rope_base, ws, l.plan, stream)) != ESM_ATTN_OK)
     return s;
-  if (rope && (s = esm_attn_rotate_planned(q, k, batch, total_tokens, max_seqlen, num_heads,
-                                           head_dim, rope_base, qr, kr, ws, l.plan, stream)) !=
-                  ESM_ATTN_OK)
+  const int32_t ld = num_heads * head_dim;
+  if (rope && (s = esm_attn_rotate_planned(q, k, ld, batch, total_tokens, max_seqlen, num_heads,
+                                           head_dim, rope_base, qr, kr, ld, ws, l.plan,
+                                           stream)) != ESM_ATTN_OK)
     return s;
-  return esm_attn_bwd_planned(rope ? qr : q, rope ? kr : k, v, o, d_o, lse, batch, total_tokens,
-                              max_seqlen, num_heads, head_dim, softmax_scale, rope_base, dq, dk,
-                              dv, reinterpret_cast<float*>(ws + l.drow),
+  return esm_attn_bwd_planned(rope ? qr : q, rope ? kr : k, v, ld, o, d_o, lse, batch,
+                              total_tokens, max_seqlen, num_heads, head_dim, softmax_scale,
+                              rope_base, dq, dk, dv, ld, reinterpret_cast<float*>(ws + l.drow),
                               ESM_ATTN_PASS_DQ | ESM_ATTN_PASS_DKV, ws, l.plan, stream);
 }
 

@@ -60,13 +60,15 @@ __global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(AttnArgs a) 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 31, g = lane >> 5, prow = perm_row(r);
-  const int rs = a.H * D;  // row stride; T*H*d < 2^31 is checked on the host
+  // row strides (T * stride < 2^31 is checked on the host): q~, k~, v; o, dO
+  const int rs = a.ld_qkv, rso = a.H * D;
   const int64_t base = (int64_t)it.seq0 * rs + (int64_t)h * D;
+  const int64_t baseo = (int64_t)it.seq0 * rso + (int64_t)h * D;
   const uint16_t* __restrict__ Qg = a.q + base;
   const uint16_t* __restrict__ Kg = a.k + base;
   const uint16_t* __restrict__ Vg = a.v + base;
-  const uint16_t* __restrict__ Og = a.o + base;
-  const uint16_t* __restrict__ dOg = a.dout + base;
+  const uint16_t* __restrict__ Og = a.o + baseo;
+  const uint16_t* __restrict__ dOg = a.dout + baseo;
 
   // k~ and v rows of key block kb -> LDS stage `stage` (offsets kept in
   // registers for blocks with every key present)
@@ -78,7 +80,7 @@ __global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(AttnArgs a) 
     if (k0 + C::BN <= L)
       loader.load_full(Kg + (int64_t)k0 * rs, Vg + (int64_t)k0 * rs, koff, Ks, Ks + C::TILE, w);
     else
-      loader.template load<1>(Kg + (int64_t)k0 * rs, Vg + (int64_t)k0 * rs, rs, L - k0, Ks,
+      loader.template load<1>(Kg + (int64_t)k0 * rs, rs, Vg + (int64_t)k0 * rs, rs, L - k0, Ks,
                               Ks + C::TILE, w);
   };
   const int nkb = (L + C::BN - 1) / C::BN;
@@ -98,8 +100,8 @@ __global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(AttnArgs a) 
       qreg[s] = ld16(Qg + qi * rs + 16 * s + 8 * g);
 #pragma unroll
       for (int e = 0; e < 4; ++e) qreg[s][e] ^= qflip;
-      doreg[s] = ld16(dOg + qi * rs + 16 * s + 8 * g);
-      const u32x4 ov = ld16(Og + qi * rs + 16 * s + 8 * g);
+      doreg[s] = ld16(dOg + qi * rso + 16 * s + 8 * g);
+      const u32x4 ov = ld16(Og + qi * rso + 16 * s + 8 * g);
       float fo[8], fd[8];
       unpack8(ov, fo);
       unpack8(doreg[s], fd);
@@ -207,7 +209,8 @@ __global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(AttnArgs a) 
     }
   }
   __syncthreads();
-  store_rows<D, ROPE>(F, C::BM, q0, L, a.dq + base, rs, a.rope, true, tid);
+  store_rows<D, ROPE>(F, C::BM, q0, L, a.dq + (int64_t)it.seq0 * a.ld_grad + (int64_t)h * D,
+                     a.ld_grad, a.rope, true, tid);
 }
 
 // =========================================================================
@@ -242,12 +245,13 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkv_kernel(AttnArgs a
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 31, g = lane >> 5, prow = perm_row(r);
-  const int rs = a.H * D;  // row stride; T*H*d < 2^31 is checked on the host
+  // row strides (T * stride < 2^31 is checked on the host): q~, k~, v; dO
+  const int rs = a.ld_qkv, rso = a.H * D;
   const int64_t base = (int64_t)it.seq0 * rs + (int64_t)h * D;
   const uint16_t* __restrict__ Qg = a.q + base;
   const uint16_t* __restrict__ Kg = a.k + base;
   const uint16_t* __restrict__ Vg = a.v + base;
-  const uint16_t* __restrict__ dOg = a.dout + base;
+  const uint16_t* __restrict__ dOg = a.dout + (int64_t)it.seq0 * rso + (int64_t)h * D;
   const int64_t row0 = (int64_t)h * a.T + it.seq0;
   // waves 0-1 copy halves of the lse2 row, waves 2-3 halves of the D row
   const float* __restrict__ Fg =
@@ -259,7 +263,8 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkv_kernel(AttnArgs a
     const int q0 = qb * C::BQ, lim = L - q0;
     uint16_t* Qs = lds + stage * C::STAGE;
     float* Fs = reinterpret_cast<float*>(Qs + 2 * C::TILE) + (w < 2 ? 0 : C::BQ);
-    loader.load(Qg + (int64_t)q0 * rs, dOg + (int64_t)q0 * rs, rs, lim, Qs, Qs + C::TILE, w);
+    loader.load(Qg + (int64_t)q0 * rs, rs, dOg + (int64_t)q0 * rso, rso, lim, Qs, Qs + C::TILE,
+                w);
     load_half_row_f32(Fg + q0, C::BQ, lim, Fs, w & 1);
   };
   const int nqb = (L + C::BQ - 1) / C::BQ;
@@ -399,7 +404,8 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkv_kernel(AttnArgs a
     }
   }
   __syncthreads();
-  store_rows<D, ROPE>(F, C::BK, k0, L, a.dk + base, rs, a.rope, true, tid);
+  const int64_t baseg = (int64_t)it.seq0 * a.ld_grad + (int64_t)h * D;
+  store_rows<D, ROPE>(F, C::BK, k0, L, a.dk + baseg, a.ld_grad, a.rope, true, tid);
   __syncthreads();
 #pragma unroll
   for (int dt = 0; dt < C::ND; ++dt) {
@@ -410,7 +416,7 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkv_kernel(AttnArgs a
     }
   }
   __syncthreads();
-  store_rows<D, ROPE>(F, C::BK, k0, L, a.dv + base, rs, a.rope, false, tid);
+  store_rows<D, ROPE>(F, C::BK, k0, L, a.dv + baseg, a.ld_grad, a.rope, false, tid);
 }
 
 template <int D, bool ROPE>

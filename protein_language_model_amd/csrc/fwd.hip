@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 31, g = lane >> 5, prow = perm_row(r);
-  const int rs = a.H * D;  // row stride; T*H*d < 2^31 is checked on the host
+  const int rs = a.ld_qkv;  // row stride of q~, k~, v; T * rs < 2^31 is checked on the host
   const int64_t base = (int64_t)it.seq0 * rs + (int64_t)h * D;
   const uint16_t* __restrict__ Qg = a.q + base;
   const uint16_t* __restrict__ Kg = a.k + base;
@@ -81,7 +81,7 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(AttnArgs a) {
     if (k0 + C::BN <= L)
       loader.load_full(Kg + (int64_t)k0 * rs, Vg + (int64_t)k0 * rs, koff, Ks, Ks + C::TILE, w);
     else
-      loader.template load<1>(Kg + (int64_t)k0 * rs, Vg + (int64_t)k0 * rs, rs, L - k0, Ks,
+      loader.template load<1>(Kg + (int64_t)k0 * rs, rs, Vg + (int64_t)k0 * rs, rs, L - k0, Ks,
                               Ks + C::TILE, w);
   };
   const int nkb = (L + C::BN - 1) / C::BN;
@@ -222,7 +222,8 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(AttnArgs a) {
   l += xor32(l);
   if (qi < L) {
     const float inv = 1.0f / l;
-    uint16_t* Og = a.out + base + qi * rs;
+    const int rso = a.H * D;
+    uint16_t* Og = a.out + (int64_t)(it.seq0 + qi) * rso + (int64_t)h * D;
 #pragma unroll
     for (int dt = 0; dt < C::ND; ++dt) {
       const int d0 = 32 * dt + 16 * g;

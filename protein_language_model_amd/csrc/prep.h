@@ -25,10 +25,12 @@ hipError_t launch_prep(const PrepArgs& a, hipStream_t stream);
 // Rotation pass: q_rot = bf16(R(p) q), k_rot = bf16(R(p) k), or copies when
 // rope is null.
 struct RotArgs {
-  const uint16_t* q;
-  const uint16_t* k;
+  const uint16_t* q;    // may equal q_rot (in place, same row stride)
+  const uint16_t* k;    // may equal k_rot
   uint16_t* q_rot;
   uint16_t* k_rot;
+  int32_t ld_in;        // elements between consecutive tokens' rows of q, k
+  int32_t ld_out;       // ... of q_rot, k_rot
   const float2* rope;   // [max_seqlen][d/2]
   const Item* items;
   int32_t H;
@@ -58,6 +60,8 @@ struct AttnArgs {
   float q_sign;         // sign applied to rotated q so that scores use |scale|
   float scale;          // softmax_scale (signed)
   float scale_abs;
+  int32_t ld_qkv;       // elements between consecutive tokens' rows of q~, k~, v
+  int32_t ld_grad;      // ... of dq, dk, dv (o, dO: H * d)
 };
 
 hipError_t launch_fwd(int head_dim, const AttnArgs& a, int64_t n_slots, hipStream_t stream);

@@ -8,6 +8,8 @@
 // by one (rotate8) and the result is rounded once to bf16 (round to nearest
 // even). Rotary embedding as in RoFormer (Su et al. 2021), with x_j paired
 // with x_{j+d/2}. With no rotary table (rope_base = 0) the kernel copies.
+// Every element is read and written by one thread, loads first, so the
+// outputs may be the inputs themselves (rotation in place).
 #include "common.h"
 #include "prep.h"
 
@@ -29,10 +31,10 @@ __global__ __launch_bounds__(256) void rotate_kernel(RotArgs a) {
   constexpr int UPR = D / 16;                        // 8-pair chunks per row
   constexpr int RR = kItemRows / kRotSplit;          // rows per workgroup
   constexpr int NU = (RR * UPR + 255) / 256;         // units per thread
-  const int rs = a.H * D;
   const int r0 = it.blk * kItemRows + blockIdx.y * RR;
   const int n = min(RR, it.len - r0) * UPR;          // may be <= 0
-  const int64_t base = (int64_t)it.seq0 * rs + (int64_t)it.head * D;
+  const int64_t bin = (int64_t)it.seq0 * a.ld_in + (int64_t)it.head * D;
+  const int64_t bout = (int64_t)it.seq0 * a.ld_out + (int64_t)it.head * D;
   u32x4 ql[NU], qh[NU], kl[NU], kh[NU];
   float2 cs[NU][8];
 #pragma unroll
@@ -40,7 +42,7 @@ __global__ __launch_bounds__(256) void rotate_kernel(RotArgs a) {
     const int u = threadIdx.x + 256 * x;
     if (u < n) {
       const int row = u / UPR, j0 = (u % UPR) * 8, pos = r0 + row;
-      const int64_t off = base + (int64_t)pos * rs + j0;
+      const int64_t off = bin + (int64_t)pos * a.ld_in + j0;
       ql[x] = ld16(a.q + off);
       qh[x] = ld16(a.q + off + D / 2);
       kl[x] = ld16(a.k + off);
@@ -53,7 +55,7 @@ __global__ __launch_bounds__(256) void rotate_kernel(RotArgs a) {
     const int u = threadIdx.x + 256 * x;
     if (u < n) {
       const int row = u / UPR, j0 = (u % UPR) * 8, pos = r0 + row;
-      const int64_t off = base + (int64_t)pos * rs + j0;
+      const int64_t off = bout + (int64_t)pos * a.ld_out + j0;
       u32x4 q0 = ql[x], q1 = qh[x], k0 = kl[x], k1 = kh[x];
       if (ROPE) {
         float lo[8], hi[8];

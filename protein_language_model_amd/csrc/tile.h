@@ -55,7 +55,7 @@ __device__ __forceinline__ void wait_vmem() {
 }
 
 // Loads two tiles of R rows at once, tile t's row i being global row
-// G_t + min(i, lim-1)*rs (rows past the valid range repeat the last valid
+// G_t + min(i, lim-1)*rs_t (rows past the valid range repeat the last valid
 // one, lim >= 1), into the swizzled LDS tiles T0 and T1. The tiles are
 // written in 1 KB pieces, one global_load_lds_dwordx4 per wave and piece
 // (lane l fills bytes 16l..16l+15 of the piece); wave w takes pieces
@@ -129,8 +129,8 @@ struct TilePair {
   // copies with load_full passes 1 here: the two call sites then cannot be
   // merged into one copy from a selected 64-bit address.
   template <int AUX = 0>
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ G0,
-                                       const uint16_t* __restrict__ G1, int rs, int lim,
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ G0, int rs0,
+                                       const uint16_t* __restrict__ G1, int rs1, int lim,
                                        uint16_t* T0, uint16_t* T1, int w) const {
     const int wp = SMALL ? (w & 1) : w;
     const int lane = lane_id_here();
@@ -139,7 +139,8 @@ struct TilePair {
     // uniform 64-bit base + 32-bit per-lane byte offset (the saddr form)
     if (SMALL) {
       const bool second = w >= 2;
-      const uint32_t off = 2u * (uint32_t)(min(rowbase, lim - 1) * rs + xbase);
+      const uint32_t off =
+          2u * (uint32_t)(min(rowbase, lim - 1) * (second ? rs1 : rs0) + xbase);
       const char* src = reinterpret_cast<const char*>(second ? G1 : G0) + off;
       uint16_t* dst = (second ? T1 : T0) + wp * 512;
       __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)dst, 16, 0, AUX);
@@ -151,7 +152,7 @@ struct TilePair {
       for (int j = 0; j < PER_TILE; ++j) {
         const int row = rowbase + ROWSTEP * j;
         const int x = xbase ^ (8 * swz<D>(ROWSTEP * j));
-        const uint32_t off = 2u * (uint32_t)(min(row, lim - 1) * rs + x);
+        const uint32_t off = 2u * (uint32_t)(min(row, lim - 1) * (t ? rs1 : rs0) + x);
         const char* src = reinterpret_cast<const char*>(t ? G1 : G0) + off;
         uint16_t* dst = (t ? T1 : T0) + (wp + 4 * j) * 512;
         __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)dst, 16, 0, AUX);

@@ -89,14 +89,14 @@ def lib():
     L.esm_attn_plan.restype = i32
     L.esm_attn_plan.argtypes = [vp, i32, i32, i32, i32, i32, f32, vp, u64, vp]
     L.esm_attn_rotate_planned.restype = i32
-    L.esm_attn_rotate_planned.argtypes = [vp, vp, i32, i32, i32, i32, i32, f32, vp, vp, vp, u64,
-                                          vp]
+    L.esm_attn_rotate_planned.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, f32, vp, vp, i32,
+                                          vp, u64, vp]
     L.esm_attn_fwd_planned.restype = i32
-    L.esm_attn_fwd_planned.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, f32, vp, vp, vp, u64,
-                                       vp]
+    L.esm_attn_fwd_planned.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp,
+                                       u64, vp]
     L.esm_attn_bwd_planned.restype = i32
-    L.esm_attn_bwd_planned.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32,
-                                       f32, vp, vp, vp, vp, i32, vp, u64, vp]
+    L.esm_attn_bwd_planned.argtypes = [vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, f32,
+                                       f32, vp, vp, vp, i32, vp, i32, vp, u64, vp]
     L.esm_attn_check_cu_seqlens_host.restype = i32
     L.esm_attn_check_cu_seqlens_host.argtypes = [vp, i32, i32, i32]
     L.esm_attn_schedule_host.restype = i32
@@ -148,6 +148,34 @@ def _check_qkv(*ts):
         if t.device != ts[0].device:
             raise ValueError("tensors on different devices")
     return T, H, d
+
+
+def _check_packed(shape, *ts):
+    for t in ts:
+        if t.dtype != torch.bfloat16 or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+            raise ValueError("expected a contiguous bf16 tensor of shape %s" % (tuple(shape),))
+
+
+def _row_stride(*ts):
+    """Common token row stride of bf16 [T, H, d] tensors whose (H, d) part is
+    packed (strides (ld, d, 1)); ld > H*d for views of a fused buffer such as
+    qkv.view(T, 3, H, d)[:, i]. Tensors of at most one token use H*d."""
+    T, H, d = ts[0].shape
+    strides = set()
+    for t in ts:
+        if t.dtype != torch.bfloat16 or t.shape != (T, H, d):
+            raise ValueError("expected bf16 tensors of shape [T, H, d]")
+        if t.device != ts[0].device:
+            raise ValueError("tensors on different devices")
+        if t.stride(2) != 1 or (H > 1 and t.stride(1) != d):
+            raise ValueError("expected rows with packed (H, d) (strides (ld, d, 1))")
+        strides.add(t.stride(0))
+    if T <= 1:
+        return H * d
+    if len(strides) != 1:
+        raise ValueError("these tensors must share one token row stride, got %s"
+                         % sorted(strides))
+    return strides.pop()
 
 
 def _workspace(nbytes, device, workspace):
@@ -216,26 +244,36 @@ def esm_attn_plan(cu_seqlens, total_tokens, max_seqlen, num_heads, head_dim,
 def esm_attn_rotate_planned(q, k, batch, max_seqlen, plan, rope_base=10000.0, q_rot=None,
                             k_rot=None, stream=None):
     """q~ = bf16(R(p) q), k~ = bf16(R(p) k) with the plan's rotary table;
-    returns (q_rot, k_rot)."""
-    T, H, d = _check_qkv(q, k)
-    q_rot = torch.empty_like(q) if q_rot is None else q_rot
-    k_rot = torch.empty_like(k) if k_rot is None else k_rot
-    _check(lib().esm_attn_rotate_planned(_ptr(q), _ptr(k), int(batch), T, int(max_seqlen), H, d,
-                                         float(rope_base), _ptr(q_rot), _ptr(k_rot), _ptr(plan),
-                                         plan.numel(), _stream(stream)))
+    returns (q_rot, k_rot). q and k may be views of a fused [T, 3, H, d]
+    buffer; q_rot=q, k_rot=k rotates in place."""
+    T, H, d = q.shape
+    ld_in = _row_stride(q, k)
+    if q_rot is None:
+        q_rot = torch.empty((T, H, d), dtype=q.dtype, device=q.device)
+    if k_rot is None:
+        k_rot = torch.empty((T, H, d), dtype=k.dtype, device=k.device)
+    ld_out = _row_stride(q_rot, k_rot)
+    _check(lib().esm_attn_rotate_planned(_ptr(q), _ptr(k), ld_in, int(batch), T,
+                                         int(max_seqlen), H, d, float(rope_base), _ptr(q_rot),
+                                         _ptr(k_rot), ld_out, _ptr(plan), plan.numel(),
+                                         _stream(stream)))
     return q_rot, k_rot
 
 
 def esm_attn_fwd_planned(q_rot, k_rot, v, batch, max_seqlen, plan, softmax_scale=None,
                          out=None, lse=None, stream=None):
-    """Forward on rotated q~, k~ (esm_attn_rotate_planned's outputs)."""
-    T, H, d = _check_qkv(q_rot, k_rot, v)
+    """Forward on rotated q~, k~ (esm_attn_rotate_planned's outputs) and v,
+    which share one token row stride (e.g. views of a fused [T, 3, H, d]
+    buffer). out: packed [T, H, d]."""
+    T, H, d = v.shape
+    ld = _row_stride(q_rot, k_rot, v)
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     if out is None:
-        out = torch.empty_like(v)
+        out = torch.empty((T, H, d), dtype=v.dtype, device=v.device)
+    _check_packed((T, H, d), out)
     if lse is None:
         lse = torch.empty((H, T), dtype=torch.float32, device=v.device)
-    _check(lib().esm_attn_fwd_planned(_ptr(q_rot), _ptr(k_rot), _ptr(v), int(batch), T,
+    _check(lib().esm_attn_fwd_planned(_ptr(q_rot), _ptr(k_rot), _ptr(v), ld, int(batch), T,
                                       int(max_seqlen), H, d, scale, _ptr(out), _ptr(lse),
                                       _ptr(plan), plan.numel(), _stream(stream)))
     return out, lse
@@ -244,20 +282,30 @@ def esm_attn_fwd_planned(q_rot, k_rot, v, batch, max_seqlen, plan, softmax_scale
 def esm_attn_bwd_planned(q_rot, k_rot, v, o, d_o, lse, batch, max_seqlen, plan,
                          softmax_scale=None, rope_base=10000.0, dq=None, dk=None, dv=None,
                          drow=None, passes=PASS_DQ | PASS_DKV, stream=None):
-    """Backward on rotated q~, k~; dq and dk are gradients with respect to the
-    pre-rotation q and k. drow: fp32 [2, H, T] scratch shared by the passes."""
-    T, H, d = _check_qkv(q_rot, k_rot, v, d_o)
+    """Backward on rotated q~, k~ (and v, one token row stride, as for the
+    forward; o and d_o packed); dq and dk are gradients with respect to the
+    pre-rotation q and k. dq, dk, dv share one token row stride (e.g. views
+    of a fused [T, 3, H, d] gradient). drow: fp32 [2, H, T] scratch shared
+    by the passes."""
+    T, H, d = v.shape
+    ld = _row_stride(q_rot, k_rot, v)
+    _check_packed((T, H, d), d_o, *([o] if passes & PASS_DQ else []))
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     if drow is None:
         drow = torch.empty((2, H, T), dtype=torch.float32, device=v.device)
-    if passes & PASS_DQ and dq is None:
-        dq = torch.empty_like(q_rot)
+    new = lambda: torch.empty((T, H, d), dtype=v.dtype, device=v.device)
+    grads = []
+    if passes & PASS_DQ:
+        dq = new() if dq is None else dq
+        grads.append(dq)
     if passes & PASS_DKV:
-        dk = torch.empty_like(k_rot) if dk is None else dk
-        dv = torch.empty_like(v) if dv is None else dv
-    _check(lib().esm_attn_bwd_planned(_ptr(q_rot), _ptr(k_rot), _ptr(v), _ptr(o), _ptr(d_o),
+        dk = new() if dk is None else dk
+        dv = new() if dv is None else dv
+        grads += [dk, dv]
+    ld_grad = _row_stride(*grads)
+    _check(lib().esm_attn_bwd_planned(_ptr(q_rot), _ptr(k_rot), _ptr(v), ld, _ptr(o), _ptr(d_o),
                                       _ptr(lse), int(batch), T, int(max_seqlen), H, d, scale,
-                                      float(rope_base), _ptr(dq), _ptr(dk), _ptr(dv),
+                                      float(rope_base), _ptr(dq), _ptr(dk), _ptr(dv), ld_grad,
                                       _ptr(drow), int(passes), _ptr(plan), plan.numel(),
                                       _stream(stream)))
     return dq, dk, dv, drow

@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported():
     for n in names:
         assert hasattr(lib, n), n
     assert set(E.EXPORTED) == set(names)
-    assert E.esm_attn_abi_version() == 2
+    assert E.esm_attn_abi_version() == 3
 
 
 def test_single_hip_runtime_is_mapped():
@@ -105,29 +105,70 @@ def test_backward_and_planned_validation():
     assert st == E.ERR_INVALID_ARGUMENT
     st = L.esm_attn_bwd(p, p, p, p, p, p, p, 1, 8, 8, 1, 32, 0.1, 1e4, p, p, p, p, 8, None)
     assert st == E.ERR_WORKSPACE_TOO_SMALL
-    st = L.esm_attn_bwd_planned(p, p, p, p, p, p, 1, 8, 8, 1, 32, 0.1, 1e4, p, p, p, p, 0, p,
-                                1 << 30, None)
+    st = L.esm_attn_bwd_planned(p, p, p, 32, p, p, p, 1, 8, 8, 1, 32, 0.1, 1e4, p, p, p, 32, p,
+                                0, p, 1 << 30, None)
     assert st == E.ERR_INVALID_ARGUMENT      # no pass selected
-    st = L.esm_attn_bwd_planned(p, p, p, p, p, p, 1, 8, 8, 1, 32, 0.1, 1e4, None, p, p, p, 1, p,
-                                1 << 30, None)
+    st = L.esm_attn_bwd_planned(p, p, p, 32, p, p, p, 1, 8, 8, 1, 32, 0.1, 1e4, None, p, p, 32,
+                                p, 1, p, 1 << 30, None)
     assert st == E.ERR_INVALID_ARGUMENT      # dq pass without dq
     st = L.esm_attn_plan(p, 1, 8, 8, 1, 32, -5.0, p, 1 << 30, None)
     assert st == E.ERR_INVALID_ARGUMENT
-    st = L.esm_attn_fwd_planned(p, p, p, 1, 8, 8, 1, 32, 0.1, p, p, p, 4, None)
+    st = L.esm_attn_fwd_planned(p, p, p, 32, 1, 8, 8, 1, 32, 0.1, p, p, p, 4, None)
     assert st == E.ERR_WORKSPACE_TOO_SMALL
-    st = L.esm_attn_fwd_planned(p, p, p, 1, 8, 8, 1, 32, float("nan"), p, p, p, 1 << 30, None)
+    st = L.esm_attn_fwd_planned(p, p, p, 32, 1, 8, 8, 1, 32, float("nan"), p, p, p, 1 << 30,
+                                None)
     assert st == E.ERR_INVALID_ARGUMENT
-    # rotation step
-    st = L.esm_attn_rotate_planned(p, p, 1, 8, 8, 1, 32, 1e4, p, p, p, 4, None)
+    # rotation step (q_rot == q and k_rot == k with equal strides: in place)
+    st = L.esm_attn_rotate_planned(p, p, 32, 1, 8, 8, 1, 32, 1e4, p, p, 32, p, 4, None)
     assert st == E.ERR_WORKSPACE_TOO_SMALL
-    st = L.esm_attn_rotate_planned(p, p, 1, 8, 8, 1, 32, -1.0, p, p, p, 1 << 30, None)
+    st = L.esm_attn_rotate_planned(p, p, 32, 1, 8, 8, 1, 32, -1.0, p, p, 32, p, 1 << 30, None)
     assert st == E.ERR_INVALID_ARGUMENT
-    st = L.esm_attn_rotate_planned(p, p, 1, 8, 8, 1, 32, 1e4, None, p, p, 1 << 30, None)
+    st = L.esm_attn_rotate_planned(p, p, 32, 1, 8, 8, 1, 32, 1e4, None, p, 32, p, 1 << 30, None)
     assert st == E.ERR_INVALID_ARGUMENT
-    st = L.esm_attn_rotate_planned(p, p, 1, 8, 8, 1, 48, 1e4, p, p, p, 1 << 30, None)
+    st = L.esm_attn_rotate_planned(p, p, 48, 1, 8, 8, 1, 48, 1e4, p, p, 48, p, 1 << 30, None)
     assert st == E.ERR_UNSUPPORTED
-    assert L.esm_attn_rotate_planned(None, None, 1, 0, 0, 1, 32, 1e4, None, None, None, 0,
-                                     None) == E.OK
+    assert L.esm_attn_rotate_planned(None, None, 32, 1, 0, 0, 1, 32, 1e4, None, None, 32, None,
+                                     0, None) == E.OK
+
+
+@pytest.mark.parametrize("call,ld,status", [
+    ("rotate", 16, E.ERR_INVALID_ARGUMENT),         # below H*d (H = 2, d = 16)
+    ("rotate", 36, E.ERR_INVALID_ARGUMENT),         # not a multiple of 8
+    ("rotate", 1 << 28, E.ERR_UNSUPPORTED),         # T * stride >= 2^31
+    ("fwd", 24, E.ERR_INVALID_ARGUMENT),
+    ("fwd", 1 << 28, E.ERR_UNSUPPORTED),
+    ("bwd_qkv", 20, E.ERR_INVALID_ARGUMENT),
+    ("bwd_grad", 1 << 28, E.ERR_UNSUPPORTED),
+])
+def test_row_stride_validation(call, ld, status):
+    """Token row strides are checked on the host before anything is enqueued
+    (fake device pointers: a launch would fault)."""
+    L = E.lib()
+    p, q, T = 1 << 12, 1 << 13, 8
+    if call == "rotate":
+        st = L.esm_attn_rotate_planned(p, p, ld, 1, T, T, 2, 16, 1e4, q, q, 32, p, 1 << 30, None)
+    elif call == "fwd":
+        st = L.esm_attn_fwd_planned(p, p, p, ld, 1, T, T, 2, 16, 0.1, q, q, p, 1 << 30, None)
+    else:
+        lq, lg = (ld, 96) if call == "bwd_qkv" else (96, ld)
+        st = L.esm_attn_bwd_planned(p, p, p, lq, p, p, p, 1, T, T, 2, 16, 0.1, 1e4, q, q, q, lg,
+                                    q, 3, p, 1 << 30, None)
+    assert st == status
+
+
+def test_in_place_rotation_rules():
+    """In place means both outputs on their inputs with one stride."""
+    L = E.lib()
+    p, q, r, T = 1 << 12, 1 << 13, 1 << 14, 8
+    # q in place, k not
+    assert L.esm_attn_rotate_planned(p, q, 32, 1, T, T, 2, 16, 1e4, p, r, 32, p, 4,
+                                     None) == E.ERR_INVALID_ARGUMENT
+    # in place with different strides
+    assert L.esm_attn_rotate_planned(p, q, 96, 1, T, T, 2, 16, 1e4, p, q, 32, p, 4,
+                                     None) == E.ERR_INVALID_ARGUMENT
+    # in place, one stride: only the (too small) plan is left to reject
+    assert L.esm_attn_rotate_planned(p, q, 96, 1, T, T, 2, 16, 1e4, p, q, 96, p, 4,
+                                     None) == E.ERR_WORKSPACE_TOO_SMALL
 
 
 def test_check_cu_seqlens_host():

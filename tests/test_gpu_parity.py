@@ -214,6 +214,50 @@ def test_repeated_calls_on_one_plan(device, d):
         np.testing.assert_array_equal(a, gpu[n], err_msg=n)
 
 
+@pytest.mark.parametrize("d,pad", [(16, 0), (32, 8), (64, 0), (64, 24), (128, 0)])
+def test_fused_qkv_layout(device, d, pad):
+    """Strided operands: q, k, v as views of one [T, 3, H, d] projection
+    output (token row stride 3*H*d + pad), rotated in place, and dq, dk, dv
+    written into one fused gradient. Bitwise equal to the packed layout."""
+    name = {16: "esm2_8m", 32: "esm2_150m", 64: "esm2_650m", 128: "esm2_15b"}[d]
+    inp = _case(name, lengths=[300, 1, 129, 64, 0, 77], H=3)
+    T, H, B = inp["T"], inp["H"], len(inp["lengths"])
+    maxL, scale, base = max(inp["lengths"]), inp["scale"], inp["rope_base"]
+    ld = 3 * H * d + pad
+    say("case fused", d, "row stride", ld, "T", T)
+    ref = run_gpu(inp, device)
+    q, k, v, do = (to_dev(inp[x], device) for x in ("q", "k", "v", "do"))
+    buf = torch.zeros(T * ld + 64, dtype=torch.bfloat16, device=device)
+    rows = buf[: T * ld].view(T, ld)
+    view = lambda i: rows[:, i * H * d:(i + 1) * H * d].view(T, H, d)
+    qf, kf, vf = view(0), view(1), view(2)
+    qf.copy_(q)
+    kf.copy_(k)
+    vf.copy_(v)
+    assert qf.stride(0) == ld
+    cu = torch.from_numpy(inp["cu_seqlens"]).to(device)
+    plan = E.esm_attn_plan(cu, T, maxL, H, d, base)
+    qr, kr = E.esm_attn_rotate_planned(qf, kf, B, maxL, plan, base, q_rot=qf, k_rot=kf)
+    assert qr.data_ptr() == qf.data_ptr() and kr.data_ptr() == kf.data_ptr()
+    o, lse = E.esm_attn_fwd_planned(qf, kf, vf, B, maxL, plan, scale)
+    gbuf = torch.full((T * ld + 64,), float("nan"), dtype=torch.bfloat16, device=device)
+    grows = gbuf[: T * ld].view(T, ld)
+    gview = lambda i: grows[:, i * H * d:(i + 1) * H * d].view(T, H, d)
+    dq, dk, dv, _ = E.esm_attn_bwd_planned(qf, kf, vf, o, do, lse, B, maxL, plan, scale, base,
+                                           dq=gview(0), dk=gview(1), dv=gview(2))
+    torch.cuda.synchronize()
+    for n, t in (("o", o), ("dq", dq), ("dk", dk), ("dv", dv)):
+        np.testing.assert_array_equal(bf16_f64(t), ref[n], err_msg=n)
+    np.testing.assert_array_equal(lse.cpu().numpy().astype(np.float64), ref["lse"])
+    # the rotated q~, k~ sit in the q and k slots; v and the padding are untouched
+    qr2, kr2 = E.esm_attn_rotate_planned(q, k, B, maxL, plan, base)
+    torch.cuda.synchronize()
+    assert torch.equal(qf, qr2) and torch.equal(kf, kr2) and torch.equal(vf, v)
+    if pad:
+        assert not rows[:, 3 * H * d:].any()
+        assert torch.isnan(grows[:, 3 * H * d:].float()).all()
+
+
 def test_many_short_sequences(device):
     """More sequences than the planning kernel keeps in LDS (4096): the
     schedule then works from global memory."""
