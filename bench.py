@@ -16,6 +16,13 @@ each call inside the timed steps, on the stream the kernels are launched on;
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload esm2_650m]
                     [--no-cpu-baseline] [--cpu-seconds 15]
+
+`--attention-block` times instead the whole attention block of one layer at
+the workload's shape: QKV projection (one GEMM to [T][3][H][d]), this path
+on that fused buffer in place (rotation in place, strided q, k, v; dq, dk, dv
+into one fused gradient), output projection, forward and backward with the
+weight gradients; and the same block with the split layout (q, k, v copied
+out of the projection, the gradients concatenated). Prints one JSON line.
 """
 
 import argparse
@@ -41,6 +48,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 256 MiB device copy (calibrates HBM byte counters)")
+    p.add_argument("--attention-block", action="store_true",
+                   help="time QKV projection + attention + output projection, fwd + bwd")
     return p.parse_args()
 
 
@@ -128,16 +137,129 @@ def cpu_baseline(inp, budget_s):
                       % (done, inp["name"], len(slices), dt)}
 
 
+def attention_block(args):
+    """One layer's attention block, forward and backward, at the workload's
+    shape (hidden = H*d): qkv = x Wqkv^T + b; attention; y = o Wo^T + b; then
+    dO = dy Wo, dWo = dy^T o, the attention backward, dx = dqkv Wqkv,
+    dWqkv = dqkv^T x and the bias gradients. GEMMs are torch's (hipBLASLt);
+    the attention path is this library's. Counted flops: 24 T hidden^2 for
+    the GEMMs plus the attention's counted flops."""
+    import torch
+    import torch.nn.functional as F
+    from protein_language_model_amd import esm_attn as E
+    from protein_language_model_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    wl = W.WORKLOADS[args.workload]
+    lengths = W.lengths_of(args.workload)
+    H, d = wl.num_heads, wl.head_dim
+    hid, T, B, maxL = H * d, int(sum(lengths)), len(lengths), max(lengths)
+    scale, base = 1.0 / math.sqrt(d), W.ROPE_BASE
+    g = torch.Generator(device=dev).manual_seed(7)
+    rnd = lambda *shape, s=1.0: (torch.randn(*shape, generator=g, device=dev) * s).to(
+        torch.bfloat16)
+    x, dy = rnd(T, hid), rnd(T, hid)
+    wqkv, bqkv = rnd(3 * hid, hid, s=hid ** -0.5), rnd(3 * hid, s=0.02)
+    wo, bo = rnd(hid, hid, s=hid ** -0.5), rnd(hid, s=0.02)
+    cu = torch.from_numpy(W.cu_from_lengths(lengths)).to(dev)
+    plan = torch.empty(E.esm_attn_plan_bytes(B, T, maxL, H, d), dtype=torch.uint8, device=dev)
+    drow = torch.empty((2, H, T), dtype=torch.float32, device=dev)
+    dqkv = torch.empty((T, 3 * hid), dtype=torch.bfloat16, device=dev)
+    st = torch.cuda.current_stream()
+
+    def step(fused, ev=None):
+        def mark(j):
+            if ev is not None:
+                ev[j].record(st)
+        mark(0)
+        E.esm_attn_plan(cu, T, maxL, H, d, base, plan=plan)
+        qkv = F.linear(x, wqkv, bqkv).view(T, 3, H, d)
+        mark(1)
+        if fused:
+            q, k, v = qkv[:, 0], qkv[:, 1], qkv[:, 2]
+            E.esm_attn_rotate_planned(q, k, B, maxL, plan, base, q_rot=q, k_rot=k)
+        else:
+            q, k, v = qkv[:, 0].contiguous(), qkv[:, 1].contiguous(), qkv[:, 2].contiguous()
+            q, k = E.esm_attn_rotate_planned(q, k, B, maxL, plan, base)
+        o, lse = E.esm_attn_fwd_planned(q, k, v, B, maxL, plan, scale)
+        mark(2)
+        F.linear(o.view(T, hid), wo, bo)
+        dout = torch.mm(dy, wo).view(T, H, d)
+        torch.mm(dy.t(), o.view(T, hid))
+        dy.sum(0)
+        mark(3)
+        if fused:
+            g3 = dqkv.view(T, 3, H, d)
+            E.esm_attn_bwd_planned(q, k, v, o, dout, lse, B, maxL, plan, scale, base,
+                                   dq=g3[:, 0], dk=g3[:, 1], dv=g3[:, 2], drow=drow)
+            grad = dqkv
+        else:
+            dq, dk, dv, _ = E.esm_attn_bwd_planned(q, k, v, o, dout, lse, B, maxL, plan, scale,
+                                                   base, drow=drow)
+            grad = torch.stack((dq, dk, dv), dim=1).view(T, 3 * hid)
+        mark(4)
+        torch.mm(grad, wqkv)
+        torch.mm(grad.t(), x)
+        grad.sum(0)
+        mark(5)
+
+    def run(fused):
+        for _ in range(args.warmup):
+            step(fused)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(fused, evs[i])
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / args.steps
+        parts = ["plan + qkv proj", "rotate + attn fwd", "out proj fwd + bwd", "attn bwd",
+                 "qkv proj bwd"]
+        us = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) * 1e3
+              for j, n in enumerate(parts)}
+        return wall, us
+
+    wall_f, us_f = run(True)
+    wall_s, us_s = run(False)
+    gemm_f = 24.0 * T * hid * hid
+    fa, ba = W.counted_flops(lengths, H, d)
+    total = gemm_f + fa + ba
+    out = {
+        "metric": "attention block (QKV proj + attention + out proj) fwd+bwd TFLOP/s",
+        "value": round(total / wall_f / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_f * 1e3, 4),
+        "higher_is_better": True,
+        "dtype": "bf16",
+        "data": "synthetic (seeded normal activations and weights)",
+        "config": {"workload": "%s attention block: %d sequences, %d tokens, hidden %d, H=%d, d=%d"
+                               % (args.workload, B, T, hid, H, d)},
+        "mfu": round(total / wall_f / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "counted_flops": {"gemms": gemm_f, "attention": fa + ba},
+        "parts_us": {n: round(x, 1) for n, x in us_f.items()},
+        "split_layout": {"ms_per_step": round(wall_s * 1e3, 4),
+                         "value": round(total / wall_s / 1e12, 2),
+                         "parts_us": {n: round(x, 1) for n, x in us_s.items()}},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration()
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build runs the attention hot path on a "
-              "single MI355X (no sharding, no collectives); --gpus %d is not supported"
+        print("bench.py measures one GPU only: the library runs the attention hot path on "
+              "a single MI355X (no sharding, no collectives); --gpus %d is not supported"
               % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.attention_block:
+        attention_block(args)
+        return
 
     import torch
     from protein_language_model_amd import esm_attn as E
