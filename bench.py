@@ -23,6 +23,15 @@ on that fused buffer in place (rotation in place, strided q, k, v; dq, dk, dv
 into one fused gradient), output projection, forward and backward with the
 weight gradients; and the same block with the split layout (q, k, v copied
 out of the projection, the gradients concatenated). Prints one JSON line.
+
+`--packing-study` forms batches from a UniRef-like length mix (20,000
+lengths, lognormal with median 300 and sigma 0.8, cropped to [30, 1024]) with
+the library's size-aware bucket batcher under a 16,384-token budget, four
+ways (no buckets / 64-token buckets, packed / padded cost), reports padding
+and wasted attention work, and times this path (plan, rotation, forward,
+backward; H = 20, d = 64) over all of each way's batches (one epoch), padded
+batches run with every sequence at its batch's longest length. Prints one
+JSON line.
 """
 
 import argparse
@@ -50,6 +59,8 @@ def parse():
                    help="only run a plain 256 MiB device copy (calibrates HBM byte counters)")
     p.add_argument("--attention-block", action="store_true",
                    help="time QKV projection + attention + output projection, fwd + bwd")
+    p.add_argument("--packing-study", action="store_true",
+                   help="padded vs packed batches of a length mix: padding, waste, tokens/s")
     return p.parse_args()
 
 
@@ -247,6 +258,94 @@ def attention_block(args):
     print(json.dumps(out), flush=True)
 
 
+def packing_study(args):
+    """Bucketed size-aware batching, packed vs padded (see the module doc)."""
+    import torch
+    from protein_language_model_amd import esm_attn as E
+
+    rng = np.random.default_rng(2024)
+    lengths = np.clip(np.rint(rng.lognormal(math.log(300.0), 0.8, 20000)), 30, 1024).astype(
+        np.int64)
+    budget, H, d, base = 16384, 20, 64, 10000.0
+    scale = 1.0 / math.sqrt(d)
+    ways = {"no_buckets_padded": ([], True), "buckets64_padded": (list(range(64, 1025, 64)), True),
+            "no_buckets_packed": ([], False), "buckets64_packed": (list(range(64, 1025, 64)), False)}
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(5)
+    cap = 2 * budget  # tokens of the largest batch run (a padded batch of one can exceed budget)
+    buf = {n: (torch.randn(cap, H, d, generator=g, device=dev)).to(torch.bfloat16)
+           for n in ("q", "k", "v", "do")}
+    outs = {n: torch.empty(cap, H, d, dtype=torch.bfloat16, device=dev)
+            for n in ("qr", "kr", "o", "dq", "dk", "dv")}
+    lse = torch.empty(H * cap, dtype=torch.float32, device=dev)
+    drow = torch.empty(2 * H * cap, dtype=torch.float32, device=dev)
+
+    def prepare(run_lengths):  # device cu_seqlens and plan buffer, before timing
+        T, B, maxL = int(sum(run_lengths)), len(run_lengths), int(max(run_lengths))
+        cu = torch.from_numpy(np.concatenate([[0], np.cumsum(run_lengths)]).astype(np.int32)).to(
+            dev)
+        plan = torch.empty(E.esm_attn_plan_bytes(B, T, maxL, H, d), dtype=torch.uint8,
+                           device=dev)
+        return T, B, maxL, cu, plan
+
+    def run_batch(prep):
+        T, B, maxL, cu, plan = prep
+        q, k, v, do = (buf[n][:T] for n in ("q", "k", "v", "do"))
+        qr, kr, o, dq, dk, dv = (outs[n][:T] for n in ("qr", "kr", "o", "dq", "dk", "dv"))
+        E.esm_attn_plan(cu, T, maxL, H, d, base, plan=plan)
+        E.esm_attn_rotate_planned(q, k, B, maxL, plan, base, q_rot=qr, k_rot=kr)
+        E.esm_attn_fwd_planned(qr, kr, v, B, maxL, plan, scale, out=o, lse=lse[:H * T].view(H, T))
+        E.esm_attn_bwd_planned(qr, kr, v, o, do, lse[:H * T].view(H, T), B, maxL, plan, scale,
+                               base, dq=dq, dk=dk, dv=dv, drow=drow[:2 * H * T].view(2, H, T))
+
+    def tiles(L):  # pairs the 128-query x 64-key tiles cover
+        return -(-L // 128) * 128 * (-(-L // 64)) * 64
+
+    report = {}
+    sq = float((lengths ** 2).sum())
+    for name, (bounds, padded) in ways.items():
+        batches = E.esm_attn_bucket_batches(lengths, bounds, budget, padded)
+        run = [np.full(len(b), lengths[b].max()) if padded else lengths[b] for b in batches]
+        real = float(lengths.sum())
+        slots = float(sum(r.sum() for r in run))
+        pairs = float(sum((r.astype(np.float64) ** 2).sum() for r in run))
+        tile = float(sum(tiles(int(L)) for r in run for L in r))
+        # one pass over every batch (an epoch of the length mix), after a warmup
+        assert all(r.sum() <= cap for r in run)
+        epoch = [prepare(r) for r in run]
+        for r in epoch[:8]:
+            run_batch(r)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for r in epoch:
+            run_batch(r)
+        torch.cuda.synchronize()
+        best = time.perf_counter() - t0
+        report[name] = {
+            "batches": len(batches),
+            "mean_sequences_per_batch": round(len(lengths) / len(batches), 2),
+            "padding_fraction": round(1.0 - real / slots, 4),
+            "attention_pairs_over_sum_L2": round(pairs / sq, 4),
+            "kernel_tile_pairs_over_sum_L2": round(tile / sq, 4),
+            "epoch_ms": round(best * 1e3, 2),
+            "real_tokens_per_s": round(real / best, 1),
+        }
+    ref = report["buckets64_packed"]["real_tokens_per_s"]
+    out = {
+        "metric": "attention fwd+bwd real tokens/s by batching, packed vs padded",
+        "value": ref,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "higher_is_better": True,
+        "dtype": "bf16",
+        "data": "synthetic lengths (lognormal median 300, sigma 0.8, crop [30, 1024]), "
+                "seeded normal activations",
+        "config": {"workload": "20000 sequences, %d-token budget, H=%d, d=%d" % (budget, H, d)},
+        "ways": report,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -259,6 +358,9 @@ def main():
         sys.exit(2)
     if args.attention_block:
         attention_block(args)
+        return
+    if args.packing_study:
+        packing_study(args)
         return
 
     import torch

@@ -222,6 +222,33 @@ esm_attn_status_t esm_attn_bwd_planned(
     float* drow, int32_t passes,
     const void* plan, size_t plan_bytes, void* stream);
 
+/* Size-aware bucket batching (host only; reads host arrays, enqueues
+ * nothing). The "BioNeMo Framework" review page names a size-aware batcher and
+ * a bucket batch sampler ("proposed method") and credits them with
+ * near-uniform batch sizes and almost no padding ("main findings"); the rule
+ * implemented is this reading of them:
+ *   buckets   : n_boundaries increasing lengths b_0 < ... < b_{K-1} (each
+ *               >= 1) make the buckets [0, b_0), [b_0, b_1), ...,
+ *               [b_{K-1}, inf); no boundaries = one bucket;
+ *   batcher   : inside each bucket, sequences in input order are appended to
+ *               the current batch while its cost stays <= budget; one that
+ *               would exceed it starts the next batch (a sequence over budget
+ *               alone forms a batch of one). Cost = sum of lengths (padded = 0,
+ *               the packed layout) or batch size * longest length (padded = 1);
+ *   output    : batches bucket by bucket, in the order formed: batch b is
+ *               order[batch_offsets[b] .. batch_offsets[b+1]), indices into
+ *               lengths; order has n entries, batch_offsets
+ *               batch_capacity + 1 (n batches at most, so batch_capacity = n
+ *               always suffices); *n_batches receives the count.
+ * Returns ESM_ATTN_ERR_INVALID_ARGUMENT for a negative length, boundaries not
+ * increasing or < 1, budget < 1, padded not 0 or 1, a null pointer, or more
+ * batches than batch_capacity. */
+esm_attn_status_t esm_attn_bucket_batches(const int32_t* lengths, int32_t n,
+                                          const int32_t* boundaries, int32_t n_boundaries,
+                                          int64_t budget, int32_t padded, int32_t* order,
+                                          int32_t* batch_offsets, int32_t batch_capacity,
+                                          int32_t* n_batches);
+
 /* Host-only check of a HOST copy of cu_seqlens: cu[0] = 0, nondecreasing,
  * cu[batch] = total_tokens, every length <= max_seqlen. Returns ESM_ATTN_OK or
  * ESM_ATTN_ERR_INVALID_ARGUMENT. Reads batch+1 entries; enqueues nothing. */

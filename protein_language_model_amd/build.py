@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libesm_attn.so")
-SOURCES = ["api.hip", "prep.hip", "rope.hip", "fwd.hip", "bwd.hip"]
+SOURCES = ["api.hip", "prep.hip", "rope.hip", "fwd.hip", "bwd.hip", "batching.hip"]
 ARCH = "gfx950"
 
 

@@ -12,8 +12,9 @@ Functions keep the C names:
                rope_base) -> (dq, dk, dv)
 the planned steps (esm_attn_plan, esm_attn_rotate_planned,
 esm_attn_fwd_planned, esm_attn_bwd_planned), the workspace queries,
-esm_attn_check_cu_seqlens_host, esm_attn_schedule_host, and `attention`, an
-autograd wrapper over the planned steps.
+esm_attn_check_cu_seqlens_host, esm_attn_schedule_host, the host batch former
+esm_attn_bucket_batches, and `attention`, an autograd wrapper over the
+planned steps.
 """
 
 import ctypes
@@ -42,6 +43,7 @@ EXPORTED = (
     "esm_attn_bwd_planned",
     "esm_attn_check_cu_seqlens_host",
     "esm_attn_schedule_host",
+    "esm_attn_bucket_batches",
 )
 
 PASS_DQ, PASS_DKV = 1, 2
@@ -101,6 +103,9 @@ def lib():
     L.esm_attn_check_cu_seqlens_host.argtypes = [vp, i32, i32, i32]
     L.esm_attn_schedule_host.restype = i32
     L.esm_attn_schedule_host.argtypes = [vp, i32, i32, i32, i32, i32, vp, i32, vp]
+    L.esm_attn_bucket_batches.restype = i32
+    L.esm_attn_bucket_batches.argtypes = [vp, i32, vp, i32, ctypes.c_int64, i32, vp, vp, i32,
+                                          vp]
     if len(_hip_runtimes()) > 1:
         raise EsmAttnError(ERR_HIP, "two HIP runtimes are mapped: %s" % _hip_runtimes())
     _lib = L
@@ -332,6 +337,23 @@ def esm_attn_schedule_host(cu, total_tokens, max_seqlen, num_heads, block_rows=1
                                         int(block_rows), items.ctypes.data_as(ctypes.c_void_p),
                                         int(capacity), ctypes.byref(n)))
     return items[: n.value].copy()
+
+
+def esm_attn_bucket_batches(lengths, boundaries, budget, padded=False):
+    """Size-aware bucket batching on the host (see the C header): returns a
+    list of int32 index arrays into `lengths`, one per batch, bucket by
+    bucket."""
+    ln = np.ascontiguousarray(lengths, dtype=np.int32)
+    bd = np.ascontiguousarray(boundaries, dtype=np.int32)
+    n = ln.size
+    order = np.zeros(max(n, 1), dtype=np.int32)
+    offsets = np.zeros(n + 1, dtype=np.int32)
+    nb = ctypes.c_int32(0)
+    vp = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    _check(lib().esm_attn_bucket_batches(vp(ln), n, vp(bd) if bd.size else None, bd.size,
+                                         int(budget), int(bool(padded)), vp(order),
+                                         vp(offsets), n, ctypes.byref(nb)))
+    return [order[offsets[b]:offsets[b + 1]].copy() for b in range(nb.value)]
 
 
 class _Attention(torch.autograd.Function):
