@@ -1,5 +1,6 @@
 """CPU oracle for bidirectional varlen multi-head attention with rotary
-position embedding, forward and backward, in float64.
+position embedding, forward and backward, in float64; key-range partials and
+their merge; size-aware bucket batching (batching.py).
 
 TEST INFRASTRUCTURE. Only the test-suite, the smoke check and the benchmark's
 CPU-baseline leg may import this package. The product path (the HIP library
@@ -17,6 +18,8 @@ from .attention import (  # noqa: F401
     rope_rotate,
     rope_rotate_f32,
     attention_forward_slice,
+    attention_forward_partial_slice,
+    merge_partials,
     attention_backward_slice,
     forward,
     backward,

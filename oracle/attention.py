@@ -181,6 +181,50 @@ def attention_forward_slice(q, k, v, scale, base, mode="bf16_operands"):
     return P @ v, lse
 
 
+def attention_forward_partial_slice(q, k, v, scale, base, key_lo, key_hi,
+                                    mode="bf16_operands"):
+    """Attention of every query of one sequence and head against only the
+    keys key_lo .. key_hi-1 (rotary positions those of the whole sequence):
+    a key-range partial, the unit of work that context parallelism deals out
+    when one sequence's keys are split across devices ("Scaling biomolecular
+    modeling with context parallelism in NVIDIA BioNeMo" page, "2D tiling of
+    the pairwise representation": each device owns a sub-block of the N x N
+    interactions).
+
+    Returns O_r [L, d] = sum_{j in range} P^r_ij v_j with P^r the softmax over
+    the range, and LSE_r [L] = log sum_{j in range} exp(S_ij); an empty
+    range gives O_r = 0 and LSE_r = -inf."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    L = q.shape[0]
+    if L == 0 or key_hi <= key_lo:
+        return np.zeros((L, v.shape[1])), np.full((L,), -np.inf)
+    _, qr, kr = _rotated_operands(q, k, base, mode)
+    S = float(scale) * (qr @ kr[key_lo:key_hi].T)
+    m = S.max(axis=1)
+    lse = m + np.log(np.exp(S - m[:, None]).sum(axis=1))
+    P = np.exp(S - lse[:, None])
+    return P @ v[key_lo:key_hi], lse
+
+
+def merge_partials(o_parts, lse_parts):
+    """Combines key-range partials of the same queries: with
+    LSE = log sum_r exp(LSE_r), the softmax over the union of the ranges is
+    exp(S_ij - LSE) = exp(LSE_r - LSE) P^r_ij, hence
+    O = sum_r exp(LSE_r - LSE) O_r. Parts with LSE_r = -inf add nothing.
+    o_parts [R, L, d], lse_parts [R, L] -> (O [L, d], LSE [L])."""
+    o_parts = np.asarray(o_parts, np.float64)
+    lse_parts = np.asarray(lse_parts, np.float64)
+    m = lse_parts.max(axis=0)
+    safe = np.where(np.isfinite(m), m, 0.0)
+    w = np.exp(lse_parts - safe[None, :])
+    tot = w.sum(axis=0)
+    lse = np.where(tot > 0, safe + np.log(np.where(tot > 0, tot, 1.0)), -np.inf)
+    o = (w[:, :, None] * o_parts).sum(axis=0) / np.where(tot > 0, tot, 1.0)[:, None]
+    return o, lse
+
+
 def attention_backward_slice(q, k, v, do, scale, base, mode="bf16_operands",
                              return_intermediates=False):
     """Gradients of sum(dO * O) for one sequence and one head.
