@@ -32,6 +32,12 @@ and wasted attention work, and times this path (plan, rotation, forward,
 backward; H = 20, d = 64) over all of each way's batches (one epoch), padded
 batches run with every sequence at its batch's longest length. Prints one
 JSON line.
+
+`--split-kv` times the forward plain and split into n_split key-range
+partials plus their merge (esm_attn_fwd_split_planned) on shapes with few
+work items: one 8,192-token sequence with 5 heads of 128 (the local heads of
+a sequence-parallel shard of the 15B shape), two 4,096-token sequences with 8
+heads of 64, and the 16 x 1,024 650M batch. Prints one JSON line.
 """
 
 import argparse
@@ -61,6 +67,8 @@ def parse():
                    help="time QKV projection + attention + output projection, fwd + bwd")
     p.add_argument("--packing-study", action="store_true",
                    help="padded vs packed batches of a length mix: padding, waste, tokens/s")
+    p.add_argument("--split-kv", action="store_true",
+                   help="forward plain vs split into key-range partials + merge")
     return p.parse_args()
 
 
@@ -346,6 +354,66 @@ def packing_study(args):
     print(json.dumps(out), flush=True)
 
 
+def split_kv_study(args):
+    """Plain vs split-KV forward on few-item shapes (see the module doc)."""
+    import torch
+    from protein_language_model_amd import esm_attn as E
+    from protein_language_model_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    shapes = [("1 x 8192, H=5, d=128", [8192], 5, 128),
+              ("2 x 4096, H=8, d=64", [4096, 4096], 8, 64),
+              ("16 x 1024, H=20, d=64", [1024] * 16, 20, 64)]
+    g = torch.Generator(device=dev).manual_seed(3)
+    st = torch.cuda.current_stream()
+    res = {}
+    for name, lengths, H, d in shapes:
+        T, B, maxL = sum(lengths), len(lengths), max(lengths)
+        q, k, v = (torch.randn(T, H, d, generator=g, device=dev).to(torch.bfloat16)
+                   for _ in range(3))
+        cu = torch.from_numpy(W.cu_from_lengths(lengths)).to(dev)
+        plan = E.esm_attn_plan(cu, T, maxL, H, d, W.ROPE_BASE)
+        qr, kr = E.esm_attn_rotate_planned(q, k, B, maxL, plan, W.ROPE_BASE)
+        o = torch.empty_like(q)
+        lse = torch.empty((H, T), dtype=torch.float32, device=dev)
+        parts = {R: (torch.empty((R, T, H, d), dtype=torch.float32, device=dev),
+                     torch.empty((R, H, T), dtype=torch.float32, device=dev))
+                 for R in (2, 3, 4, 6, 8)}
+
+        def timed(fn, n=20):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(n)]
+            for e0, e1 in evs:
+                e0.record(st)
+                fn()
+                e1.record(st)
+            torch.cuda.synchronize()
+            return float(np.median([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs]))
+
+        plain = timed(lambda: E.esm_attn_fwd_planned(qr, kr, v, B, maxL, plan, out=o, lse=lse))
+        split = {R: timed(lambda R=R: E.esm_attn_fwd_split_planned(
+            qr, kr, v, B, maxL, plan, R, out=o, lse=lse, o_part=parts[R][0],
+            lse_part=parts[R][1])) for R in parts}
+        best = min(split, key=split.get)
+        fwd_f, _ = W.counted_flops(lengths, H, d)
+        items = H * sum(-(-L // 128) for L in lengths)
+        res[name] = {"items": items, "plain_us": round(plain, 1),
+                     "split_us": {str(R): round(t, 1) for R, t in split.items()},
+                     "best_n_split": best, "speedup": round(plain / split[best], 3),
+                     "plain_tflops": round(fwd_f / plain * 1e-6, 1),
+                     "best_split_tflops": round(fwd_f / split[best] * 1e-6, 1)}
+    first = res[shapes[0][0]]
+    out = {"metric": "forward TFLOP/s, plain vs split-KV (key-range partials + merge)",
+           "value": first["best_split_tflops"], "unit": "TFLOP/s", "n_gpus": 1,
+           "higher_is_better": True, "dtype": "bf16",
+           "data": "synthetic (seeded normal bf16 activations)",
+           "config": {"workload": shapes[0][0]}, "shapes": res}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -361,6 +429,9 @@ def main():
         return
     if args.packing_study:
         packing_study(args)
+        return
+    if args.split_kv:
+        split_kv_study(args)
         return
 
     import torch

@@ -197,6 +197,43 @@ esm_attn_status_t esm_attn_fwd_planned(
     uint16_t* o, float* lse,
     const void* plan, size_t plan_bytes, void* stream);
 
+/* Split-KV forward: the same result as esm_attn_fwd_planned (to fp32
+ * rounding; bitwise equal for n_split = 1) computed as n_split key-range
+ * partials per work item and their merge. Each sequence's key blocks are
+ * dealt out in n_split contiguous chunks of ceil(blocks / n_split); chunk r of
+ * every item is one more workgroup, which fills the chip when a batch has few
+ * (sequence, head, query-block) items (few long sequences, few heads: e.g.
+ * the local heads of a sequence-parallel shard). Key-range partials and their
+ * merge are the per-device half of attention with keys sharded over devices
+ * ("Scaling biomolecular modeling with context parallelism in NVIDIA BioNeMo"
+ * page, "2D tiling of the pairwise representation").
+ *   o_part   : fp32 [n_split][T][H][d], caller-owned scratch; chunk outputs,
+ *              each normalised over its own keys (0 for an empty chunk)
+ *   lse_part : fp32 [n_split][H][T], chunk LSEs (-inf for an empty chunk)
+ *   o, lse   : as esm_attn_fwd_planned.
+ * 1 <= n_split <= 64, else ESM_ATTN_ERR_INVALID_ARGUMENT. */
+esm_attn_status_t esm_attn_fwd_split_planned(
+    const uint16_t* q_rot, const uint16_t* k_rot, const uint16_t* v,
+    int32_t qkv_row_stride,
+    int32_t batch, int32_t total_tokens, int32_t max_seqlen,
+    int32_t num_heads, int32_t head_dim, float softmax_scale,
+    int32_t n_split, float* o_part, float* lse_part,
+    uint16_t* o, float* lse,
+    const void* plan, size_t plan_bytes, void* stream);
+
+/* Merge of n_parts attention partials of the same queries over disjoint key
+ * sets (fp32 o_part [n_parts][T][H][d], lse_part [n_parts][H][T], as the split
+ * forward writes them, or as received from other devices):
+ *   LSE = log sum_r exp(LSE_r),  O = sum_r exp(LSE_r - LSE) O_r,
+ * computed in fp32 (relative to the largest LSE_r); parts with LSE_r = -inf
+ * add nothing; rows whose parts are all -inf get O = 0, LSE = -inf. Writes
+ * o (bf16 [T][H][d], round to nearest even) and lse (fp32 [H][T]). Needs no
+ * plan. 1 <= n_parts <= 64. */
+esm_attn_status_t esm_attn_merge_partials(
+    const float* o_part, const float* lse_part, int32_t n_parts,
+    int32_t total_tokens, int32_t num_heads, int32_t head_dim,
+    uint16_t* o, float* lse, void* stream);
+
 /* Backward on rotated operands (q_rot, k_rot, v and their stride as for the
  * forward; o and d_o packed [T][H][d]); dq and dk are still the gradients
  * with respect to the pre-rotation q and k: the kernels apply R(p)^T, for

@@ -20,7 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libesm_attn.so")
-SOURCES = ["api.hip", "prep.hip", "rope.hip", "fwd.hip", "bwd.hip", "batching.hip"]
+SOURCES = ["api.hip", "prep.hip", "rope.hip", "fwd.hip", "bwd.hip", "batching.hip",
+           "merge.hip"]
 ARCH = "gfx950"
 
 

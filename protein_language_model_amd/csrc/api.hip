@@ -14,6 +14,7 @@ namespace {
 using namespace esm;
 
 constexpr size_t kAlign = 256;
+constexpr int32_t kMaxSplit = 64;  // key chunks / partials per merge
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
@@ -230,7 +231,72 @@ esm_attn_status_t esm_attn_fwd_planned(const uint16_t* q_rot, const uint16_t* k_
   a.items = reinterpret_cast<const Item*>(ws + l.items);
   a.ld_qkv = qkv_row_stride;
   fill_common(&a, total_tokens, num_heads, softmax_scale);
-  if (launch_fwd(head_dim, a, l.n_slots, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+  if (launch_fwd(head_dim, a, l.n_slots, false, reinterpret_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return ESM_ATTN_ERR_HIP;
+  return ESM_ATTN_OK;
+}
+
+esm_attn_status_t esm_attn_fwd_split_planned(const uint16_t* q_rot, const uint16_t* k_rot,
+                                             const uint16_t* v, int32_t qkv_row_stride,
+                                             int32_t batch, int32_t total_tokens,
+                                             int32_t max_seqlen, int32_t num_heads,
+                                             int32_t head_dim, float softmax_scale,
+                                             int32_t n_split, float* o_part, float* lse_part,
+                                             uint16_t* o, float* lse, const void* plan,
+                                             size_t plan_bytes, void* stream) {
+  esm_attn_status_t s = check_sizes(batch, total_tokens, max_seqlen, num_heads, head_dim);
+  if (s != ESM_ATTN_OK) return s;
+  if ((s = check_scalars(softmax_scale, 0.f)) != ESM_ATTN_OK) return s;
+  if ((s = check_stride(qkv_row_stride, total_tokens, num_heads, head_dim)) != ESM_ATTN_OK)
+    return s;
+  if (n_split < 1 || n_split > kMaxSplit) return ESM_ATTN_ERR_INVALID_ARGUMENT;
+  if (total_tokens == 0) return ESM_ATTN_OK;
+  const void* ptrs[] = {q_rot, k_rot, v, o_part, lse_part, o, lse, plan};
+  for (const void* p : ptrs)
+    if (p == nullptr || !aligned16(p)) return ESM_ATTN_ERR_INVALID_ARGUMENT;
+  const Layout l = make_layout(batch, total_tokens, max_seqlen, num_heads, head_dim, false);
+  if (plan_bytes < l.plan) return ESM_ATTN_ERR_WORKSPACE_TOO_SMALL;
+  if (max_seqlen == 0) return ESM_ATTN_OK;
+  const char* ws = static_cast<const char*>(plan);
+  AttnArgs a = {};
+  a.q = q_rot;
+  a.k = k_rot;
+  a.v = v;
+  a.items = reinterpret_cast<const Item*>(ws + l.items);
+  a.ld_qkv = qkv_row_stride;
+  a.n_split = n_split;
+  a.o_part = o_part;
+  a.lse_part = lse_part;
+  a.n_items = (int32_t)l.n_slots;
+  fill_common(&a, total_tokens, num_heads, softmax_scale);
+  // grid x extent = slots padded to B*H modulo 8: chunk y of group g then
+  // runs on XCD (g + y*B*H) mod 8 under round-robin dispatch
+  const int64_t groups8 = ((int64_t)batch * num_heads) % 8;
+  const int64_t grid_x = l.n_slots + ((groups8 - l.n_slots % 8) + 8) % 8;
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (launch_fwd(head_dim, a, grid_x, true, st) != hipSuccess) return ESM_ATTN_ERR_HIP;
+  if (launch_merge(head_dim, o_part, lse_part, n_split, total_tokens, num_heads, o, lse, st) !=
+      hipSuccess)
+    return ESM_ATTN_ERR_HIP;
+  return ESM_ATTN_OK;
+}
+
+esm_attn_status_t esm_attn_merge_partials(const float* o_part, const float* lse_part,
+                                          int32_t n_parts, int32_t total_tokens,
+                                          int32_t num_heads, int32_t head_dim, uint16_t* o,
+                                          float* lse, void* stream) {
+  if (n_parts < 1 || n_parts > kMaxSplit || total_tokens < 0 || num_heads < 1)
+    return ESM_ATTN_ERR_INVALID_ARGUMENT;
+  if (!head_dim_ok(head_dim)) return ESM_ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)total_tokens * num_heads * head_dim >= ((int64_t)1 << 31))
+    return ESM_ATTN_ERR_UNSUPPORTED;
+  if (total_tokens == 0) return ESM_ATTN_OK;
+  const void* ptrs[] = {o_part, lse_part, o, lse};
+  for (const void* p : ptrs)
+    if (p == nullptr || !aligned16(p)) return ESM_ATTN_ERR_INVALID_ARGUMENT;
+  if (launch_merge(head_dim, o_part, lse_part, n_parts, total_tokens, num_heads, o, lse,
+                   reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
     return ESM_ATTN_ERR_HIP;
   return ESM_ATTN_OK;
 }

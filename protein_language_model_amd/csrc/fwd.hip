@@ -54,11 +54,23 @@ struct FwdCfg {
 
 constexpr float kLazyBound = 65536.0f;  // 2^16: largest block sum of P kept
 
-template <int D>
+// SPLIT: key-range partials. Workgroup (x, y) attends the queries of item x
+// to key chunk y of its sequence (the sequence's key blocks dealt out in
+// n_split contiguous runs of ceil(blocks / n_split)) and writes the chunk's
+// own normalised O_y (fp32) and LSE_y; an empty chunk writes 0 and -inf.
+// merge_kernel then combines the chunks (split-KV: more work items when a
+// batch has too few for the chip, and the per-device half of attention
+// with keys sharded over devices). The grid's x extent is padded to
+// B*H modulo 8 (padding workgroups exit), so that under round-robin
+// dispatch chunk y of (sequence, head) group g runs on XCD (g + y*B*H) mod 8:
+// few groups still spread over all eight XCDs, and each chunk's keys stay in
+// one XCD's L2.
+template <int D, bool SPLIT>
 __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(AttnArgs a) {
   using C = FwdCfg<D>;
   __shared__ __attribute__((aligned(1024))) uint16_t lds[C::LDS];
 
+  if (SPLIT && (int)blockIdx.x >= a.n_items) return;  // grid padding
   const Item it = a.items[blockIdx.x];
   if (it.len <= 0) return;
   const int L = it.len, h = it.head, q0 = it.blk * C::BM;
@@ -68,8 +80,26 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(AttnArgs a) {
   const int rs = a.ld_qkv;  // row stride of q~, k~, v; T * rs < 2^31 is checked on the host
   const int64_t base = (int64_t)it.seq0 * rs + (int64_t)h * D;
   const uint16_t* __restrict__ Qg = a.q + base;
-  const uint16_t* __restrict__ Kg = a.k + base;
-  const uint16_t* __restrict__ Vg = a.v + base;
+  // keys kbase .. kbase + Lk - 1 of the sequence (all of them unless SPLIT)
+  int kbase = 0, Lk = L;
+  if (SPLIT) {
+    const int per = (((L + C::BN - 1) / C::BN) + a.n_split - 1) / a.n_split;  // blocks per chunk
+    kbase = min((int)blockIdx.y * per * C::BN, L);
+    Lk = min(per * C::BN, L - kbase);
+  }
+  const uint16_t* __restrict__ Kg = a.k + base + (int64_t)kbase * rs;
+  const uint16_t* __restrict__ Vg = a.v + base + (int64_t)kbase * rs;
+  const int qi = q0 + w * 32 + r;  // this lane's query
+  if (SPLIT && Lk <= 0) {  // empty chunk: O_y = 0, LSE_y = -inf
+    if (qi < L) {
+      float* Op = a.o_part + (((int64_t)blockIdx.y * a.T + it.seq0 + qi) * a.H + h) * D;
+      for (int d0 = 16 * g; d0 < D; d0 += 32)
+#pragma unroll
+        for (int e = 0; e < 16; e += 4) *reinterpret_cast<f32x4*>(Op + d0 + e) = f32x4{};
+      if (g == 0) a.lse_part[((int64_t)blockIdx.y * a.H + h) * a.T + it.seq0 + qi] = -INFINITY;
+    }
+    return;
+  }
 
   // k~ and v rows of key block kb -> LDS stage `stage` (offsets kept in
   // registers for blocks with every key present)
@@ -78,19 +108,18 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(AttnArgs a) {
   auto issue = [&](int kb, int stage) {
     const int k0 = kb * C::BN;
     uint16_t* Ks = lds + stage * C::STAGE;
-    if (k0 + C::BN <= L)
+    if (k0 + C::BN <= Lk)
       loader.load_full(Kg + (int64_t)k0 * rs, Vg + (int64_t)k0 * rs, koff, Ks, Ks + C::TILE, w);
     else
-      loader.template load<1>(Kg + (int64_t)k0 * rs, rs, Vg + (int64_t)k0 * rs, rs, L - k0, Ks,
+      loader.template load<1>(Kg + (int64_t)k0 * rs, rs, Vg + (int64_t)k0 * rs, rs, Lk - k0, Ks,
                               Ks + C::TILE, w);
   };
-  const int nkb = (L + C::BN - 1) / C::BN;
+  const int nkb = (Lk + C::BN - 1) / C::BN;
   issue(0, 0);
 
   // queries: B operands (8 d values per k-step); rows past the end are zero.
   // A negative softmax scale is applied as a sign flip of q~ (exact), so that
   // scores use |scale|.
-  const int qi = q0 + w * 32 + r;
   const uint32_t qflip = a.q_sign < 0.f ? 0x80008000u : 0u;
   u32x4 qreg[C::NS];
 #pragma unroll
@@ -139,7 +168,7 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(AttnArgs a) {
 
     // S^T tiles: lane (q = r, g) register i of tile t = key 32t + 16g + i.
     // Keys past the end of the sequence get S = -inf, so P = 0.
-    const int lim = L - kb * C::BN;  // valid keys in this block
+    const int lim = Lk - kb * C::BN;  // valid keys in this block
     f32x16 sacc[C::NT];
     auto scores = [&]() {
 #pragma unroll
@@ -214,12 +243,33 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(AttnArgs a) {
       for (int u = 0; u < C::NU; ++u) oacc[dt] = mfma32(av[u], preg[u], oacc[dt]);
     }
   };
-  const int nfull = L / C::BN;
+  const int nfull = Lk / C::BN;
   for (int kb = 0; kb < nfull; ++kb) block(kb, Full{});
   if (nfull < nkb) block(nfull, Ragged{});
 
   // ---- epilogue
   l += xor32(l);
+  if (SPLIT) {  // the chunk's O_y (fp32) and LSE_y
+    if (qi < L) {
+      const float inv = 1.0f / l;
+      float* Op = a.o_part + (((int64_t)blockIdx.y * a.T + it.seq0 + qi) * a.H + h) * D;
+#pragma unroll
+      for (int dt = 0; dt < C::ND; ++dt) {
+        const int d0 = 32 * dt + 16 * g;
+        if (d0 < D) {
+#pragma unroll
+          for (int e = 0; e < 16; e += 4)
+            *reinterpret_cast<f32x4*>(Op + d0 + e) =
+                f32x4{oacc[dt][e] * inv, oacc[dt][e + 1] * inv, oacc[dt][e + 2] * inv,
+                      oacc[dt][e + 3] * inv};
+        }
+      }
+      if (g == 0)
+        a.lse_part[((int64_t)blockIdx.y * a.H + h) * a.T + it.seq0 + qi] =
+            (mc + __log2f(l)) * kLn2;
+    }
+    return;
+  }
   if (qi < L) {
     const float inv = 1.0f / l;
     const int rso = a.H * D;
@@ -239,13 +289,23 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(AttnArgs a) {
   }
 }
 
-hipError_t launch_fwd(int head_dim, const AttnArgs& a, int64_t n_slots, hipStream_t stream) {
+template <int D>
+static void launch_fwd_d(const AttnArgs& a, unsigned n, int n_split, hipStream_t stream) {
+  if (n_split > 0)
+    fwd_kernel<D, true><<<dim3(n, (unsigned)n_split), 256, 0, stream>>>(a);
+  else
+    fwd_kernel<D, false><<<n, 256, 0, stream>>>(a);
+}
+
+hipError_t launch_fwd(int head_dim, const AttnArgs& a, int64_t n_slots, bool split,
+                      hipStream_t stream) {
   const unsigned n = (unsigned)n_slots;
+  const int ns = split ? a.n_split : 0;
   switch (head_dim) {
-    case 16: fwd_kernel<16><<<n, 256, 0, stream>>>(a); break;
-    case 32: fwd_kernel<32><<<n, 256, 0, stream>>>(a); break;
-    case 64: fwd_kernel<64><<<n, 256, 0, stream>>>(a); break;
-    case 128: fwd_kernel<128><<<n, 256, 0, stream>>>(a); break;
+    case 16: launch_fwd_d<16>(a, n, ns, stream); break;
+    case 32: launch_fwd_d<32>(a, n, ns, stream); break;
+    case 64: launch_fwd_d<64>(a, n, ns, stream); break;
+    case 128: launch_fwd_d<128>(a, n, ns, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -62,9 +62,20 @@ struct AttnArgs {
   float scale_abs;
   int32_t ld_qkv;       // elements between consecutive tokens' rows of q~, k~, v
   int32_t ld_grad;      // ... of dq, dk, dv (o, dO: H * d)
+  int32_t n_items;      // split forward: slots with an item record (the grid may be wider)
+  int32_t n_split;      // split forward: key chunks per sequence
+  float* o_part;        // split forward: [n_split][T][H][d] chunk outputs
+  float* lse_part;      // split forward: [n_split][H][T] chunk LSEs
 };
 
-hipError_t launch_fwd(int head_dim, const AttnArgs& a, int64_t n_slots, hipStream_t stream);
+hipError_t launch_fwd(int head_dim, const AttnArgs& a, int64_t n_slots, bool split,
+                      hipStream_t stream);
+
+// O = sum_r exp(LSE_r - LSE) O_r, LSE = log sum_r exp(LSE_r) over n_parts
+// partials o_part [n_parts][T][H][d] (fp32), lse_part [n_parts][H][T];
+// writes o (bf16, [T][H][d]) and lse ([H][T]).
+hipError_t launch_merge(int head_dim, const float* o_part, const float* lse_part, int n_parts,
+                        int T, int H, uint16_t* o, float* lse, hipStream_t stream);
 hipError_t launch_bwd(int head_dim, bool rope, const AttnArgs& a, int64_t n_slots, bool dq_pass,
                       bool dkv_pass, hipStream_t stream);
 

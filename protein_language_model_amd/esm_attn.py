@@ -44,6 +44,8 @@ EXPORTED = (
     "esm_attn_check_cu_seqlens_host",
     "esm_attn_schedule_host",
     "esm_attn_bucket_batches",
+    "esm_attn_fwd_split_planned",
+    "esm_attn_merge_partials",
 )
 
 PASS_DQ, PASS_DKV = 1, 2
@@ -103,6 +105,11 @@ def lib():
     L.esm_attn_check_cu_seqlens_host.argtypes = [vp, i32, i32, i32]
     L.esm_attn_schedule_host.restype = i32
     L.esm_attn_schedule_host.argtypes = [vp, i32, i32, i32, i32, i32, vp, i32, vp]
+    L.esm_attn_fwd_split_planned.restype = i32
+    L.esm_attn_fwd_split_planned.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32,
+                                             vp, vp, vp, vp, vp, u64, vp]
+    L.esm_attn_merge_partials.restype = i32
+    L.esm_attn_merge_partials.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp]
     L.esm_attn_bucket_batches.restype = i32
     L.esm_attn_bucket_batches.argtypes = [vp, i32, vp, i32, ctypes.c_int64, i32, vp, vp, i32,
                                           vp]
@@ -281,6 +288,58 @@ def esm_attn_fwd_planned(q_rot, k_rot, v, batch, max_seqlen, plan, softmax_scale
     _check(lib().esm_attn_fwd_planned(_ptr(q_rot), _ptr(k_rot), _ptr(v), ld, int(batch), T,
                                       int(max_seqlen), H, d, scale, _ptr(out), _ptr(lse),
                                       _ptr(plan), plan.numel(), _stream(stream)))
+    return out, lse
+
+
+def esm_attn_fwd_split_planned(q_rot, k_rot, v, batch, max_seqlen, plan, n_split,
+                               softmax_scale=None, out=None, lse=None, o_part=None,
+                               lse_part=None, stream=None):
+    """Split-KV forward: n_split key-range partials per work item, then their
+    merge. Returns (o, lse, o_part, lse_part); o_part fp32 [n_split, T, H, d]
+    and lse_part fp32 [n_split, H, T] hold the chunk partials."""
+    T, H, d = v.shape
+    ld = _row_stride(q_rot, k_rot, v)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    dev = v.device
+    if out is None:
+        out = torch.empty((T, H, d), dtype=v.dtype, device=dev)
+    _check_packed((T, H, d), out)
+    if lse is None:
+        lse = torch.empty((H, T), dtype=torch.float32, device=dev)
+    if o_part is None:
+        o_part = torch.empty((n_split, T, H, d), dtype=torch.float32, device=dev)
+    if lse_part is None:
+        lse_part = torch.empty((n_split, H, T), dtype=torch.float32, device=dev)
+    _check_partials(o_part, lse_part, n_split, T, H, d)
+    _check(lib().esm_attn_fwd_split_planned(_ptr(q_rot), _ptr(k_rot), _ptr(v), ld, int(batch), T,
+                                            int(max_seqlen), H, d, scale, int(n_split),
+                                            _ptr(o_part), _ptr(lse_part), _ptr(out), _ptr(lse),
+                                            _ptr(plan), plan.numel(), _stream(stream)))
+    return out, lse, o_part, lse_part
+
+
+def _check_partials(o_part, lse_part, R, T, H, d):
+    if (o_part.dtype != torch.float32 or tuple(o_part.shape) != (R, T, H, d)
+            or not o_part.is_contiguous()):
+        raise ValueError("o_part must be contiguous fp32 [R, T, H, d]")
+    if (lse_part.dtype != torch.float32 or tuple(lse_part.shape) != (R, H, T)
+            or not lse_part.is_contiguous()):
+        raise ValueError("lse_part must be contiguous fp32 [R, H, T]")
+
+
+def esm_attn_merge_partials(o_part, lse_part, out=None, lse=None, stream=None):
+    """O = sum_r exp(LSE_r - LSE) O_r, LSE = log sum_r exp(LSE_r) over the
+    partials o_part fp32 [R, T, H, d], lse_part fp32 [R, H, T]; returns
+    (o bf16 [T, H, d], lse fp32 [H, T])."""
+    R, T, H, d = o_part.shape
+    _check_partials(o_part, lse_part, R, T, H, d)
+    if out is None:
+        out = torch.empty((T, H, d), dtype=torch.bfloat16, device=o_part.device)
+    _check_packed((T, H, d), out)
+    if lse is None:
+        lse = torch.empty((H, T), dtype=torch.float32, device=o_part.device)
+    _check(lib().esm_attn_merge_partials(_ptr(o_part), _ptr(lse_part), R, T, H, d, _ptr(out),
+                                         _ptr(lse), _stream(stream)))
     return out, lse
 
 

@@ -171,6 +171,25 @@ def test_in_place_rotation_rules():
                                      None) == E.ERR_WORKSPACE_TOO_SMALL
 
 
+def test_split_forward_and_merge_validation():
+    """Host checks of the split forward and the merge (fake device pointers:
+    a launch would fault, so every case must be rejected on the host)."""
+    L = E.lib()
+    p, q, T = 1 << 12, 1 << 13, 8
+    args = lambda ns, plan_bytes: (p, p, p, 32, 1, T, T, 2, 16, 0.1, ns, q, q, q, q, p,
+                                   plan_bytes, None)
+    assert L.esm_attn_fwd_split_planned(*args(0, 1 << 30)) == E.ERR_INVALID_ARGUMENT
+    assert L.esm_attn_fwd_split_planned(*args(65, 1 << 30)) == E.ERR_INVALID_ARGUMENT
+    assert L.esm_attn_fwd_split_planned(*args(4, 4)) == E.ERR_WORKSPACE_TOO_SMALL
+    assert L.esm_attn_fwd_split_planned(p, p, p, 32, 1, T, T, 2, 16, float("inf"), 2, q, q, q,
+                                        q, p, 1 << 30, None) == E.ERR_INVALID_ARGUMENT
+    assert L.esm_attn_merge_partials(q, q, 0, T, 2, 16, q, q, None) == E.ERR_INVALID_ARGUMENT
+    assert L.esm_attn_merge_partials(q, q, 2, T, 2, 48, q, q, None) == E.ERR_UNSUPPORTED
+    assert L.esm_attn_merge_partials(q, None, 2, T, 2, 16, q, q, None) == E.ERR_INVALID_ARGUMENT
+    assert L.esm_attn_merge_partials(q + 4, q, 2, T, 2, 16, q, q, None) == E.ERR_INVALID_ARGUMENT
+    assert L.esm_attn_merge_partials(None, None, 2, 0, 2, 16, None, None, None) == E.OK
+
+
 def test_check_cu_seqlens_host():
     ok = np.array([0, 3, 3, 10], np.int32)
     assert E.esm_attn_check_cu_seqlens_host(ok, 10, 7) == E.OK
