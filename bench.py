@@ -38,6 +38,10 @@ partials plus their merge (esm_attn_fwd_split_planned) on shapes with few
 work items: one 8,192-token sequence with 5 heads of 128 (the local heads of
 a sequence-parallel shard of the 15B shape), two 4,096-token sequences with 8
 heads of 64, and the 16 x 1,024 650M batch. Prints one JSON line.
+
+`--fp8` times the E4M3 forward (quantization of the rotated q, k + the FP8
+forward) against the bf16 forward (rotation + forward) on the 650M and 15B
+batches. Prints one JSON line.
 """
 
 import argparse
@@ -69,6 +73,8 @@ def parse():
                    help="padded vs packed batches of a length mix: padding, waste, tokens/s")
     p.add_argument("--split-kv", action="store_true",
                    help="forward plain vs split into key-range partials + merge")
+    p.add_argument("--fp8", action="store_true",
+                   help="E4M3 forward vs bf16 forward (inference)")
     return p.parse_args()
 
 
@@ -414,6 +420,77 @@ def split_kv_study(args):
     print(json.dumps(out), flush=True)
 
 
+def fp8_study(args):
+    """E4M3 vs bf16 forward (see the module doc)."""
+    import torch
+    from protein_language_model_amd import esm_attn as E
+    from protein_language_model_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    st = torch.cuda.current_stream()
+    res = {}
+    for name in ("esm2_650m", "esm2_15b"):
+        wl = W.WORKLOADS[name]
+        lengths = W.lengths_of(name)
+        H, d = wl.num_heads, wl.head_dim
+        T, B, maxL = sum(lengths), len(lengths), max(lengths)
+        g = torch.Generator(device=dev).manual_seed(11)
+        q, k, v = (torch.randn(T, H, d, generator=g, device=dev).to(torch.bfloat16)
+                   for _ in range(3))
+        cu = torch.from_numpy(W.cu_from_lengths(lengths)).to(dev)
+        plan = E.esm_attn_plan(cu, T, maxL, H, d, W.ROPE_BASE)
+        qs = float(q.abs().max()) * math.sqrt(2) / 448
+        ks = float(k.abs().max()) * math.sqrt(2) / 448
+        qr, kr = torch.empty_like(q), torch.empty_like(k)
+        q8 = torch.empty((T, H, d), dtype=torch.uint8, device=dev)
+        k8 = torch.empty_like(q8)
+        o = torch.empty_like(q)
+        lse = torch.empty((H, T), dtype=torch.float32, device=dev)
+
+        def timed(fn, n=20):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+            for e in ev:
+                e[0].record(st)
+                fn(e[1])
+                e[2].record(st)
+            torch.cuda.synchronize()
+            prep = float(np.median([e[0].elapsed_time(e[1]) * 1e3 for e in ev]))
+            attn = float(np.median([e[1].elapsed_time(e[2]) * 1e3 for e in ev]))
+            return prep, attn
+
+        def bf16(mid=None):
+            E.esm_attn_rotate_planned(q, k, B, maxL, plan, W.ROPE_BASE, q_rot=qr, k_rot=kr)
+            if mid is not None:
+                mid.record(st)
+            E.esm_attn_fwd_planned(qr, kr, v, B, maxL, plan, out=o, lse=lse)
+
+        def fp8(mid=None):
+            E.esm_attn_quantize_fp8_planned(q, k, B, maxL, plan, qs, ks, W.ROPE_BASE, q8=q8,
+                                            k8=k8)
+            if mid is not None:
+                mid.record(st)
+            E.esm_attn_fwd_fp8_planned(q8, k8, v, B, maxL, plan, qs, ks, out=o, lse=lse)
+
+        pb, ab = timed(bf16)
+        p8, a8 = timed(fp8)
+        fwd_f, _ = W.counted_flops(lengths, H, d)
+        res[name] = {"bf16": {"rotate_us": round(pb, 1), "fwd_us": round(ab, 1),
+                              "fwd_tflops": round(fwd_f / ab * 1e-6, 1)},
+                     "fp8": {"quantize_us": round(p8, 1), "fwd_us": round(a8, 1),
+                             "fwd_tflops": round(fwd_f / a8 * 1e-6, 1)},
+                     "fwd_speedup": round(ab / a8, 3),
+                     "with_prep_speedup": round((pb + ab) / (p8 + a8), 3)}
+    out = {"metric": "forward TFLOP/s, E4M3 scores vs bf16", "unit": "TFLOP/s",
+           "value": res["esm2_650m"]["fp8"]["fwd_tflops"], "n_gpus": 1,
+           "higher_is_better": True, "dtype": "fp8 e4m3 (scores) / bf16 (P V)",
+           "data": "synthetic (seeded normal bf16 activations)",
+           "config": {"workload": "esm2_650m and esm2_15b batches"}, "workloads": res}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -432,6 +509,9 @@ def main():
         return
     if args.split_kv:
         split_kv_study(args)
+        return
+    if args.fp8:
+        fp8_study(args)
         return
 
     import torch

@@ -221,6 +221,38 @@ esm_attn_status_t esm_attn_fwd_split_planned(
     uint16_t* o, float* lse,
     const void* plan, size_t plan_bytes, void* stream);
 
+/* ---- FP8 (OCP E4M3) forward, inference first ------------------------------
+ * The BioNeMo Recipes hub page lists FP8 among its training precisions
+ * (multi-precision training section). Here the scores take E4M3 operands on
+ * gfx950's 32x32x64 FP8 matrix instruction; softmax, P (bf16) and P V (bf16
+ * V) are those of the bf16 forward. head_dim 64 or 128 (else
+ * ESM_ATTN_ERR_UNSUPPORTED); q_scale, k_scale finite and > 0 with finite
+ * reciprocals (else ESM_ATTN_ERR_INVALID_ARGUMENT).
+ *
+ * Quantization: q8 = E4M3(clamp(R(p) q * fl32(1 / q_scale), +-448)), k8
+ * likewise: the rotation in float32 as esm_attn_rotate_planned (no bf16
+ * rounding in between), one float32 product, saturation at the largest E4M3
+ * value (448; E4M3 has no infinity), one rounding to nearest even. q and k
+ * read with in_row_stride; q8, k8 written packed [T][H][d] bytes. A scale of
+ * amax(|q|) * sqrt(2) / 448 avoids saturation (the rotation can grow one
+ * component of a pair by at most sqrt(2)). */
+esm_attn_status_t esm_attn_quantize_fp8_planned(
+    const uint16_t* q, const uint16_t* k, int32_t in_row_stride,
+    int32_t batch, int32_t total_tokens, int32_t max_seqlen,
+    int32_t num_heads, int32_t head_dim, float rope_base,
+    float q_scale, float k_scale, uint8_t* q8, uint8_t* k8,
+    const void* plan, size_t plan_bytes, void* stream);
+
+/* Forward on E4M3 q8, k8 (packed, from esm_attn_quantize_fp8_planned with the
+ * same scales) and bf16 v (row stride v_row_stride): S = softmax_scale *
+ * q_scale * k_scale * (q8 . k8); o and lse as esm_attn_fwd_planned. */
+esm_attn_status_t esm_attn_fwd_fp8_planned(
+    const uint8_t* q8, const uint8_t* k8, const uint16_t* v, int32_t v_row_stride,
+    int32_t batch, int32_t total_tokens, int32_t max_seqlen,
+    int32_t num_heads, int32_t head_dim, float softmax_scale,
+    float q_scale, float k_scale, uint16_t* o, float* lse,
+    const void* plan, size_t plan_bytes, void* stream);
+
 /* Merge of n_parts attention partials of the same queries over disjoint key
  * sets (fp32 o_part [n_parts][T][H][d], lse_part [n_parts][H][T], as the split
  * forward writes them, or as received from other devices):

@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libesm_attn.so")
 SOURCES = ["api.hip", "prep.hip", "rope.hip", "fwd.hip", "bwd.hip", "batching.hip",
-           "merge.hip"]
+           "merge.hip", "fwd_fp8.hip"]
 ARCH = "gfx950"
 
 

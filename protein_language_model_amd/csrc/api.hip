@@ -66,6 +66,15 @@ Layout make_layout(int32_t B, int32_t T, int32_t maxL, int32_t H, int32_t d, boo
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// E4M3 per-tensor scales: finite, positive, with finite float32 reciprocals
+// (the quantization multiplies by them).
+esm_attn_status_t check_fp8_scales(float q_scale, float k_scale) {
+  const float scales[] = {q_scale, k_scale};
+  for (float x : scales)
+    if (!(isfinite(x) && x > 0.f && isfinite(1.0f / x))) return ESM_ATTN_ERR_INVALID_ARGUMENT;
+  return ESM_ATTN_OK;
+}
+
 // A token row stride: at least H*d elements, rows 16-byte aligned, and every
 // element offset below 2^31 (the kernels address rows with 32-bit offsets).
 esm_attn_status_t check_stride(int32_t ld, int32_t T, int32_t H, int32_t d) {
@@ -277,6 +286,86 @@ esm_attn_status_t esm_attn_fwd_split_planned(const uint16_t* q_rot, const uint16
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (launch_fwd(head_dim, a, grid_x, true, st) != hipSuccess) return ESM_ATTN_ERR_HIP;
   if (launch_merge(head_dim, o_part, lse_part, n_split, total_tokens, num_heads, o, lse, st) !=
+      hipSuccess)
+    return ESM_ATTN_ERR_HIP;
+  return ESM_ATTN_OK;
+}
+
+esm_attn_status_t esm_attn_quantize_fp8_planned(const uint16_t* q, const uint16_t* k,
+                                               int32_t in_row_stride, int32_t batch,
+                                               int32_t total_tokens, int32_t max_seqlen,
+                                               int32_t num_heads, int32_t head_dim,
+                                               float rope_base, float q_scale, float k_scale,
+                                               uint8_t* q8, uint8_t* k8, const void* plan,
+                                               size_t plan_bytes, void* stream) {
+  esm_attn_status_t s = check_sizes(batch, total_tokens, max_seqlen, num_heads, head_dim);
+  if (s != ESM_ATTN_OK) return s;
+  if (head_dim != 64 && head_dim != 128) return ESM_ATTN_ERR_UNSUPPORTED;
+  if ((s = check_scalars(0.f, rope_base)) != ESM_ATTN_OK) return s;
+  if ((s = check_fp8_scales(q_scale, k_scale)) != ESM_ATTN_OK) return s;
+  const float q_inv = 1.0f / q_scale, k_inv = 1.0f / k_scale;
+  if ((s = check_stride(in_row_stride, total_tokens, num_heads, head_dim)) != ESM_ATTN_OK)
+    return s;
+  if (total_tokens == 0) return ESM_ATTN_OK;
+  const void* ptrs[] = {q, k, q8, k8, plan};
+  for (const void* p : ptrs)
+    if (p == nullptr || !aligned16(p)) return ESM_ATTN_ERR_INVALID_ARGUMENT;
+  const Layout l = make_layout(batch, total_tokens, max_seqlen, num_heads, head_dim, false);
+  if (plan_bytes < l.plan) return ESM_ATTN_ERR_WORKSPACE_TOO_SMALL;
+  if (max_seqlen == 0) return ESM_ATTN_OK;
+  const char* ws = static_cast<const char*>(plan);
+  RotArgs a = {};
+  a.q = q;
+  a.k = k;
+  a.ld_in = in_row_stride;
+  a.q8 = q8;
+  a.k8 = k8;
+  a.q_inv = q_inv;
+  a.k_inv = k_inv;
+  a.rope = reinterpret_cast<const float2*>(ws + l.rope);
+  a.items = reinterpret_cast<const Item*>(ws + l.items);
+  a.H = num_heads;
+  if (launch_quantize_fp8(head_dim, rope_base != 0.f, a, l.n_slots,
+                          reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return ESM_ATTN_ERR_HIP;
+  return ESM_ATTN_OK;
+}
+
+esm_attn_status_t esm_attn_fwd_fp8_planned(const uint8_t* q8, const uint8_t* k8,
+                                           const uint16_t* v, int32_t v_row_stride,
+                                           int32_t batch, int32_t total_tokens,
+                                           int32_t max_seqlen, int32_t num_heads,
+                                           int32_t head_dim, float softmax_scale, float q_scale,
+                                           float k_scale, uint16_t* o, float* lse,
+                                           const void* plan, size_t plan_bytes, void* stream) {
+  esm_attn_status_t s = check_sizes(batch, total_tokens, max_seqlen, num_heads, head_dim);
+  if (s != ESM_ATTN_OK) return s;
+  if (head_dim != 64 && head_dim != 128) return ESM_ATTN_ERR_UNSUPPORTED;
+  if ((s = check_scalars(softmax_scale, 0.f)) != ESM_ATTN_OK) return s;
+  if ((s = check_fp8_scales(q_scale, k_scale)) != ESM_ATTN_OK) return s;
+  if ((s = check_stride(v_row_stride, total_tokens, num_heads, head_dim)) != ESM_ATTN_OK)
+    return s;
+  if (total_tokens == 0) return ESM_ATTN_OK;
+  const void* ptrs[] = {q8, k8, v, o, lse, plan};
+  for (const void* p : ptrs)
+    if (p == nullptr || !aligned16(p)) return ESM_ATTN_ERR_INVALID_ARGUMENT;
+  const Layout l = make_layout(batch, total_tokens, max_seqlen, num_heads, head_dim, false);
+  if (plan_bytes < l.plan) return ESM_ATTN_ERR_WORKSPACE_TOO_SMALL;
+  if (max_seqlen == 0) return ESM_ATTN_OK;
+  const char* ws = static_cast<const char*>(plan);
+  AttnArgs a = {};
+  a.q8 = q8;
+  a.k8 = k8;
+  a.ld8 = num_heads * head_dim;
+  a.v = v;
+  a.ld_qkv = v_row_stride;
+  a.out = o;
+  a.lse = lse;
+  a.items = reinterpret_cast<const Item*>(ws + l.items);
+  fill_common(&a, total_tokens, num_heads, softmax_scale);
+  // scores come out of the E4M3 products in units of 1 / (s_q s_k)
+  a.c = fmaxf(fabsf(softmax_scale) * kLog2e * q_scale * k_scale, 1e-30f);
+  if (launch_fwd_fp8(head_dim, a, l.n_slots, reinterpret_cast<hipStream_t>(stream)) !=
       hipSuccess)
     return ESM_ATTN_ERR_HIP;
   return ESM_ATTN_OK;

@@ -17,6 +17,7 @@ using Full = Tag<true>;
 using Ragged = Tag<false>;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -166,6 +167,28 @@ constexpr uint32_t kBf16OnePair = 0x3f803f80u;  // (1.0, 1.0) in bf16
 __device__ __forceinline__ float add_bf16x2(uint32_t x, float sum) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x),
                                          __builtin_bit_cast(bf16x2, 0x3f803f80u), sum, false);
+}
+
+// D(32x32, fp32) += A(32x64, fp8 E4M3) * B(64x32, fp8 E4M3), the gfx950
+// matrix instruction with unit block scales (E8M0 127 = 2^0). Lane (r, g)
+// holds 32 bytes (a0 then a1) of A row r, and the same 32 k positions of B
+// column r; D as for mfma32.
+__device__ __forceinline__ f32x16 mfma32_fp8(const u32x4& a0, const u32x4& a1, const u32x4& b0,
+                                             const u32x4& b1, const f32x16& c) {
+  typedef int v8i __attribute__((ext_vector_type(8)));
+  const v8i a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                 (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+  const v8i b = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
+                 (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// Four floats -> four E4M3 bytes (low byte first), round to nearest even;
+// the caller clamps to [-448, 448] (E4M3 has no infinity).
+__device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
+  int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  v = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
+  return (uint32_t)v;
 }
 
 // True if any lane of the wave has pred set (wave-uniform result).

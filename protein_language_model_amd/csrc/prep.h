@@ -31,6 +31,9 @@ struct RotArgs {
   uint16_t* k_rot;
   int32_t ld_in;        // elements between consecutive tokens' rows of q, k
   int32_t ld_out;       // ... of q_rot, k_rot
+  uint8_t* q8;          // E4M3 quantization: outputs [T][H][d] bytes (packed)
+  uint8_t* k8;
+  float q_inv, k_inv;   // fl32(1 / scale) of q and k
   const float2* rope;   // [max_seqlen][d/2]
   const Item* items;
   int32_t H;
@@ -38,6 +41,9 @@ struct RotArgs {
 
 hipError_t launch_rotate(int head_dim, bool rope, const RotArgs& a, int64_t n_slots,
                          hipStream_t stream);
+// q8 = E4M3(R(p) q * q_inv), k8 likewise (saturating, round to nearest even).
+hipError_t launch_quantize_fp8(int head_dim, bool rope, const RotArgs& a, int64_t n_slots,
+                               hipStream_t stream);
 
 // Everything the attention kernels read. Pointers to bf16 data are uint16_t.
 struct AttnArgs {
@@ -66,10 +72,14 @@ struct AttnArgs {
   int32_t n_split;      // split forward: key chunks per sequence
   float* o_part;        // split forward: [n_split][T][H][d] chunk outputs
   float* lse_part;      // split forward: [n_split][H][T] chunk LSEs
+  const uint8_t* q8;    // FP8 forward: E4M3 q~, k~ [T][H][d] bytes, row stride ld8
+  const uint8_t* k8;
+  int32_t ld8;
 };
 
 hipError_t launch_fwd(int head_dim, const AttnArgs& a, int64_t n_slots, bool split,
                       hipStream_t stream);
+hipError_t launch_fwd_fp8(int head_dim, const AttnArgs& a, int64_t n_slots, hipStream_t stream);
 
 // O = sum_r exp(LSE_r - LSE) O_r, LSE = log sum_r exp(LSE_r) over n_parts
 // partials o_part [n_parts][T][H][d] (fp32), lse_part [n_parts][H][T];

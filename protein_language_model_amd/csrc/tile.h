@@ -122,6 +122,36 @@ struct TilePair {
       }
   }
 
+  // One tile alone (the kernels that stream two tiles of different shapes):
+  // wave w takes pieces w, w + 4, ... of it, PER_TILE loads per wave.
+  template <int AUX = 0>
+  __device__ __forceinline__ void load_one(const uint16_t* __restrict__ G, int rs, int lim,
+                                           uint16_t* T, int w) const {
+    static_assert(!SMALL, "a tile of at least four pieces");
+    const int lane = lane_id_here();
+    const int rowbase = w * (64 / NC) + lane / NC;
+    const int xbase = 8 * ((lane % NC) ^ swz<D>(rowbase));
+#pragma unroll
+    for (int j = 0; j < PER_TILE; ++j) {
+      const int row = rowbase + ROWSTEP * j;
+      const int x = xbase ^ (8 * swz<D>(ROWSTEP * j));
+      const uint32_t off = 2u * (uint32_t)(min(row, lim - 1) * rs + x);
+      __builtin_amdgcn_global_load_lds((gptr_t)(reinterpret_cast<const char*>(G) + off),
+                                       (lptr_t)(T + (w + 4 * j) * 512), 16, 0, AUX);
+    }
+  }
+  __device__ __forceinline__ void load_full_one(const uint16_t* __restrict__ G, const Offsets& o,
+                                                uint16_t* T, int w) const {
+    static_assert(!SMALL, "a tile of at least four pieces");
+#pragma unroll
+    for (int j = 0; j < PER_TILE; ++j) {
+      uint32_t v = o.v[j];
+      asm volatile("" : "+v"(v));  // fresh 32-bit value: the saddr form (see load_full)
+      __builtin_amdgcn_global_load_lds((gptr_t)(reinterpret_cast<const char*>(G) + v),
+                                       (lptr_t)(T + (w + 4 * j) * 512), 16, 0, 0);
+    }
+  }
+
   // Per-lane values of load() are recomputed at each call (a few
   // instructions) rather than kept live across the kernels' main loops.
   __device__ __forceinline__ TilePair(int, int) {}
@@ -197,7 +227,6 @@ __device__ __forceinline__ void block_barrier() {
   asm volatile("" ::: "memory");
 }
 
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // MFMA operands whose k index runs along the ROWS of a tile (the transposed
 // tile), for the row blocks k0(u) = 32 (u / 2) + 8 (u % 2), u < NU, of the

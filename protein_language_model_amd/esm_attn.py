@@ -46,6 +46,8 @@ EXPORTED = (
     "esm_attn_bucket_batches",
     "esm_attn_fwd_split_planned",
     "esm_attn_merge_partials",
+    "esm_attn_quantize_fp8_planned",
+    "esm_attn_fwd_fp8_planned",
 )
 
 PASS_DQ, PASS_DKV = 1, 2
@@ -108,6 +110,12 @@ def lib():
     L.esm_attn_fwd_split_planned.restype = i32
     L.esm_attn_fwd_split_planned.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32,
                                              vp, vp, vp, vp, vp, u64, vp]
+    L.esm_attn_quantize_fp8_planned.restype = i32
+    L.esm_attn_quantize_fp8_planned.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, f32, f32,
+                                                f32, vp, vp, vp, u64, vp]
+    L.esm_attn_fwd_fp8_planned.restype = i32
+    L.esm_attn_fwd_fp8_planned.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, f32,
+                                           f32, vp, vp, vp, u64, vp]
     L.esm_attn_merge_partials.restype = i32
     L.esm_attn_merge_partials.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp]
     L.esm_attn_bucket_batches.restype = i32
@@ -340,6 +348,48 @@ def esm_attn_merge_partials(o_part, lse_part, out=None, lse=None, stream=None):
         lse = torch.empty((H, T), dtype=torch.float32, device=o_part.device)
     _check(lib().esm_attn_merge_partials(_ptr(o_part), _ptr(lse_part), R, T, H, d, _ptr(out),
                                          _ptr(lse), _stream(stream)))
+    return out, lse
+
+
+def esm_attn_quantize_fp8_planned(q, k, batch, max_seqlen, plan, q_scale, k_scale,
+                                  rope_base=10000.0, q8=None, k8=None, stream=None):
+    """E4M3 q8 = E4M3(R(p) q / q_scale), k8 likewise (saturating); returns
+    (q8, k8), uint8 [T, H, d] (packed). q, k may be strided views."""
+    T, H, d = q.shape
+    ld = _row_stride(q, k)
+    if q8 is None:
+        q8 = torch.empty((T, H, d), dtype=torch.uint8, device=q.device)
+    if k8 is None:
+        k8 = torch.empty((T, H, d), dtype=torch.uint8, device=q.device)
+    for t in (q8, k8):
+        if t.dtype != torch.uint8 or tuple(t.shape) != (T, H, d) or not t.is_contiguous():
+            raise ValueError("q8, k8 must be contiguous uint8 [T, H, d]")
+    _check(lib().esm_attn_quantize_fp8_planned(_ptr(q), _ptr(k), ld, int(batch), T,
+                                               int(max_seqlen), H, d, float(rope_base),
+                                               float(q_scale), float(k_scale), _ptr(q8), _ptr(k8),
+                                               _ptr(plan), plan.numel(), _stream(stream)))
+    return q8, k8
+
+
+def esm_attn_fwd_fp8_planned(q8, k8, v, batch, max_seqlen, plan, q_scale, k_scale,
+                             softmax_scale=None, out=None, lse=None, stream=None):
+    """Forward with E4M3 q8, k8 (esm_attn_quantize_fp8_planned's outputs) and
+    bf16 v; returns (o bf16 [T, H, d], lse fp32 [H, T])."""
+    T, H, d = v.shape
+    ldv = _row_stride(v)
+    for t in (q8, k8):
+        if t.dtype != torch.uint8 or tuple(t.shape) != (T, H, d) or not t.is_contiguous():
+            raise ValueError("q8, k8 must be contiguous uint8 [T, H, d]")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty((T, H, d), dtype=v.dtype, device=v.device)
+    _check_packed((T, H, d), out)
+    if lse is None:
+        lse = torch.empty((H, T), dtype=torch.float32, device=v.device)
+    _check(lib().esm_attn_fwd_fp8_planned(_ptr(q8), _ptr(k8), _ptr(v), ldv, int(batch), T,
+                                          int(max_seqlen), H, d, scale, float(q_scale),
+                                          float(k_scale), _ptr(out), _ptr(lse), _ptr(plan),
+                                          plan.numel(), _stream(stream)))
     return out, lse
 
 

@@ -20,7 +20,7 @@ NULL = None
 
 def _header_functions():
     text = open(os.path.join(ROOT, "include", "esm_attn.h")).read()
-    return sorted(set(re.findall(r"\b(esm_attn_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(esm_attn_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_every_declared_symbol_is_exported():
@@ -188,6 +188,23 @@ def test_split_forward_and_merge_validation():
     assert L.esm_attn_merge_partials(q, None, 2, T, 2, 16, q, q, None) == E.ERR_INVALID_ARGUMENT
     assert L.esm_attn_merge_partials(q + 4, q, 2, T, 2, 16, q, q, None) == E.ERR_INVALID_ARGUMENT
     assert L.esm_attn_merge_partials(None, None, 2, 0, 2, 16, None, None, None) == E.OK
+
+
+def test_fp8_validation():
+    """Host checks of the FP8 calls (fake device pointers)."""
+    L = E.lib()
+    p, q, T = 1 << 12, 1 << 13, 8
+    quant = lambda d, qs, ks, pb=1 << 30: L.esm_attn_quantize_fp8_planned(
+        p, p, 2 * d, 1, T, T, 2, d, 1e4, qs, ks, q, q, p, pb, None)
+    fwd = lambda d, qs, ks, pb=1 << 30: L.esm_attn_fwd_fp8_planned(
+        q, q, p, 2 * d, 1, T, T, 2, d, 0.1, qs, ks, q, q, p, pb, None)
+    for call in (quant, fwd):
+        assert call(32, 1.0, 1.0) == E.ERR_UNSUPPORTED          # head_dim 64 or 128 only
+        assert call(64, 0.0, 1.0) == E.ERR_INVALID_ARGUMENT
+        assert call(64, 1.0, -2.0) == E.ERR_INVALID_ARGUMENT
+        assert call(64, float("nan"), 1.0) == E.ERR_INVALID_ARGUMENT
+        assert call(64, 1e-40, 1.0) == E.ERR_INVALID_ARGUMENT   # 1 / scale overflows
+        assert call(64, 1.0, 1.0, pb=4) == E.ERR_WORKSPACE_TOO_SMALL
 
 
 def test_check_cu_seqlens_host():
