@@ -90,38 +90,43 @@ __global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(AttnArgs a) 
   const int qi = q0 + w * 32 + r;  // this lane's query
   const bool qvalid = qi < L;
   const uint32_t qflip = a.q_sign < 0.f ? 0x80008000u : 0u;
-  u32x4 qreg[C::NS], doreg[C::NS];
+  // Every load reads a clamped row and is issued before any is used (loads
+  // under a branch would each be awaited at the branch's end); rows past the
+  // end are zeroed afterwards.
+  const int qc = min(qi, L - 1);
+  const int64_t rowidx = (int64_t)h * a.T + it.seq0 + qi;
+  const float lse_raw = a.lse_in[(int64_t)h * a.T + it.seq0 + qc];
+  u32x4 qreg[C::NS], doreg[C::NS], oreg[C::NS];
+#pragma unroll
+  for (int s = 0; s < C::NS; ++s) {
+    qreg[s] = ld16(Qg + qc * rs + 16 * s + 8 * g);
+    doreg[s] = ld16(dOg + qc * rso + 16 * s + 8 * g);
+    oreg[s] = ld16(Og + qc * rso + 16 * s + 8 * g);
+  }
   float dpart = 0.f;
 #pragma unroll
   for (int s = 0; s < C::NS; ++s) {
-    qreg[s] = zero4();
-    doreg[s] = zero4();
-    if (qvalid) {
-      qreg[s] = ld16(Qg + qi * rs + 16 * s + 8 * g);
+    float fo[8], fd[8];
+    unpack8(oreg[s], fo);
+    unpack8(doreg[s], fd);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) qreg[s][e] ^= qflip;
-      doreg[s] = ld16(dOg + qi * rso + 16 * s + 8 * g);
-      const u32x4 ov = ld16(Og + qi * rso + 16 * s + 8 * g);
-      float fo[8], fd[8];
-      unpack8(ov, fo);
-      unpack8(doreg[s], fd);
+    for (int e = 0; e < 8; ++e) dpart = fmaf(fd[e], fo[e], dpart);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) dpart = fmaf(fd[e], fo[e], dpart);
+    for (int e = 0; e < 4; ++e) {
+      qreg[s][e] = qvalid ? qreg[s][e] ^ qflip : 0u;
+      doreg[s][e] = qvalid ? doreg[s][e] : 0u;
     }
   }
+  if (!qvalid) dpart = 0.f;
   const float Dq = dpart + xor32(dpart);
   // dP - D in one more MFMA k-step: A = (1, 1), B = (-D_hi, -D_lo), in the
   // k slots of lane half 0.
   const u32x4 a_one = {g == 0 ? kBf16OnePair : 0u, 0u, 0u, 0u};
   const u32x4 b_negd = {g == 0 ? neg_bf16_pair(Dq) : 0u, 0u, 0u, 0u};
-  const int64_t rowidx = (int64_t)h * a.T + it.seq0 + qi;
-  float lse2 = 0.f;
-  if (qvalid) {
-    lse2 = a.lse_in[rowidx] * kLog2e;
-    if (g == 0) {
-      a.drow[rowidx] = Dq;
-      a.drow[(int64_t)a.H * a.T + rowidx] = lse2;
-    }
+  const float lse2 = qvalid ? lse_raw * kLog2e : 0.f;
+  if (qvalid && g == 0) {
+    a.drow[rowidx] = Dq;
+    a.drow[(int64_t)a.H * a.T + rowidx] = lse2;
   }
 
   // blocks 1 .. NSTAGE-2 after the prologue's global loads (see the wait below)
@@ -275,18 +280,21 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkv_kernel(AttnArgs a
   // signed scale.
   const int kj = k0 + w * 32 + r;
   const uint32_t kflip = a.q_sign < 0.f ? 0x80008000u : 0u;
+  // (branch-free loads of a clamped row, zeroed past the end: see the dq pass)
+  const int kc = min(kj, L - 1);
   u32x4 kreg[C::NS], vreg[C::NS];
 #pragma unroll
   for (int s = 0; s < C::NS; ++s) {
-    kreg[s] = zero4();
-    vreg[s] = zero4();
-    if (kj < L) {
-      kreg[s] = ld16(Kg + kj * rs + 16 * s + 8 * g);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) kreg[s][e] ^= kflip;
-      vreg[s] = ld16(Vg + kj * rs + 16 * s + 8 * g);
-    }
+    kreg[s] = ld16(Kg + kc * rs + 16 * s + 8 * g);
+    vreg[s] = ld16(Vg + kc * rs + 16 * s + 8 * g);
   }
+#pragma unroll
+  for (int s = 0; s < C::NS; ++s)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      kreg[s][e] = kj < L ? kreg[s][e] ^ kflip : 0u;
+      vreg[s][e] = kj < L ? vreg[s][e] : 0u;
+    }
 
   // blocks 1 .. NSTAGE-2 after the prologue's global loads (see the wait below)
 #pragma unroll

@@ -119,18 +119,18 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(AttnArgs a) {
 
   // queries: B operands (8 d values per k-step); rows past the end are zero.
   // A negative softmax scale is applied as a sign flip of q~ (exact), so that
-  // scores use |scale|.
+  // scores use |scale|. The loads read a clamped row and are selected away
+  // afterwards: loads under a branch would each be awaited at the branch's
+  // end, one memory round trip per k-step.
   const uint32_t qflip = a.q_sign < 0.f ? 0x80008000u : 0u;
+  const int qc = min(qi, L - 1);
   u32x4 qreg[C::NS];
 #pragma unroll
-  for (int s = 0; s < C::NS; ++s) {
-    qreg[s] = zero4();
-    if (qi < L) {
-      qreg[s] = ld16(Qg + qi * rs + 16 * s + 8 * g);
+  for (int s = 0; s < C::NS; ++s) qreg[s] = ld16(Qg + qc * rs + 16 * s + 8 * g);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) qreg[s][e] ^= qflip;
-    }
-  }
+  for (int s = 0; s < C::NS; ++s)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) qreg[s][e] = qi < L ? qreg[s][e] ^ qflip : 0u;
   // Blocks 1 .. NSTAGE-2 are issued after the q~ loads, so that the first
   // wait below (which lets one block's loads stay in flight) covers those.
 #pragma unroll

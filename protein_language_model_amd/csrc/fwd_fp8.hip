@@ -81,19 +81,21 @@ __global__ __launch_bounds__(256, Fp8Cfg<D>::OCC) void fwd_fp8_kernel(AttnArgs a
   // queries: 32 bytes per k-step (d values 64s + 32g ..), zero past the end;
   // a negative softmax scale flips the sign bit of every q8 byte (exact)
   const int qi = q0 + w * 32 + r;
+  // (branch-free loads of a clamped row, as in the bf16 forward)
   const uint32_t qflip = a.q_sign < 0.f ? 0x80808080u : 0u;
+  const int qc = min(qi, L - 1);
   u32x4 qreg[C::NS8][2];
 #pragma unroll
   for (int s = 0; s < C::NS8; ++s)
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      qreg[s][hh] = zero4();
-      if (qi < L) {
-        qreg[s][hh] = ld16(Qg + (int64_t)qi * a.ld8 + 64 * s + 32 * g + 16 * hh);
+    for (int hh = 0; hh < 2; ++hh)
+      qreg[s][hh] = ld16(Qg + (int64_t)qc * a.ld8 + 64 * s + 32 * g + 16 * hh);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) qreg[s][hh][e] ^= qflip;
-      }
-    }
+  for (int s = 0; s < C::NS8; ++s)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qreg[s][hh][e] = qi < L ? qreg[s][hh][e] ^ qflip : 0u;
 #pragma unroll
   for (int j = 1; j < C::NSTAGE - 1; ++j)
     if (j < nkb) issue(j, j);
