@@ -13,8 +13,9 @@ Functions keep the C names:
 the planned steps (esm_attn_plan, esm_attn_rotate_planned,
 esm_attn_fwd_planned, esm_attn_bwd_planned), the workspace queries,
 esm_attn_check_cu_seqlens_host, esm_attn_schedule_host, the host batch former
-esm_attn_bucket_batches, and `attention`, an autograd wrapper over the
-planned steps.
+esm_attn_bucket_batches, the split-KV, merge and FP8 calls, and the autograd
+wrappers `attention` (packed q, k, v) and `attention_qkv` (one fused projection
+output, rotated in place).
 """
 
 import ctypes
@@ -490,6 +491,69 @@ class _Attention(torch.autograd.Function):
         dq, dk, dv, _ = esm_attn_bwd_planned(q_rot, k_rot, v, o, grad.contiguous(), lse, B,
                                              max_seqlen, plan, scale, rope_base)
         return dq, dk, dv, None, None, None, None
+
+
+class _AttentionQKV(torch.autograd.Function):
+    """Fused layer boundary: q, k, v are views of one projection output
+    qkv [T, 3*H*d]; q and k are rotated in place (the buffer then holds q~,
+    k~, v and is kept for backward in place of any copy), and the backward
+    writes dq, dk, dv into one [T, 3*H*d] gradient, the operand of the
+    projection's backward GEMMs."""
+
+    @staticmethod
+    def forward(ctx, qkv, cu_seqlens, max_seqlen, num_heads, scale, rope_base, plan):
+        T = qkv.shape[0]
+        H = num_heads
+        d = qkv.shape[1] // (3 * H)
+        view = qkv.view(T, 3, H, d)
+        q, k, v = view[:, 0], view[:, 1], view[:, 2]
+        B = cu_seqlens.numel() - 1
+        if plan is None:
+            plan = esm_attn_plan(cu_seqlens, T, max_seqlen, H, d, rope_base)
+        if rope_base != 0.0:
+            esm_attn_rotate_planned(q, k, B, max_seqlen, plan, rope_base, q_rot=q, k_rot=k)
+        ctx.mark_dirty(qkv)
+        o, lse = esm_attn_fwd_planned(q, k, v, B, max_seqlen, plan, scale)
+        ctx.save_for_backward(qkv, o, lse, plan)
+        ctx.args = (B, max_seqlen, H, d, scale, rope_base)
+        ctx.set_materialize_grads(False)
+        return o, qkv
+
+    @staticmethod
+    def backward(ctx, grad_o, grad_qkv):
+        if grad_qkv is not None:
+            raise RuntimeError("attention_qkv: the rotated qkv buffer it returns is not "
+                               "differentiable; use only the attention output")
+        qkv, o, lse, plan = ctx.saved_tensors
+        B, max_seqlen, H, d, scale, rope_base = ctx.args
+        T = qkv.shape[0]
+        view = qkv.view(T, 3, H, d)
+        dqkv = torch.empty_like(qkv)
+        g3 = dqkv.view(T, 3, H, d)
+        if grad_o is None:
+            return dqkv.zero_(), None, None, None, None, None, None
+        esm_attn_bwd_planned(view[:, 0], view[:, 1], view[:, 2], o, grad_o.contiguous(), lse, B,
+                             max_seqlen, plan, scale, rope_base, dq=g3[:, 0], dk=g3[:, 1],
+                             dv=g3[:, 2])
+        return dqkv, None, None, None, None, None, None
+
+
+def attention_qkv(qkv, cu_seqlens, max_seqlen, num_heads, softmax_scale=None,
+                  rope_base=10000.0, plan=None):
+    """Autograd entry on a fused projection output qkv [T, 3*H*d] (contiguous,
+    bf16; q, k, v are its column blocks of H*d): returns o [T, H, d]. q and k
+    are rotated IN PLACE inside qkv (which must not be used afterwards), so no
+    rotated copies exist; the gradient of qkv is one fused [T, 3*H*d] tensor.
+    `plan` may be a plan built once for the batch and shared by every layer."""
+    if qkv.dim() != 2 or qkv.dtype != torch.bfloat16 or not qkv.is_contiguous():
+        raise ValueError("qkv must be a contiguous bf16 [T, 3*H*d] tensor")
+    if qkv.shape[1] % (3 * num_heads) != 0:
+        raise ValueError("qkv width must be 3 * num_heads * head_dim")
+    d = qkv.shape[1] // (3 * num_heads)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    o, _ = _AttentionQKV.apply(qkv, cu_seqlens, int(max_seqlen), int(num_heads), scale,
+                               float(rope_base), plan)
+    return o
 
 
 def attention(q, k, v, cu_seqlens, max_seqlen, softmax_scale=None, rope_base=10000.0):

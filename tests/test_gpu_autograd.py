@@ -1,0 +1,74 @@
+"""The autograd wrappers: `attention` (packed q, k, v) equals the one-shot
+calls bit for bit, forward and backward; `attention_qkv` (fused projection
+output, rotated in place) gives the same output and the same gradients of
+the projection's input and weight as the packed path."""
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import say, to_dev
+from protein_language_model_amd import workloads as W
+from protein_language_model_amd import esm_attn as E
+
+pytestmark = pytest.mark.gpu
+
+
+def test_attention_autograd_equals_one_shot(device):
+    inp = W.make_inputs("esm2_650m", lengths=[300, 1, 129, 0, 64], num_heads=2)
+    maxL, s, base = max(inp["lengths"]), inp["scale"], inp["rope_base"]
+    cu = torch.from_numpy(inp["cu_seqlens"]).to(device)
+    q, k, v, do = (to_dev(inp[x], device) for x in ("q", "k", "v", "do"))
+    o_ref, lse_ref = E.esm_attn_fwd(q, k, v, cu, maxL, s, base)
+    dq_ref, dk_ref, dv_ref = E.esm_attn_bwd(q, k, v, o_ref, do, lse_ref, cu, maxL, s, base)
+    qa, ka, va = (t.clone().requires_grad_(True) for t in (q, k, v))
+    o = E.attention(qa, ka, va, cu, maxL, s, base)
+    o.backward(do)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref)
+    for a, b in ((qa.grad, dq_ref), (ka.grad, dk_ref), (va.grad, dv_ref)):
+        assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_attention_qkv_in_a_projection(device, d):
+    rng = np.random.default_rng(d)
+    lengths = [300, 1, 129, 64]
+    H, T, C = 2, sum(lengths), 64
+    cu = torch.from_numpy(W.cu_from_lengths(lengths)).to(device)
+    maxL = max(lengths)
+    say("case attention_qkv", d)
+    x0 = torch.from_numpy(rng.standard_normal((T, C)).astype(np.float32)).to(device)
+    w0 = torch.from_numpy((rng.standard_normal((3 * H * d, C)) / 8).astype(np.float32)).to(device)
+    do = torch.from_numpy(rng.standard_normal((T, H, d)).astype(np.float32)).to(device)
+    x0, w0, do = x0.to(torch.bfloat16), w0.to(torch.bfloat16), do.to(torch.bfloat16)
+
+    def run(fused):
+        x = x0.clone().requires_grad_(True)
+        w = w0.clone().requires_grad_(True)
+        qkv = x @ w.t()
+        if fused:
+            o = E.attention_qkv(qkv, cu, maxL, H)
+        else:
+            q, k, v = (qkv.view(T, 3, H, d)[:, i].contiguous() for i in range(3))
+            o = E.attention(q, k, v, cu, maxL)
+        o.backward(do)
+        torch.cuda.synchronize()
+        return o.detach(), x.grad, w.grad
+
+    of, xf, wf = run(True)
+    op, xp, wp = run(False)
+    assert torch.equal(of, op)
+    assert torch.equal(xf, xp) and torch.equal(wf, wp)
+
+
+def test_attention_qkv_buffer_is_not_differentiable(device):
+    lengths = [40, 9]
+    H, d, T = 1, 64, 49
+    cu = torch.from_numpy(W.cu_from_lengths(lengths)).to(device)
+    w = torch.randn(3 * H * d, 16, device=device, dtype=torch.bfloat16, requires_grad=True)
+    x = torch.randn(T, 16, device=device, dtype=torch.bfloat16)
+    qkv = x @ w.t()
+    o = E.attention_qkv(qkv, cu, 40, H)
+    with pytest.raises(RuntimeError):
+        (o.float().sum() + qkv.float().sum()).backward()
