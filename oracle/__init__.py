@@ -21,6 +21,7 @@ from .attention import (  # noqa: F401
     attention_forward_partial_slice,
     merge_partials,
     attention_backward_slice,
+    attention_rows_slice,
     forward,
     backward,
 )

@@ -268,6 +268,30 @@ def attention_backward_slice(q, k, v, do, scale, base, mode="bf16_operands",
     return dq, dk, dv
 
 
+def attention_rows_slice(q, k, v, do, scale, base, rows, mode="bf16_operands"):
+    """The forward and the query gradient of one sequence and head at the
+    query rows `rows` only: the definitions above restricted to those rows
+    (every key still enters), O(len(rows) * L * d) work, so long sequences
+    can be checked row by row. Returns (O [r, d], LSE [r], dq [r, d])."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    do = np.asarray(do, np.float64)
+    rows = np.asarray(rows, dtype=np.int64)
+    pos, qr, kr = _rotated_operands(q, k, base, mode)
+    s = float(scale)
+    S = s * (qr[rows] @ kr.T)
+    m = S.max(axis=1)
+    lse = m + np.log(np.exp(S - m[:, None]).sum(axis=1))
+    P = np.exp(S - lse[:, None])
+    O = P @ v
+    dP = do[rows] @ v.T
+    D = (P * dP).sum(axis=1)
+    dqr = s * ((P * (dP - D[:, None])) @ kr)
+    dq = rope_rotate(dqr, pos[rows], base, inverse=True)
+    return O, lse, dq
+
+
 # --------------------------------------------------------------------------
 # packed batches
 # --------------------------------------------------------------------------

@@ -260,3 +260,20 @@ def test_packed_backward_equals_per_sequence():
             np.testing.assert_array_equal(dq[a:e, h], g[0])
             np.testing.assert_array_equal(dk[a:e, h], g[1])
             np.testing.assert_array_equal(dv[a:e, h], g[2])
+
+
+@pytest.mark.parametrize("mode", ["exact", "bf16_operands"])
+def test_row_restricted_forward_and_dq_equal_the_full_slice(mode):
+    """attention_rows_slice is the full-slice definition restricted to some
+    query rows (the full slice is pinned above by a brute force, torch and
+    finite differences)."""
+    rng = np.random.default_rng(30)
+    L, d, s = 70, 16, 0.3
+    q, k, v, do = (rng.standard_normal((L, d)) for _ in range(4))
+    rows = [0, 1, 33, 69]
+    O, lse = oracle.attention_forward_slice(q, k, v, s, BASE, mode=mode)
+    dq, _, _ = oracle.attention_backward_slice(q, k, v, do, s, BASE, mode=mode)
+    Or, lr, dqr = oracle.attention_rows_slice(q, k, v, do, s, BASE, rows, mode=mode)
+    np.testing.assert_allclose(Or, O[rows], atol=1e-12)
+    np.testing.assert_allclose(lr, lse[rows], atol=1e-12)
+    np.testing.assert_allclose(dqr, dq[rows], atol=1e-12)
