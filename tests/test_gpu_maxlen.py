@@ -1,0 +1,45 @@
+"""The longest sequence the library accepts (max_seqlen 65536) next to a
+short one: forward rows and query-gradient rows against the oracle restricted
+to sampled rows, and dk, dv through identities that hold at any size:
+sum_j dv_j = sum_i dO_i (the rows of P sum to 1) and sum_j R(p_j) dk_j = 0
+(sum_j dS_ij = 0 for every query i)."""
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_helpers import compare, run_gpu, say, oracle_inputs, ulp_bf16
+from protein_language_model_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+NAMES = {64: "esm2_650m", 128: "esm2_15b"}
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_maximum_sequence_length(device, d):
+    lengths = [65536, 77]
+    inp = W.make_inputs(NAMES[d], lengths=lengths, num_heads=1)
+    say("case max length", d, lengths)
+    gpu = run_gpu(inp, device)
+    compare(gpu, inp, seqs=[1], label="short sequence beside the longest")
+    q, k, v, do = oracle_inputs(inp)
+    s, base = inp["scale"], inp["rope_base"]
+    L = lengths[0]
+    rng = np.random.default_rng(d)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 129, 4095, 32767, 65534, 65535],
+                                     rng.integers(0, L, size=8)]))
+    O, lse, dq = oracle.attention_rows_slice(q[:L, 0], k[:L, 0], v[:L, 0], do[:L, 0], s, base,
+                                             rows)
+    og, lg, dqg = gpu["o"][rows, 0], gpu["lse"][0, rows], gpu["dq"][rows, 0]
+    assert (np.abs(og - O) <= 1e-2 + 0.5 * ulp_bf16(O)).all(), float(np.abs(og - O).max())
+    assert np.abs(lg - lse).max() <= 2e-3
+    assert np.linalg.norm(dqg - dq) / np.linalg.norm(dq) <= 2e-2
+    # identities over all keys of the long sequence (each dv_j, dk_j carries
+    # one bf16 rounding, relative 2^-9)
+    dv, dk = gpu["dv"][:L, 0], gpu["dk"][:L, 0]
+    gap_v = np.abs(dv.sum(axis=0) - do[:L, 0].sum(axis=0))
+    assert (gap_v <= 2.0 ** -8 * np.abs(dv).sum(axis=0) + 1e-6).all(), float(gap_v.max())
+    rot = oracle.rope_rotate(dk, np.arange(L), base)
+    gap_k = np.abs(rot.sum(axis=0))
+    assert (gap_k <= 1e-2 * np.abs(dk).sum(axis=0)).all(), float(gap_k.max())
