@@ -18,7 +18,7 @@ constexpr int32_t kMaxSplit = 64;  // key chunks / partials per merge
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t rope = 0, sorted = 0, chunk = 0, items = 0, plan = 0;  // the plan
+  size_t rope = 0, sorted = 0, chunk = 0, items = 0, pos = 0, plan = 0;  // the plan
   size_t drow = 0, qrot = 0, krot = 0, total = 0;                // one-shot calls only
   int64_t n_slots = 0;
   int32_t n_chunks = 0;
@@ -55,6 +55,7 @@ Layout make_layout(int32_t B, int32_t T, int32_t maxL, int32_t H, int32_t d, boo
   l.sorted = take((size_t)B * sizeof(int32_t));
   l.chunk = take((size_t)(l.n_chunks + 1) * sizeof(int32_t));
   l.items = take((size_t)(l.n_slots > 0 ? l.n_slots : 1) * sizeof(Item));
+  l.pos = take((size_t)(T > 0 ? T : 1) * sizeof(int32_t));
   l.plan = off;
   const size_t elems = (size_t)T * H * d;
   l.qrot = take(elems * sizeof(uint16_t));
@@ -119,6 +120,7 @@ esm_attn_status_t run_prep(const int32_t* cu, int32_t B, int32_t T, int32_t maxL
   p.n_slots = l.n_slots;
   p.rope = rope_base != 0.f ? reinterpret_cast<float2*>(ws + l.rope) : nullptr;
   p.rope_base = rope_base;
+  p.pos = reinterpret_cast<int32_t*>(ws + l.pos);
   return launch_prep(p, st) == hipSuccess ? ESM_ATTN_OK : ESM_ATTN_ERR_HIP;
 }
 
@@ -204,10 +206,12 @@ esm_attn_status_t esm_attn_rotate_planned(const uint16_t* q, const uint16_t* k,
   a.ld_in = in_row_stride;
   a.ld_out = out_row_stride;
   a.rope = reinterpret_cast<const float2*>(ws + l.rope);
-  a.items = reinterpret_cast<const Item*>(ws + l.items);
+  a.pos = reinterpret_cast<const int32_t*>(ws + l.pos);
   a.H = num_heads;
-  if (launch_rotate(head_dim, rope_base != 0.f, a, l.n_slots,
-                    reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+  a.T = total_tokens;
+  a.max_pos = max_seqlen - 1;
+  if (launch_rotate(head_dim, rope_base != 0.f, a, reinterpret_cast<hipStream_t>(stream)) !=
+      hipSuccess)
     return ESM_ATTN_ERR_HIP;
   return ESM_ATTN_OK;
 }

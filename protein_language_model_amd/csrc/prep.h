@@ -18,6 +18,7 @@ struct PrepArgs {
   int64_t n_slots;
   float2* rope;         // [max_seqlen][head_dim/2], or null
   double rope_base;
+  int32_t* pos;         // [T] position of each token in its sequence
 };
 
 hipError_t launch_prep(const PrepArgs& a, hipStream_t stream);
@@ -35,12 +36,14 @@ struct RotArgs {
   uint8_t* k8;
   float q_inv, k_inv;   // fl32(1 / scale) of q and k
   const float2* rope;   // [max_seqlen][d/2]
+  const int32_t* pos;   // [T] token positions (the plan's)
   const Item* items;
-  int32_t H;
+  int32_t H, T;
+  int32_t max_pos;      // max_seqlen - 1: positions are clamped to [0, max_pos]
 };
 
-hipError_t launch_rotate(int head_dim, bool rope, const RotArgs& a, int64_t n_slots,
-                         hipStream_t stream);
+// Rotation pass over all tokens (token-major: whole token rows, every head).
+hipError_t launch_rotate(int head_dim, bool rope, const RotArgs& a, hipStream_t stream);
 // q8 = E4M3(R(p) q * q_inv), k8 likewise (saturating, round to nearest even).
 hipError_t launch_quantize_fp8(int head_dim, bool rope, const RotArgs& a, int64_t n_slots,
                                hipStream_t stream);

@@ -133,8 +133,24 @@ __global__ __launch_bounds__(256) void schedule_fill_kernel(
     const int32_t* __restrict__ cu, const int32_t* __restrict__ sorted,
     const int32_t* __restrict__ chunk_base, int32_t n_chunks, int32_t B, int32_t T, int32_t H,
     int32_t max_seqlen, int32_t block, Item* __restrict__ items, int64_t n_slots,
-    float2* __restrict__ rope, int32_t head_dim, double rope_base) {
+    float2* __restrict__ rope, int32_t head_dim, double rope_base, int32_t* __restrict__ pos,
+    int32_t pos_chunks) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (blockIdx.y == 2) {
+    // token positions: workgroup x covers tokens 256 c .. 256 c + 255 of
+    // sequence b (x = b * pos_chunks + c). Every token of a valid cu_seqlens
+    // belongs to exactly one sequence; the readers clamp whatever they read
+    // to [0, max_seqlen), so a bad cu_seqlens cannot make them index out of
+    // the rotary table.
+    const int64_t b = blockIdx.x / pos_chunks;
+    if (b >= B) return;
+    const int32_t c = (int32_t)(blockIdx.x - b * pos_chunks);
+    int32_t st, L;
+    seq_bounds(cu, (int32_t)b, T, max_seqlen, &st, &L);
+    const int32_t p = 256 * c + (int32_t)threadIdx.x;
+    if (p < L) pos[st + p] = p;
+    return;
+  }
   if (blockIdx.y == 0) {
     if (i >= n_slots) return;
     Item it;
@@ -168,11 +184,15 @@ hipError_t launch_prep(const PrepArgs& a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t table = (int64_t)a.max_seqlen * (a.head_dim / 2);
-  const int64_t work = a.n_slots > table ? a.n_slots : table;
-  dim3 grid((unsigned)ceil_div64(work > 0 ? work : 1, 256), 2);
+  const int32_t pos_chunks = (int32_t)ceil_div64(a.max_seqlen > 0 ? a.max_seqlen : 1, 256);
+  const int64_t pos_wgs = (int64_t)a.B * pos_chunks;
+  int64_t wgs = ceil_div64(a.n_slots > table ? a.n_slots : table, 256);
+  if (pos_wgs > wgs) wgs = pos_wgs;
+  dim3 grid((unsigned)(wgs > 0 ? wgs : 1), 3);
   schedule_fill_kernel<<<grid, 256, 0, stream>>>(a.cu, a.sorted, a.chunk_base, a.n_chunks, a.B,
                                                  a.T, a.H, a.max_seqlen, a.block, a.items,
-                                                 a.n_slots, a.rope, a.head_dim, a.rope_base);
+                                                 a.n_slots, a.rope, a.head_dim, a.rope_base,
+                                                 a.pos, pos_chunks);
   return hipGetLastError();
 }
 

@@ -15,47 +15,48 @@
 
 namespace esm {
 
-constexpr int kRotSplit = 2;  // workgroups per 128-row item
+constexpr int kRotSplit = 2;  // workgroups per 128-row item (quantization pass)
+constexpr int kRotUnits = 4;  // 8-pair units per thread (rotation pass)
 
-// Workgroup (x, y) rotates rows [blk * 128 + y * RR, blk * 128 + (y + 1) * RR)
-// (RR = 128 / kRotSplit) of the (sequence, head) of schedule slot x, q and k:
-// one 8-pair chunk (16 bytes of the low half, 16 of the high half) per
-// thread and tensor, all loads issued before any arithmetic. Many small
-// workgroups keep enough loads in flight to stream at close to copy speed
-// (grouping several heads per workgroup to share the cos/sin loads measured
-// slower: fewer loads in flight).
+// Rotation pass, token-major: unit u (8 rotary pairs: 16 bytes of the low
+// half and 16 bytes of the high half of one head row) is token
+// u / (H d/16), head and pair offset from the rest, so consecutive threads
+// read consecutive bytes of whole token rows (every head of a token in one
+// stretch of memory) and the cos/sin row of a position is reused by every
+// head of the token. Each thread issues the loads of kRotUnits units before
+// any arithmetic. Positions come from the plan (clamped into the table).
 template <int D, bool ROPE>
 __global__ __launch_bounds__(256) void rotate_kernel(RotArgs a) {
-  const Item it = a.items[blockIdx.x];
-  if (it.len <= 0) return;
-  constexpr int UPR = D / 16;                        // 8-pair chunks per row
-  constexpr int RR = kItemRows / kRotSplit;          // rows per workgroup
-  constexpr int NU = (RR * UPR + 255) / 256;         // units per thread
-  const int r0 = it.blk * kItemRows + blockIdx.y * RR;
-  const int n = min(RR, it.len - r0) * UPR;          // may be <= 0
-  const int64_t bin = (int64_t)it.seq0 * a.ld_in + (int64_t)it.head * D;
-  const int64_t bout = (int64_t)it.seq0 * a.ld_out + (int64_t)it.head * D;
-  u32x4 ql[NU], qh[NU], kl[NU], kh[NU];
-  float2 cs[NU][8];
+  constexpr int UPR = D / 16;  // units per head row
+  const int upt = a.H * UPR;   // units per token
+  const int64_t total = (int64_t)a.T * upt;
+  const int64_t u0 = (int64_t)blockIdx.x * 256 * kRotUnits + threadIdx.x;
+  u32x4 ql[kRotUnits], qh[kRotUnits], kl[kRotUnits], kh[kRotUnits];
+  float2 cs[kRotUnits][8];
+  int64_t offo[kRotUnits];
 #pragma unroll
-  for (int x = 0; x < NU; ++x) {
-    const int u = threadIdx.x + 256 * x;
-    if (u < n) {
-      const int row = u / UPR, j0 = (u % UPR) * 8, pos = r0 + row;
-      const int64_t off = bin + (int64_t)pos * a.ld_in + j0;
+  for (int x = 0; x < kRotUnits; ++x) {
+    const int64_t u = u0 + 256 * x;
+    if (u < total) {
+      const int64_t t = u / upt;
+      const int rest = (int)(u - t * upt);
+      const int h = rest / UPR, j0 = (rest % UPR) * 8;
+      const int64_t off = t * a.ld_in + h * D + j0;
+      offo[x] = t * a.ld_out + h * D + j0;
       ql[x] = ld16(a.q + off);
       qh[x] = ld16(a.q + off + D / 2);
       kl[x] = ld16(a.k + off);
       kh[x] = ld16(a.k + off + D / 2);
-      if (ROPE) load_cs8(a.rope, pos * (D / 2) + j0, cs[x]);
+      if (ROPE) {
+        const int p = min(max(a.pos[t], 0), a.max_pos);
+        load_cs8(a.rope, (int64_t)p * (D / 2) + j0, cs[x]);
+      }
     }
   }
 #pragma unroll
-  for (int x = 0; x < NU; ++x) {
-    const int u = threadIdx.x + 256 * x;
-    if (u < n) {
-      const int row = u / UPR, j0 = (u % UPR) * 8, pos = r0 + row;
-      const int64_t off = bout + (int64_t)pos * a.ld_out + j0;
+  for (int x = 0; x < kRotUnits; ++x) {
+    const int64_t u = u0 + 256 * x;
+    if (u < total) {
       u32x4 q0 = ql[x], q1 = qh[x], k0 = kl[x], k1 = kh[x];
       if (ROPE) {
         float lo[8], hi[8];
@@ -70,10 +71,10 @@ __global__ __launch_bounds__(256) void rotate_kernel(RotArgs a) {
         k0 = pack8(lo);
         k1 = pack8(hi);
       }
-      st16(a.q_rot + off, q0);
-      st16(a.q_rot + off + D / 2, q1);
-      st16(a.k_rot + off, k0);
-      st16(a.k_rot + off + D / 2, k1);
+      st16(a.q_rot + offo[x], q0);
+      st16(a.q_rot + offo[x] + D / 2, q1);
+      st16(a.k_rot + offo[x], k0);
+      st16(a.k_rot + offo[x] + D / 2, k1);
     }
   }
 }
@@ -137,8 +138,10 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(RotArgs a) {
 }
 
 template <int D>
-static hipError_t launch_rotate_d(bool rope, const RotArgs& a, int64_t n_slots, hipStream_t st) {
-  const dim3 grid((unsigned)n_slots, kRotSplit);
+static hipError_t launch_rotate_d(bool rope, const RotArgs& a, hipStream_t st) {
+  const int64_t units = (int64_t)a.T * a.H * (D / 16);
+  const unsigned grid = (unsigned)((units + 256 * kRotUnits - 1) / (256 * kRotUnits));
+  if (grid == 0) return hipSuccess;
   if (rope)
     rotate_kernel<D, true><<<grid, 256, 0, st>>>(a);
   else
@@ -146,13 +149,12 @@ static hipError_t launch_rotate_d(bool rope, const RotArgs& a, int64_t n_slots, 
   return hipGetLastError();
 }
 
-hipError_t launch_rotate(int head_dim, bool rope, const RotArgs& a, int64_t n_slots,
-                         hipStream_t stream) {
+hipError_t launch_rotate(int head_dim, bool rope, const RotArgs& a, hipStream_t stream) {
   switch (head_dim) {
-    case 16: return launch_rotate_d<16>(rope, a, n_slots, stream);
-    case 32: return launch_rotate_d<32>(rope, a, n_slots, stream);
-    case 64: return launch_rotate_d<64>(rope, a, n_slots, stream);
-    case 128: return launch_rotate_d<128>(rope, a, n_slots, stream);
+    case 16: return launch_rotate_d<16>(rope, a, stream);
+    case 32: return launch_rotate_d<32>(rope, a, stream);
+    case 64: return launch_rotate_d<64>(rope, a, stream);
+    case 128: return launch_rotate_d<128>(rope, a, stream);
     default: return hipErrorInvalidValue;
   }
 }
