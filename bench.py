@@ -8,13 +8,16 @@ The default workload is the ESM-2-650M-shaped dense batch: 16 sequences of
 1024 tokens, 20 heads, head dim 64, bf16, RoPE base 10000.
 
 Prints ONE JSON line. `value` is counted TFLOP/s of forward + backward
-(forward 4*sum(L^2)*H*d, backward 2.5x that) over the wall clock of the
-timed steps; `kernels_us` are per-call times from events recorded around
-each call inside the timed steps, on the stream the kernels are launched on;
-`roofline` describes the dominant kernel with that average launch time;
-`cpu_baseline` times the float64 oracle on a bounded sample on the host.
+(forward 4*sum(L^2)*H*d, backward 2.5x that) over the wall clock of the K
+timed steps, which run with nothing recorded between the calls;
+`kernels_us` are per-call times from events recorded around each call in a
+second pass of K steps, on the stream the kernels are launched on (event
+records add idle gaps between the kernels, so that pass's step time,
+`ms_per_step_with_events`, is longer); `roofline` describes the dominant
+kernel with its average launch time from that pass; `cpu_baseline` times
+the float64 oracle on a bounded sample on the host.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload esm2_650m]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 100] [--workload esm2_650m]
                     [--no-cpu-baseline] [--cpu-seconds 15]
 
 `--attention-block` times instead the whole attention block of one layer at
@@ -60,8 +63,10 @@ PEAK_HBM_GBS = 8000.0
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    # the chip's clocks ramp for the first ~40 steps of sustained load (0.64
+    # ms/step, then 0.46 at the 650M shape): the default warmup covers that
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--workload", default="esm2_650m")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -560,14 +565,24 @@ def main():
         step()
     torch.cuda.synchronize()
 
+    # timed region: K steps with nothing recorded between the calls (an event
+    # record is a barrier packet: six per step added ~80 us of idle gaps)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # instrumented pass, K more steps: events around every call give the
+    # per-kernel times (kernels_us) and the dominant kernel's launch time
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
               for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    t1 = time.perf_counter()
     for i in range(args.steps):
         step(events[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    wall_events = time.perf_counter() - t1
 
     per = {n: [] for n in names}
     for ev in events:
@@ -610,6 +625,7 @@ def main():
         "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
         "tokens_per_s": round(T / (step_ms * 1e-3), 1),
         "kernels_us": {n: round(x, 2) for n, x in avg.items()},
+        "ms_per_step_with_events": round(wall_events / args.steps * 1e3, 4),
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
