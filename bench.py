@@ -17,7 +17,7 @@ records add idle gaps between the kernels, so that pass's step time,
 kernel with its average launch time from that pass; `cpu_baseline` times
 the float64 oracle on a bounded sample on the host.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 100] [--workload esm2_650m]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 100] [--workload esm2_650m] [--seed S]
                     [--no-cpu-baseline] [--cpu-seconds 15]
 
 `--attention-block` times instead the whole attention block of one layer at
@@ -68,6 +68,8 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--workload", default="esm2_650m")
+    p.add_argument("--seed", type=int, default=None,
+                   help="input seed (default: the workload's own, which fixes its lengths)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--copy-calibration", action="store_true",
@@ -524,7 +526,8 @@ def main():
     from protein_language_model_amd import workloads as W
 
     dev = torch.device("cuda:0")
-    inp = W.make_inputs(args.workload)
+    seed = W.WORKLOADS[args.workload].seed if args.seed is None else args.seed
+    inp = W.make_inputs(args.workload, seed=seed)
     T, H, d, B = inp["T"], inp["H"], inp["d"], len(inp["lengths"])
     maxL = max(inp["lengths"])
     scale, base = inp["scale"], inp["rope_base"]
@@ -620,7 +623,7 @@ def main():
         "data": "synthetic (seeded N(0,1) bf16 activations, packed varlen batch)",
         "config": {"workload": "%s: %d sequences, %d tokens, H=%d, d=%d, RoPE base %g"
                                % (inp["name"], B, T, H, d, base),
-                   "global_batch": B, "seq_len": maxL, "tokens": T,
+                   "global_batch": B, "seq_len": maxL, "tokens": T, "seed": seed,
                    "parallelism": "single GPU"},
         "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
         "tokens_per_s": round(T / (step_ms * 1e-3), 1),

@@ -41,8 +41,9 @@
  *   starts of consecutive tokens' rows; H*d for the packed layout above): a
  *   fused projection's output [T][3][H][d] is used in place as q, k, v with
  *   stride 3*H*d, and dq, dk, dv can be written into one [T][3][H][d]
- *   gradient the same way. A stride must be >= H*d, a multiple of 8, and
- *   total_tokens * stride < 2^31 (else ESM_ATTN_ERR_UNSUPPORTED).
+ *   gradient the same way. A stride must be >= H*d and a multiple of 8
+ *   (else ESM_ATTN_ERR_INVALID_ARGUMENT), and total_tokens * stride < 2^31
+ *   (else ESM_ATTN_ERR_UNSUPPORTED).
  *
  * Ownership and execution
  *   The caller allocates every buffer (inputs, outputs, workspace); the library
@@ -56,12 +57,16 @@
  *
  * Errors
  *   Problems visible on the host are reported before anything is enqueued and
- *   leave every output untouched: null pointers (allowed when total_tokens is
- *   0), pointers not 16-byte aligned, batch < 1, num_heads < 1,
- *   total_tokens < 0, max_seqlen < 0 or > 65536, head_dim not in
- *   {16, 32, 64, 128} (ESM_ATTN_ERR_UNSUPPORTED), total_tokens*num_heads*
- *   head_dim >= 2^31 (ESM_ATTN_ERR_UNSUPPORTED), non-finite softmax_scale,
- *   rope_base negative or non-finite, workspace smaller than the matching
+ *   leave every output untouched. ESM_ATTN_ERR_INVALID_ARGUMENT: null
+ *   pointers (allowed when total_tokens is 0), pointers not 16-byte aligned,
+ *   batch < 1, num_heads < 1, total_tokens < 0, max_seqlen < 0,
+ *   softmax_scale non-finite or with |softmax_scale| * log2(e) beyond the
+ *   fp32 range, rope_base negative or non-finite. The scores
+ *   softmax_scale * (q~ . k~) must themselves lie in the fp32 range (the
+ *   kernels compute them in fp32).
+ *   ESM_ATTN_ERR_UNSUPPORTED: max_seqlen > 65536, head_dim not in
+ *   {16, 32, 64, 128}, total_tokens*num_heads*head_dim >= 2^31.
+ *   ESM_ATTN_ERR_WORKSPACE_TOO_SMALL: workspace smaller than the matching
  *   *_workspace_bytes() result. A failed kernel launch returns
  *   ESM_ATTN_ERR_HIP. Faults during execution surface at the caller's next
  *   synchronisation, as for any HIP work.
@@ -245,7 +250,9 @@ esm_attn_status_t esm_attn_quantize_fp8_planned(
 
 /* Forward on E4M3 q8, k8 (packed, from esm_attn_quantize_fp8_planned with the
  * same scales) and bf16 v (row stride v_row_stride): S = softmax_scale *
- * q_scale * k_scale * (q8 . k8); o and lse as esm_attn_fwd_planned. */
+ * q_scale * k_scale * (q8 . k8); o and lse as esm_attn_fwd_planned.
+ * ESM_ATTN_ERR_INVALID_ARGUMENT also if |softmax_scale| * q_scale * k_scale *
+ * log2(e) is not a finite fp32 value. */
 esm_attn_status_t esm_attn_fwd_fp8_planned(
     const uint8_t* q8, const uint8_t* k8, const uint16_t* v, int32_t v_row_stride,
     int32_t batch, int32_t total_tokens, int32_t max_seqlen,

@@ -3,7 +3,8 @@
     python -m protein_language_model_amd.build [--verbose]
 
 Each .hip source is compiled to an object in parallel under _build/, then
-linked into protein_language_model_amd/libesm_attn.so. Packed-fp32 VALU
+linked into protein_language_model_amd/libesm_attn.so; warnings are errors
+(-Wall -Wextra -Werror). Packed-fp32 VALU
 instructions are disabled for all device code (-packed-fp32-ops); the host
 pass of hipcc warns that it does not know that feature, which is harmless.
 """
@@ -33,8 +34,8 @@ def hipcc():
 
 
 def compile_flags():
-    return ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
-            "-Wno-unused-function", "-Xclang", "-target-feature", "-Xclang",
+    return ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra",
+            "-Werror", "-Wno-unused-function", "-Xclang", "-target-feature", "-Xclang",
             "-packed-fp32-ops", "-I", INCLUDE, "-I", CSRC]
 
 

@@ -85,7 +85,8 @@ esm_attn_status_t check_stride(int32_t ld, int32_t T, int32_t H, int32_t d) {
 }
 
 esm_attn_status_t check_scalars(float scale, float rope_base) {
-  if (!isfinite(scale)) return ESM_ATTN_ERR_INVALID_ARGUMENT;
+  // the kernels work with |scale| * log2(e), which must stay finite too
+  if (!isfinite(scale) || !isfinite(fabsf(scale) * kLog2e)) return ESM_ATTN_ERR_INVALID_ARGUMENT;
   if (!isfinite(rope_base) || rope_base < 0.f) return ESM_ATTN_ERR_INVALID_ARGUMENT;
   return ESM_ATTN_OK;
 }
@@ -347,6 +348,8 @@ esm_attn_status_t esm_attn_fwd_fp8_planned(const uint8_t* q8, const uint8_t* k8,
   if (head_dim != 64 && head_dim != 128) return ESM_ATTN_ERR_UNSUPPORTED;
   if ((s = check_scalars(softmax_scale, 0.f)) != ESM_ATTN_OK) return s;
   if ((s = check_fp8_scales(q_scale, k_scale)) != ESM_ATTN_OK) return s;
+  if (!isfinite(fabsf(softmax_scale) * kLog2e * q_scale * k_scale))
+    return ESM_ATTN_ERR_INVALID_ARGUMENT;
   if ((s = check_stride(v_row_stride, total_tokens, num_heads, head_dim)) != ESM_ATTN_OK)
     return s;
   if (total_tokens == 0) return ESM_ATTN_OK;

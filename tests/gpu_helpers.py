@@ -73,6 +73,8 @@ def compare(gpu, inp, seqs=None, heads=None, exact_too=True, scale=None, rope_ba
     oracle (bf16 storage of O alone can err by half an ulp); dq/dk/dv: relative
     Frobenius <= 2e-2. The exact-rotation oracle is always reported; with
     exact_too the literal bounds must also hold against it."""
+    for name, t in gpu.items():   # NaN / Inf scan of every output, compared rows or not
+        assert np.isfinite(t).all(), (label, name)
     q, k, v, do = oracle_inputs(inp)
     cu = inp["cu_seqlens"]
     s = inp["scale"] if scale is None else scale

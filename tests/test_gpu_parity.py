@@ -6,6 +6,7 @@ tiles and ragged tails; the full ESM-2-shaped workloads run at their real
 sizes in the benchmark's launch configuration and are compared on sampled
 (sequence, head) slices that the oracle computes one by one."""
 
+import dataclasses
 import math
 
 import numpy as np
@@ -47,6 +48,18 @@ def test_sharpened_qk_parity(device):
     say("case sharpened", inp["lengths"])
     gpu = run_gpu(inp, device)
     compare(gpu, inp, exact_too=False, label="sharpened")
+
+
+@pytest.mark.parametrize("name,H", [("esm2_650m", 1), ("esm2_15b", 2)])
+def test_overflow_scale_qk_x10(device, name, H):
+    # q and k x10: logits with a spread of hundreds, so exp overflows fp32
+    # unless the running maximum is raised; the forward's lazy rescale takes
+    # its slow path on most key blocks and the softmax is close to one-hot
+    w = dataclasses.replace(W.WORKLOADS[name], qk_scale=10.0)
+    inp = W.make_inputs(w, lengths=[1, 130, 1024, 77, 0, 256], num_heads=H)
+    say("case qk x10", name, inp["lengths"], H, inp["d"])
+    gpu = run_gpu(inp, device)
+    compare(gpu, inp, exact_too=False, label="qk x10 " + name)
 
 
 def test_zero_length_sequences_and_single_tokens(device):
