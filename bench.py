@@ -195,7 +195,7 @@ def attention_block(args):
     wo, bo = rnd(hid, hid, s=hid ** -0.5), rnd(hid, s=0.02)
     cu = torch.from_numpy(W.cu_from_lengths(lengths)).to(dev)
     plan = torch.empty(E.esm_attn_plan_bytes(B, T, maxL, H, d), dtype=torch.uint8, device=dev)
-    drow = torch.empty((2, H, T), dtype=torch.float32, device=dev)
+    drow = E.drow_buffer(H, T, dev)
     dqkv = torch.empty((T, 3 * hid), dtype=torch.bfloat16, device=dev)
     st = torch.cuda.current_stream()
 
@@ -209,10 +209,11 @@ def attention_block(args):
         mark(1)
         if fused:
             q, k, v = qkv[:, 0], qkv[:, 1], qkv[:, 2]
-            E.esm_attn_rotate_planned(q, k, B, maxL, plan, base, q_rot=q, k_rot=k)
+            E.esm_attn_rotate_planned(q, k, B, maxL, plan, base, q_rot=q, k_rot=k,
+                                      softmax_scale=scale)
         else:
             q, k, v = qkv[:, 0].contiguous(), qkv[:, 1].contiguous(), qkv[:, 2].contiguous()
-            q, k = E.esm_attn_rotate_planned(q, k, B, maxL, plan, base)
+            q, k = E.esm_attn_rotate_planned(q, k, B, maxL, plan, base, softmax_scale=scale)
         o, lse = E.esm_attn_fwd_planned(q, k, v, B, maxL, plan, scale)
         mark(2)
         F.linear(o.view(T, hid), wo, bo)
@@ -299,7 +300,7 @@ def packing_study(args):
     outs = {n: torch.empty(cap, H, d, dtype=torch.bfloat16, device=dev)
             for n in ("qr", "kr", "o", "dq", "dk", "dv")}
     lse = torch.empty(H * cap, dtype=torch.float32, device=dev)
-    drow = torch.empty(2 * H * cap, dtype=torch.float32, device=dev)
+    drow = torch.empty(4 * H * cap, dtype=torch.float32, device=dev)  # drow_buffer(H, cap) flat
 
     def prepare(run_lengths):  # device cu_seqlens and plan buffer, before timing
         T, B, maxL = int(sum(run_lengths)), len(run_lengths), int(max(run_lengths))
@@ -314,10 +315,11 @@ def packing_study(args):
         q, k, v, do = (buf[n][:T] for n in ("q", "k", "v", "do"))
         qr, kr, o, dq, dk, dv = (outs[n][:T] for n in ("qr", "kr", "o", "dq", "dk", "dv"))
         E.esm_attn_plan(cu, T, maxL, H, d, base, plan=plan)
-        E.esm_attn_rotate_planned(q, k, B, maxL, plan, base, q_rot=qr, k_rot=kr)
+        E.esm_attn_rotate_planned(q, k, B, maxL, plan, base, q_rot=qr, k_rot=kr,
+                                  softmax_scale=scale)
         E.esm_attn_fwd_planned(qr, kr, v, B, maxL, plan, scale, out=o, lse=lse[:H * T].view(H, T))
         E.esm_attn_bwd_planned(qr, kr, v, o, do, lse[:H * T].view(H, T), B, maxL, plan, scale,
-                               base, dq=dq, dk=dk, dv=dv, drow=drow[:2 * H * T].view(2, H, T))
+                               base, dq=dq, dk=dk, dv=dv, drow=drow[:4 * H * T])
 
     def tiles(L):  # pairs the 128-query x 64-key tiles cover
         return -(-L // 128) * 128 * (-(-L // 64)) * 64
@@ -386,7 +388,8 @@ def split_kv_study(args):
                    for _ in range(3))
         cu = torch.from_numpy(W.cu_from_lengths(lengths)).to(dev)
         plan = E.esm_attn_plan(cu, T, maxL, H, d, W.ROPE_BASE)
-        qr, kr = E.esm_attn_rotate_planned(q, k, B, maxL, plan, W.ROPE_BASE)
+        qr, kr = E.esm_attn_rotate_planned(q, k, B, maxL, plan, W.ROPE_BASE,
+                                           softmax_scale=1.0 / math.sqrt(d))
         o = torch.empty_like(q)
         lse = torch.empty((H, T), dtype=torch.float32, device=dev)
         parts = {R: (torch.empty((R, T, H, d), dtype=torch.float32, device=dev),
@@ -469,7 +472,8 @@ def fp8_study(args):
             return prep, attn
 
         def bf16(mid=None):
-            E.esm_attn_rotate_planned(q, k, B, maxL, plan, W.ROPE_BASE, q_rot=qr, k_rot=kr)
+            E.esm_attn_rotate_planned(q, k, B, maxL, plan, W.ROPE_BASE, q_rot=qr, k_rot=kr,
+                                      softmax_scale=1.0 / math.sqrt(d))
             if mid is not None:
                 mid.record(st)
             E.esm_attn_fwd_planned(qr, kr, v, B, maxL, plan, out=o, lse=lse)
@@ -541,7 +545,7 @@ def main():
     lse = torch.empty((H, T), dtype=torch.float32, device=dev)
     qr, kr = torch.empty_like(q), torch.empty_like(k)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    drow = torch.empty((2, H, T), dtype=torch.float32, device=dev)
+    drow = E.drow_buffer(H, T, dev)
     plan = torch.empty(E.esm_attn_plan_bytes(B, T, maxL, H, d), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     names = ["plan", "rotate", "fwd", "bwd_dq", "bwd_dkv"]
@@ -553,7 +557,8 @@ def main():
         mark(0)
         E.esm_attn_plan(cu, T, maxL, H, d, base, plan=plan)
         mark(1)
-        E.esm_attn_rotate_planned(q, k, B, maxL, plan, base, q_rot=qr, k_rot=kr)
+        E.esm_attn_rotate_planned(q, k, B, maxL, plan, base, q_rot=qr, k_rot=kr,
+                                  softmax_scale=scale)
         mark(2)
         E.esm_attn_fwd_planned(qr, kr, v, B, maxL, plan, scale, out=o, lse=lse)
         mark(3)

@@ -29,7 +29,11 @@
  *   dq_i = R(p_i)^T (softmax_scale * sum_j dS_ij k~_j)
  *   dk_j = R(p_j)^T (softmax_scale * sum_i dS_ij q~_i)
  * q~ and k~ are rounded once to bf16 before the products (they are operands
- * of bf16 matrix instructions); everything else accumulates in fp32.
+ * of bf16 matrix instructions); everything else accumulates in fp32. The
+ * rounded query operand carries the softmax scale in log2 units:
+ * q^ = bf16(fl32(c * fl32(R(p) q))) with c = fl32(softmax_scale * log2(e)),
+ * k^ = bf16(R(p) k), S_ij = ln(2) * (q^_i . k^_j), and dk_j uses
+ * ln(2) * sum_i dS_ij q^_i.
  *
  * Layouts
  *   q, k, v, o, d_o, dq, dk, dv : bf16 bit patterns (uint16_t), [T][H][d],
@@ -89,7 +93,7 @@
 extern "C" {
 #endif
 
-#define ESM_ATTN_ABI_VERSION 3
+#define ESM_ATTN_ABI_VERSION 4
 
 typedef int32_t esm_attn_status_t;
 #define ESM_ATTN_OK 0
@@ -107,8 +111,9 @@ const char* esm_attn_status_string(esm_attn_status_t status);
 /* Workspace bytes that esm_attn_fwd / esm_attn_bwd need for these sizes
  * (a pure host computation; 0 for arguments the calls would reject). The
  * workspace holds the plan (rotary cos/sin table and work-item schedule), the
- * rotated q~ and k~ (bf16 [T][H][d] each) and, for the backward, drow
- * (fp32 [2][H][T]: the row sums D = rowsum(dO * O), then LSE * log2(e)). */
+ * rotated q^ and k^ (bf16 [T][H][d] each) and, for the backward, drow
+ * ([2][H][T] entries of 8 bytes: the row sums D = rowsum(dO * O), then
+ * LSE * log2(e)). */
 size_t esm_attn_fwd_workspace_bytes(int32_t batch, int32_t total_tokens,
                                     int32_t max_seqlen, int32_t num_heads,
                                     int32_t head_dim);
@@ -147,13 +152,13 @@ esm_attn_status_t esm_attn_bwd(
  * esm_attn_fwd and esm_attn_bwd each run three steps on their workspace:
  *   1. plan   : the work-item schedule for cu_seqlens and the rotary cos/sin
  *               table (esm_attn_plan);
- *   2. rotate : q~ = bf16(R(p) q) and k~ = bf16(R(p) k), once per token
- *               (esm_attn_rotate_planned; skipped when rope_base = 0, where
- *               q~ = q and k~ = k);
- *   3. the attention kernels on q~, k~ (esm_attn_fwd_planned,
- *      esm_attn_bwd_planned).
+ *   2. rotate : q^ = bf16(c R(p) q) and k^ = bf16(R(p) k), once per token
+ *               (esm_attn_rotate_planned; c = softmax_scale log2(e); with
+ *               rope_base = 0, R(p) is the identity);
+ *   3. the attention kernels on q^, k^ (esm_attn_fwd_planned,
+ *      esm_attn_bwd_planned), given the same softmax_scale.
  * A caller that runs the forward and backward of one batch can run steps 1
- * and 2 once and keep q~ and k~ (instead of q and k) for the backward. The
+ * and 2 once and keep q^ and k^ (instead of q and k) for the backward. The
  * plan depends only on cu_seqlens, the sizes and rope_base, so one plan
  * serves every layer of a model for that batch (the rotary table is shared
  * across layers); a fused layer rotates q and k in place inside its
@@ -175,10 +180,16 @@ esm_attn_status_t esm_attn_plan(const int32_t* cu_seqlens, int32_t batch,
 
 /* Rotary embedding of q and k (RoFormer's rotation with x_j paired with
  * x_{j+d/2}, angles p * rope_base^(-2j/d) from the plan's table): every
- * element pair is turned in float32 (products and sums rounded one by one) and
- * rounded once to bf16, round to nearest even. Reads q and k with token row
+ * element pair is turned in float32 (products and sums rounded one by one);
+ * k_rot = bf16(R(p) k) and q_rot = bf16(fl32(c * fl32(R(p) q))) with
+ * c = fl32(softmax_scale * log2(e)), each rounded once to bf16, round to
+ * nearest even (the attention kernels then exponentiate q_rot . k_rot
+ * directly). softmax_scale must be the one later given to the forward and
+ * backward on these operands (a different one gives wrong values, not an
+ * error); it must be finite with a finite c. Reads q and k with token row
  * stride in_row_stride and writes q_rot and k_rot, bf16, with stride
- * out_row_stride; with rope_base = 0 it copies. In place is allowed:
+ * out_row_stride; with rope_base = 0, R(p) is the identity. In place is
+ * allowed:
  * q_rot == q and k_rot == k with equal strides (a fused layer rotates q and
  * k inside its [T][3][H][d] projection output); q_rot == q without
  * k_rot == k, or in place with different strides, is
@@ -186,14 +197,14 @@ esm_attn_status_t esm_attn_plan(const int32_t* cu_seqlens, int32_t batch,
 esm_attn_status_t esm_attn_rotate_planned(
     const uint16_t* q, const uint16_t* k, int32_t in_row_stride,
     int32_t batch, int32_t total_tokens, int32_t max_seqlen,
-    int32_t num_heads, int32_t head_dim, float rope_base,
+    int32_t num_heads, int32_t head_dim, float softmax_scale, float rope_base,
     uint16_t* q_rot, uint16_t* k_rot, int32_t out_row_stride,
     const void* plan, size_t plan_bytes, void* stream);
 
 /* Forward on rotated operands: q_rot and k_rot as esm_attn_rotate_planned
- * wrote them (or q and k themselves without rotary embedding), and v, all
- * with token row stride qkv_row_stride (they may interleave in one fused
- * buffer). Writes o ([T][H][d], packed) and lse as esm_attn_fwd does. */
+ * wrote them with this softmax_scale, and v, all with token row stride
+ * qkv_row_stride (they may interleave in one fused buffer). Writes o
+ * ([T][H][d], packed) and lse as esm_attn_fwd does. */
 esm_attn_status_t esm_attn_fwd_planned(
     const uint16_t* q_rot, const uint16_t* k_rot, const uint16_t* v,
     int32_t qkv_row_stride,
@@ -278,8 +289,10 @@ esm_attn_status_t esm_attn_merge_partials(
  * with respect to the pre-rotation q and k: the kernels apply R(p)^T, for
  * which they need rope_base. dq, dk, dv are written with token row stride
  * grad_row_stride (they may interleave in one [T][3][H][d] gradient; they
- * must not overlap any input). drow: caller-provided
- * fp32 [2][H][T] buffer (D = rowsum(dO * O), then LSE * log2(e)). passes is a
+ * must not overlap any input). softmax_scale: the one q_rot was made with.
+ * drow: caller-provided device buffer of 16 * H * T bytes, 16-byte aligned
+ * ([2][H][T] entries of 8 bytes: D = rowsum(dO * O), then LSE * log2(e),
+ * each as fp32 or as its three-way bf16 split, by head_dim). passes is a
  * bit mask: ESM_ATTN_PASS_DQ runs the dq pass (reads o and lse, writes dq and
  * drow), ESM_ATTN_PASS_DKV the dk/dv pass (reads drow, writes dk and dv);
  * both bits give the full backward. Running the dk/dv pass alone requires a

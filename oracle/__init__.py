@@ -17,6 +17,7 @@ from .attention import (  # noqa: F401
     rope_frequencies,
     rope_rotate,
     rope_rotate_f32,
+    query_operand_bf16,
     attention_forward_slice,
     attention_forward_partial_slice,
     merge_partials,

@@ -25,15 +25,21 @@ Sources and readings
   position embedding (Su et al. 2021, RoFormer) in the half-split pairing,
   frequencies theta_j = base^(-2j/d), positions counted from 0 at the start
   of each sequence.
-* Precision model ("mode"): "exact" keeps the rotated q and k in float64.
-  "bf16_operands" rounds the rotated q and k to bf16 (round-to-nearest-even),
-  as any kernel that feeds bf16 matrix units must. That rounding is a
-  quantisation decided by floating point, so it is taken in the pages'
-  arithmetic precision, float32 (BF16 storage with FP32 arithmetic): cos and
-  sin are rounded to float32 and x c - y s, y c + x s are evaluated in float32
-  with every product and sum rounded (no fused multiply-add), then rounded
-  to bf16. Gradients pass straight through that rounding. Everything else is
-  float64 in both modes.
+* Precision model ("mode"): "exact" keeps the rotated q and k in float64,
+  S = scale * (q~ . k~). "bf16_operands" models a kernel that feeds bf16
+  matrix units and exponentiates with exp2: its operands are
+    k^ = bf16(R(p) k),  q^ = bf16(fl32(c * fl32(R(p) q))),
+    c = fl32(fl32(scale) * fl32(log2 e)),
+  rounded to nearest even, and S = ln(2) * (q^ . k^) (the softmax scale and
+  log2 e ride on the query operand). Those roundings are quantisations
+  decided by floating point, so they are taken in the pages' arithmetic
+  precision, float32 (BF16 storage with FP32 arithmetic): cos and sin are
+  rounded to float32 and x c - y s, y c + x s are evaluated in float32 with
+  every product and sum rounded (no fused multiply-add), the product with c
+  is rounded to float32, then each operand is rounded to bf16. Gradients
+  pass straight through the roundings: dq~ = scale * dS k^ and
+  dk~ = dS^T (ln(2) q^), which is scale * dS^T q~ in exact arithmetic.
+  Everything else is float64 in both modes.
 """
 
 import numpy as np
@@ -141,17 +147,30 @@ def rope_rotate_f32(x, positions, base):
     return out.astype(np.float64)
 
 
-def _rotated_operands(q, k, base, mode):
+LOG2E_F32 = np.float32(np.log2(np.e))
+
+
+def query_operand_bf16(q, pos, base, scale):
+    """q^ = bf16(fl32(c * fl32(R(p) q))), c = fl32(fl32(scale) * fl32(log2 e)):
+    the bf16 query operand of the bf16_operands mode (float64 values)."""
+    c = np.float32(scale) * LOG2E_F32
+    rot = rope_rotate_f32(q, pos, base).astype(np.float32)
+    return round_to_bf16((rot * c).astype(np.float64))
+
+
+def _operands(q, k, base, scale, mode):
+    """(positions, scaled query operand qs, key operand kr), S = qs @ kr^T:
+    exact: qs = scale * R(p) q; bf16_operands: qs = ln(2) * q^."""
     if mode not in MODES:
         raise ValueError("mode must be one of %r" % (MODES,))
     pos = np.arange(q.shape[0], dtype=np.float64)  # 0-based per sequence
     if mode == "bf16_operands":
-        qr = round_to_bf16(rope_rotate_f32(q, pos, base))
+        qs = np.log(2.0) * query_operand_bf16(q, pos, base, scale)
         kr = round_to_bf16(rope_rotate_f32(k, pos, base))
     else:
-        qr = rope_rotate(q, pos, base)
+        qs = float(scale) * rope_rotate(q, pos, base)
         kr = rope_rotate(k, pos, base)
-    return pos, qr, kr
+    return pos, qs, kr
 
 
 # --------------------------------------------------------------------------
@@ -173,8 +192,8 @@ def attention_forward_slice(q, k, v, scale, base, mode="bf16_operands"):
     L = q.shape[0]
     if L == 0:
         return np.zeros_like(v), np.zeros((0,), np.float64)
-    _, qr, kr = _rotated_operands(q, k, base, mode)
-    S = float(scale) * (qr @ kr.T)
+    _, qs, kr = _operands(q, k, base, scale, mode)
+    S = qs @ kr.T
     m = S.max(axis=1)
     lse = m + np.log(np.exp(S - m[:, None]).sum(axis=1))
     P = np.exp(S - lse[:, None])
@@ -200,8 +219,8 @@ def attention_forward_partial_slice(q, k, v, scale, base, key_lo, key_hi,
     L = q.shape[0]
     if L == 0 or key_hi <= key_lo:
         return np.zeros((L, v.shape[1])), np.full((L,), -np.inf)
-    _, qr, kr = _rotated_operands(q, k, base, mode)
-    S = float(scale) * (qr @ kr[key_lo:key_hi].T)
+    _, qs, kr = _operands(q, k, base, scale, mode)
+    S = qs @ kr[key_lo:key_hi].T
     m = S.max(axis=1)
     lse = m + np.log(np.exp(S - m[:, None]).sum(axis=1))
     P = np.exp(S - lse[:, None])
@@ -235,10 +254,11 @@ def attention_backward_slice(q, k, v, do, scale, base, mode="bf16_operands",
       D_i   = sum_j P_ij dP_ij
       dS_ij = P_ij (dP_ij - D_i)
       dq~_i = scale * sum_j dS_ij k~_j
-      dk~_j = scale * sum_i dS_ij q~_i
+      dk~_j = scale * sum_i dS_ij q~_i   (sum_i dS_ij qs_i, qs the scaled
+                                          query operand of the mode)
       dq_i  = R(-p_i) dq~_i,   dk_j = R(-p_j) dk~_j
     Returns (dq, dk, dv), each [L, d]; with return_intermediates also a dict
-    of P, dS, D, LSE and the rotated-space gradients."""
+    of P, dS, D, LSE, the rotated-space gradients and the operands."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
@@ -248,9 +268,9 @@ def attention_backward_slice(q, k, v, do, scale, base, mode="bf16_operands",
         z = np.zeros_like(q)
         out = (z, z.copy(), z.copy())
         return out + ({},) if return_intermediates else out
-    pos, qr, kr = _rotated_operands(q, k, base, mode)
+    pos, qs, kr = _operands(q, k, base, scale, mode)
     s = float(scale)
-    S = s * (qr @ kr.T)
+    S = qs @ kr.T
     m = S.max(axis=1)
     lse = m + np.log(np.exp(S - m[:, None]).sum(axis=1))
     P = np.exp(S - lse[:, None])
@@ -259,12 +279,12 @@ def attention_backward_slice(q, k, v, do, scale, base, mode="bf16_operands",
     D = (P * dP).sum(axis=1)
     dS = P * (dP - D[:, None])
     dqr = s * (dS @ kr)
-    dkr = s * (dS.T @ qr)
+    dkr = dS.T @ qs
     dq = rope_rotate(dqr, pos, base, inverse=True)
     dk = rope_rotate(dkr, pos, base, inverse=True)
     if return_intermediates:
         return dq, dk, dv, dict(P=P, dS=dS, D=D, LSE=lse, dq_rot=dqr,
-                                dk_rot=dkr, q_rot=qr, k_rot=kr)
+                                dk_rot=dkr, q_scaled=qs, k_rot=kr)
     return dq, dk, dv
 
 
@@ -278,9 +298,9 @@ def attention_rows_slice(q, k, v, do, scale, base, rows, mode="bf16_operands"):
     v = np.asarray(v, np.float64)
     do = np.asarray(do, np.float64)
     rows = np.asarray(rows, dtype=np.int64)
-    pos, qr, kr = _rotated_operands(q, k, base, mode)
+    pos, qs, kr = _operands(q, k, base, scale, mode)
     s = float(scale)
-    S = s * (qr[rows] @ kr.T)
+    S = qs[rows] @ kr.T
     m = S.max(axis=1)
     lse = m + np.log(np.exp(S - m[:, None]).sum(axis=1))
     P = np.exp(S - lse[:, None])

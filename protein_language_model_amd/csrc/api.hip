@@ -15,6 +15,7 @@ using namespace esm;
 
 constexpr size_t kAlign = 256;
 constexpr int32_t kMaxSplit = 64;  // key chunks / partials per merge
+constexpr size_t kDrowEntryBytes = 8;  // per row of drow (see bwd.hip)
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
@@ -40,7 +41,8 @@ esm_attn_status_t check_sizes(int32_t B, int32_t T, int32_t maxL, int32_t H, int
 }
 
 // Plan = rotary table + schedule. The one-shot calls append the rotated q~
-// and k~ ([T][H][d] bf16 each) and, for the backward, drow ([2][H][T] fp32).
+// and k~ ([T][H][d] bf16 each) and, for the backward, drow ([2][H][T]
+// entries of 8 bytes: fp32 values, or their three-way bf16 split).
 Layout make_layout(int32_t B, int32_t T, int32_t maxL, int32_t H, int32_t d, bool bwd) {
   Layout l;
   l.n_chunks = (int32_t)schedule_num_chunks(B, H);
@@ -60,7 +62,7 @@ Layout make_layout(int32_t B, int32_t T, int32_t maxL, int32_t H, int32_t d, boo
   const size_t elems = (size_t)T * H * d;
   l.qrot = take(elems * sizeof(uint16_t));
   l.krot = take(elems * sizeof(uint16_t));
-  if (bwd) l.drow = take((size_t)2 * T * H * sizeof(float));
+  if (bwd) l.drow = take((size_t)2 * T * H * kDrowEntryBytes);
   l.total = off;
   return l;
 }
@@ -178,13 +180,14 @@ esm_attn_status_t esm_attn_plan(const int32_t* cu_seqlens, int32_t batch, int32_
 esm_attn_status_t esm_attn_rotate_planned(const uint16_t* q, const uint16_t* k,
                                           int32_t in_row_stride, int32_t batch,
                                           int32_t total_tokens, int32_t max_seqlen,
-                                          int32_t num_heads, int32_t head_dim, float rope_base,
+                                          int32_t num_heads, int32_t head_dim,
+                                          float softmax_scale, float rope_base,
                                           uint16_t* q_rot, uint16_t* k_rot,
                                           int32_t out_row_stride, const void* plan,
                                           size_t plan_bytes, void* stream) {
   esm_attn_status_t s = check_sizes(batch, total_tokens, max_seqlen, num_heads, head_dim);
   if (s != ESM_ATTN_OK) return s;
-  if ((s = check_scalars(0.f, rope_base)) != ESM_ATTN_OK) return s;
+  if ((s = check_scalars(softmax_scale, rope_base)) != ESM_ATTN_OK) return s;
   if ((s = check_stride(in_row_stride, total_tokens, num_heads, head_dim)) != ESM_ATTN_OK ||
       (s = check_stride(out_row_stride, total_tokens, num_heads, head_dim)) != ESM_ATTN_OK)
     return s;
@@ -211,6 +214,7 @@ esm_attn_status_t esm_attn_rotate_planned(const uint16_t* q, const uint16_t* k,
   a.H = num_heads;
   a.T = total_tokens;
   a.max_pos = max_seqlen - 1;
+  a.q_mul = softmax_scale * kLog2e;  // finite (check_scalars)
   if (launch_rotate(head_dim, rope_base != 0.f, a, reinterpret_cast<hipStream_t>(stream)) !=
       hipSuccess)
     return ESM_ATTN_ERR_HIP;
@@ -467,16 +471,17 @@ esm_attn_status_t esm_attn_fwd(const uint16_t* q, const uint16_t* k, const uint1
   char* ws = static_cast<char*>(workspace);
   uint16_t* qr = reinterpret_cast<uint16_t*>(ws + l.qrot);
   uint16_t* kr = reinterpret_cast<uint16_t*>(ws + l.krot);
-  const bool rope = rope_base != 0.f;
   if ((s = esm_attn_plan(cu_seqlens, batch, total_tokens, max_seqlen, num_heads, head_dim,
                          rope_base, ws, l.plan, stream)) != ESM_ATTN_OK)
     return s;
   const int32_t ld = num_heads * head_dim;
-  if (rope && (s = esm_attn_rotate_planned(q, k, ld, batch, total_tokens, max_seqlen, num_heads,
-                                           head_dim, rope_base, qr, kr, ld, ws, l.plan,
-                                           stream)) != ESM_ATTN_OK)
+  // the rotation pass also applies softmax_scale log2(e) to q, so it runs
+  // with the rotary embedding off too
+  if ((s = esm_attn_rotate_planned(q, k, ld, batch, total_tokens, max_seqlen, num_heads,
+                                   head_dim, softmax_scale, rope_base, qr, kr, ld, ws, l.plan,
+                                   stream)) != ESM_ATTN_OK)
     return s;
-  return esm_attn_fwd_planned(rope ? qr : q, rope ? kr : k, v, ld, batch, total_tokens,
+  return esm_attn_fwd_planned(qr, kr, v, ld, batch, total_tokens,
                               max_seqlen, num_heads, head_dim, softmax_scale, o, lse, ws, l.plan,
                               stream);
 }
@@ -501,16 +506,17 @@ esm_attn_status_t esm_attn_bwd(const uint16_t* q, const uint16_t* k, const uint1
   char* ws = static_cast<char*>(workspace);
   uint16_t* qr = reinterpret_cast<uint16_t*>(ws + l.qrot);
   uint16_t* kr = reinterpret_cast<uint16_t*>(ws + l.krot);
-  const bool rope = rope_base != 0.f;
   if ((s = esm_attn_plan(cu_seqlens, batch, total_tokens, max_seqlen, num_heads, head_dim,
                          rope_base, ws, l.plan, stream)) != ESM_ATTN_OK)
     return s;
   const int32_t ld = num_heads * head_dim;
-  if (rope && (s = esm_attn_rotate_planned(q, k, ld, batch, total_tokens, max_seqlen, num_heads,
-                                           head_dim, rope_base, qr, kr, ld, ws, l.plan,
-                                           stream)) != ESM_ATTN_OK)
+  // the rotation pass also applies softmax_scale log2(e) to q, so it runs
+  // with the rotary embedding off too
+  if ((s = esm_attn_rotate_planned(q, k, ld, batch, total_tokens, max_seqlen, num_heads,
+                                   head_dim, softmax_scale, rope_base, qr, kr, ld, ws, l.plan,
+                                   stream)) != ESM_ATTN_OK)
     return s;
-  return esm_attn_bwd_planned(rope ? qr : q, rope ? kr : k, v, ld, o, d_o, lse, batch,
+  return esm_attn_bwd_planned(qr, kr, v, ld, o, d_o, lse, batch,
                               total_tokens, max_seqlen, num_heads, head_dim, softmax_scale,
                               rope_base, dq, dk, dv, ld, reinterpret_cast<float*>(ws + l.drow),
                               ESM_ATTN_PASS_DQ | ESM_ATTN_PASS_DKV, ws, l.plan, stream);

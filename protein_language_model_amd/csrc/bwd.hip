@@ -1,21 +1,28 @@
 // Backward attention kernels for gfx950. P is recomputed from the LSE the
-// forward stored (P = exp2(S c - LSE log2 e)), so no L x L matrix is kept.
+// forward stored, so no L x L matrix is kept. The rotation pass stores q~
+// multiplied by softmax_scale * log2(e), so S' = q~ . k~ is the score in log2
+// units and P = exp2(S' - LSE log2 e).
 //
 // Two deterministic passes, no atomics:
 //   dq pass : one workgroup per 128 queries of a (sequence, head) (lane owns a
 //             query). Prologue computes D = rowsum(dO * O) for its queries and
 //             stores it, with LSE log2 e, for the second pass. Per 64-key
-//             block (32 at d=128): S^T = K~ Q~^T, dP^T = V dO^T,
+//             block (32 at d=128): S'^T = K~ Q~^T, dP^T = V dO^T,
 //             dS = P (dP - D), dQ~^T += K~^T dS^T.
 //             Epilogue: dq = R(-p) (scale dQ~) -> bf16.
-//             dP - D comes out of the dP MFMA itself: one extra k-step
-//             multiplies (1, 1) by (-D_hi, -D_lo) (D split into two bf16
-//             values), which replaces one vector subtraction per score.
 //   dkv pass: one workgroup per 128 keys (lane owns a key). Per 64-query block
-//             (32 at d=128): S = Q~ K~^T, dP = dO V^T, dS = P (dP - D),
-//             dV^T += dO^T P, dK~^T += Q~^T dS. Epilogue: dk = R(-p)(scale dK~),
-//             dv -> bf16. (Here D varies along the lane's 16 rows; an extra
-//             MFMA for dP - D measured slower than the subtraction.)
+//             (32 at d=128): S' = Q~ K~^T, dP = dO V^T, dS = P (dP - D),
+//             dV^T += dO^T P, dK~^T += Q~^T dS. Epilogue:
+//             dk = R(-p)(ln 2 dK~) (q~ carries the scale), dv -> bf16.
+// Folds: S' - LSE log2 e and dP - D come out of the MFMAs themselves. One
+// extra k-step multiplies (1, 1, 1) by the per-row (or per-column) value
+// split into three bf16 values (k-slots 0..2), which replaces one vector
+// FMA or subtraction per score: an MFMA blocks vector issue for fewer cycles
+// than the 16 vector instructions of a 32x32 tile. In the dkv pass the
+// values vary along the lane's 16 rows, so the dq pass stores them already
+// split (8 bytes per row) and the dkv pass reads them from LDS; at d = 128 the
+// dkv pass keeps plain fp32 rows and vector subtractions (the extra operand
+// registers would spill there).
 // q~ and k~ come rotated from the rotation pass. The streamed operands (k~
 // and v in the dq pass; q~, dO, LSE and D in the dkv pass) are copied from
 // global memory into swizzled LDS tiles by global_load_lds, in a ring of
@@ -27,6 +34,14 @@
 #include "tile.h"
 
 namespace esm {
+
+// The dq pass hands the dkv pass D and LSE log2 e per row in drow: split into
+// three bf16 values (8 bytes, -x as in neg_bf16_triple) where the dkv pass
+// folds them into its MFMAs, as fp32 otherwise.
+template <int D>
+constexpr bool drow_split() {
+  return D <= 64;
+}
 
 // =========================================================================
 // dq pass
@@ -89,7 +104,6 @@ __global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(AttnArgs a) 
   // ---- prologue: q~ and dO (B operands), D = dO . O, LSE (log2 units)
   const int qi = q0 + w * 32 + r;  // this lane's query
   const bool qvalid = qi < L;
-  const uint32_t qflip = a.q_sign < 0.f ? 0x80008000u : 0u;
   // Every load reads a clamped row and is issued before any is used (loads
   // under a branch would each be awaited at the branch's end); rows past the
   // end are zeroed afterwards.
@@ -113,20 +127,27 @@ __global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(AttnArgs a) 
     for (int e = 0; e < 8; ++e) dpart = fmaf(fd[e], fo[e], dpart);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      qreg[s][e] = qvalid ? qreg[s][e] ^ qflip : 0u;
+      qreg[s][e] = qvalid ? qreg[s][e] : 0u;
       doreg[s][e] = qvalid ? doreg[s][e] : 0u;
     }
   }
   if (!qvalid) dpart = 0.f;
   const float Dq = dpart + xor32(dpart);
-  // dP - D in one more MFMA k-step: A = (1, 1), B = (-D_hi, -D_lo), in the
-  // k slots of lane half 0.
-  const u32x4 a_one = {g == 0 ? kBf16OnePair : 0u, 0u, 0u, 0u};
-  const u32x4 b_negd = {g == 0 ? neg_bf16_pair(Dq) : 0u, 0u, 0u, 0u};
   const float lse2 = qvalid ? lse_raw * kLog2e : 0.f;
+  // S' - lse2 and dP - D in one more MFMA k-step each: A = (1, 1, 1), B = the
+  // three-way bf16 split of -lse2 or -D, in the k-slots of lane half 0
+  const u32x4 a_one = fold_ones(g);
+  const u32x2 tlse = neg_bf16_triple(lse2), td = neg_bf16_triple(Dq);
+  const u32x4 b_neglse = fold_operand(tlse, g), b_negd = fold_operand(td, g);
   if (qvalid && g == 0) {
-    a.drow[rowidx] = Dq;
-    a.drow[(int64_t)a.H * a.T + rowidx] = lse2;
+    if (drow_split<D>()) {  // split values for the dkv pass's folds
+      u32x2* R = reinterpret_cast<u32x2*>(a.drow);
+      R[rowidx] = td;
+      R[(int64_t)a.H * a.T + rowidx] = tlse;
+    } else {
+      a.drow[rowidx] = Dq;
+      a.drow[(int64_t)a.H * a.T + rowidx] = lse2;
+    }
   }
 
   // blocks 1 .. NSTAGE-2 after the prologue's global loads (see the wait below)
@@ -134,7 +155,6 @@ __global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(AttnArgs a) 
   for (int j = 1; j < C::NSTAGE - 1; ++j)
     if (j < nkb) issue(j, j);
 
-  const float c = a.c;
   const int xk = swz<D>(prow);
   const TrRows<D> kread(lane);  // transposed reads of the k~ tile
   f32x16 dqacc[C::ND];
@@ -163,7 +183,8 @@ __global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(AttnArgs a) 
     u32x4 dsreg[C::NU];
 #pragma unroll
     for (int t = 0; t < C::NT; ++t) {
-      f32x16 sacc = f32x16{}, pacc = f32x16{};
+      f32x16 sacc = mfma32(a_one, b_neglse, f32x16{});  // -lse2, then + S'
+      f32x16 pacc = f32x16{};
       const int rowoff = (32 * t + prow) * D;
 #pragma unroll
       for (int s = 0; s < C::NS; ++s) {
@@ -174,10 +195,7 @@ __global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(AttnArgs a) 
       pacc = mfma32(a_one, b_negd, pacc);  // pacc = dP - D
       float dsv[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = fast_exp2(fmaf(sacc[i], c, -lse2));
-        dsv[i] = p * pacc[i];
-      }
+      for (int i = 0; i < 16; ++i) dsv[i] = fast_exp2(sacc[i]) * pacc[i];
       if (!FULL) {  // keys past the end: dS = 0
 #pragma unroll
         for (int i = 0; i < 16; ++i)
@@ -228,13 +246,14 @@ struct DkvCfg {
   static constexpr int NS = D / 16;
   static constexpr int ND = D >= 32 ? D / 32 : 1;
   static constexpr int NT = BQ / 32;
+  static constexpr bool FOLD = drow_split<D>();  // S' - lse2 and dP - D folded into MFMAs
   static constexpr int TILE = BQ * D;           // q~ tile, then dO tile
-  static constexpr int STAGE = 2 * TILE + 4 * BQ;  // + lse2[BQ], D[BQ] as fp32
+  // + the lse2 and D rows of the block: fp32, or split (8 bytes) with FOLD
+  static constexpr int STAGE = 2 * TILE + (FOLD ? 8 : 4) * BQ;
   static constexpr int NSTAGE = 3;              // LDS ring of query blocks
   static constexpr int EPI = BK * (D + 4) * 2;
   static constexpr int LDS = NSTAGE * STAGE > EPI ? NSTAGE * STAGE : EPI;
   static constexpr int OCC = D == 128 ? 2 : 3;
-  static constexpr bool FOLD_D = D <= 64;          // dP - D folded into an MFMA
   using Loader = TilePair<D, BQ>;
   static constexpr int LOADS = Loader::LOADS_PER_WAVE + 1;  // + a half row of lse2 or D
 };
@@ -259,27 +278,25 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkv_kernel(AttnArgs a
   const uint16_t* __restrict__ dOg = a.dout + (int64_t)it.seq0 * rso + (int64_t)h * D;
   const int64_t row0 = (int64_t)h * a.T + it.seq0;
   // waves 0-1 copy halves of the lse2 row, waves 2-3 halves of the D row
+  constexpr int RW = C::FOLD ? 2 : 1;  // 4-byte words per lse2 / D entry
   const float* __restrict__ Fg =
-      a.drow + (w < 2 ? (int64_t)a.H * a.T : (int64_t)0) + row0;
+      a.drow + RW * ((w < 2 ? (int64_t)a.H * a.T : (int64_t)0) + row0);
 
   // q~, dO, lse2 and D rows of query block qb -> LDS stage `stage`
   const typename C::Loader loader(w, lane);
   auto issue = [&](int qb, int stage) {
     const int q0 = qb * C::BQ, lim = L - q0;
     uint16_t* Qs = lds + stage * C::STAGE;
-    float* Fs = reinterpret_cast<float*>(Qs + 2 * C::TILE) + (w < 2 ? 0 : C::BQ);
+    float* Fs = reinterpret_cast<float*>(Qs + 2 * C::TILE) + (w < 2 ? 0 : RW * C::BQ);
     loader.load(Qg + (int64_t)q0 * rs, rs, dOg + (int64_t)q0 * rso, rso, lim, Qs, Qs + C::TILE,
                 w);
-    load_half_row_f32(Fg + q0, C::BQ, lim, Fs, w & 1);
+    load_half_row_f32(Fg + RW * q0, RW * C::BQ, RW * lim, Fs, w & 1);
   };
   const int nqb = (L + C::BQ - 1) / C::BQ;
   issue(0, 0);
 
-  // ---- prologue: this lane's key k~ and v (B operands). A negative softmax
-  // scale is applied as a sign flip of k~ in S (exact); dK~ then takes the
-  // signed scale.
+  // ---- prologue: this lane's key k~ and v (B operands)
   const int kj = k0 + w * 32 + r;
-  const uint32_t kflip = a.q_sign < 0.f ? 0x80008000u : 0u;
   // (branch-free loads of a clamped row, zeroed past the end: see the dq pass)
   const int kc = min(kj, L - 1);
   u32x4 kreg[C::NS], vreg[C::NS];
@@ -292,7 +309,7 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkv_kernel(AttnArgs a
   for (int s = 0; s < C::NS; ++s)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      kreg[s][e] = kj < L ? kreg[s][e] ^ kflip : 0u;
+      kreg[s][e] = kj < L ? kreg[s][e] : 0u;
       vreg[s][e] = kj < L ? vreg[s][e] : 0u;
     }
 
@@ -301,9 +318,9 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkv_kernel(AttnArgs a
   for (int j = 1; j < C::NSTAGE - 1; ++j)
     if (j < nqb) issue(j, j);
 
-  const float c = a.c;
   const int xq = swz<D>(prow);
   const TrRows<D> tread(lane);  // transposed reads of the q~ and dO tiles
+  const u32x4 b_one = fold_ones(g);
   f32x16 dvacc[C::ND], dkacc[C::ND];
 #pragma unroll
   for (int dt = 0; dt < C::ND; ++dt) {
@@ -337,32 +354,35 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkv_kernel(AttnArgs a
     for (int t = 0; t < C::NT; ++t) {
       f32x16 sacc = f32x16{}, pacc = f32x16{};
       const int rowoff = (32 * t + prow) * D;
+      if (C::FOLD) {  // the A rows (queries 32t + prow) bring -lse2 and -D
+        const u32x2* F8 = reinterpret_cast<const u32x2*>(Fs);
+        sacc = mfma32(fold_operand(F8[32 * t + prow], g), b_one, sacc);
+        pacc = mfma32(fold_operand(F8[C::BQ + 32 * t + prow], g), b_one, pacc);
+      }
 #pragma unroll
       for (int s = 0; s < C::NS; ++s) {
         const int off = rowoff + 8 * ((2 * s + g) ^ xq);
         sacc = mfma32(ld16(Qs + off), kreg[s], sacc);
         pacc = mfma32(ld16(Os + off), vreg[s], pacc);
       }
-      // dP - D on the matrix core (d <= 64; at d = 128 the extra operands
-      // would spill): one more k-step whose A column pair holds -D of the
-      // query row as a bf16 hi + lo split and whose B pair is (1, 1), so
-      // every key column gets -D added in fp32
-      if (C::FOLD_D) {
-        const u32x4 a_negd = {g == 0 ? neg_bf16_pair(Fs[C::BQ + 32 * t + prow]) : 0u, 0u, 0u, 0u};
-        const u32x4 b_one = {g == 0 ? kBf16OnePair : 0u, 0u, 0u, 0u};
-        pacc = mfma32(a_negd, b_one, pacc);
-      }
-      // queries 32t + 16g + i, i = 0..15; P and dS overwrite S and dP
+      // queries 32t + 16g + i, i = 0..15; P and dS overwrite S' and dP
+      if (C::FOLD) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const u32x4 x = ld16(&Fs[32 * t + 16 * g + 4 * j]);
-        u32x4 y = zero4();
-        if (!C::FOLD_D) y = ld16(&Fs[C::BQ + 32 * t + 16 * g + 4 * j]);
+        for (int i = 0; i < 16; ++i) {
+          sacc[i] = fast_exp2(sacc[i]);
+          pacc[i] = sacc[i] * pacc[i];
+        }
+      } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * j + e;
-          sacc[i] = fast_exp2(fmaf(sacc[i], c, -__uint_as_float(x[e])));
-          pacc[i] = sacc[i] * (C::FOLD_D ? pacc[i] : pacc[i] - __uint_as_float(y[e]));
+        for (int j = 0; j < 4; ++j) {
+          const u32x4 x = ld16(&Fs[32 * t + 16 * g + 4 * j]);
+          const u32x4 y = ld16(&Fs[C::BQ + 32 * t + 16 * g + 4 * j]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * j + e;
+            sacc[i] = fast_exp2(sacc[i] - __uint_as_float(x[e]));
+            pacc[i] = sacc[i] * (pacc[i] - __uint_as_float(y[e]));
+          }
         }
       }
       if (!FULL) {  // queries past the end (copies of the last row): P = dS = 0
@@ -400,7 +420,7 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkv_kernel(AttnArgs a
   if (nfull < nqb) block(nfull, Ragged{});
   __syncthreads();  // every wave is done with the tiles
 
-  // ---- epilogue: dk = R(-p) scale dK~, dv
+  // ---- epilogue: dk = R(-p) ln2 dK~ (q~ carries softmax_scale log2 e), dv
   float* F = reinterpret_cast<float*>(lds);
   constexpr int FP = D + 4;
 #pragma unroll
@@ -408,7 +428,7 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkv_kernel(AttnArgs a
     const int d0 = 32 * dt + 16 * g;
     if (d0 < D) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) F[(w * 32 + r) * FP + d0 + i] = dkacc[dt][i] * a.scale;
+      for (int i = 0; i < 16; ++i) F[(w * 32 + r) * FP + d0 + i] = dkacc[dt][i] * kLn2;
     }
   }
   __syncthreads();

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace esm {
 
 // Compile-time flag passed to generic lambdas: selects the full-tile code path
@@ -15,6 +17,8 @@ struct Tag {
 };
 using Full = Tag<true>;
 using Ragged = Tag<false>;
+// Argument meaning "no shift": selects the code path without the subtraction.
+struct NoShift {};
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -162,6 +166,27 @@ __device__ __forceinline__ uint32_t neg_bf16_pair(float x) {
   return pack_bf16(hi, -x - hi);
 }
 constexpr uint32_t kBf16OnePair = 0x3f803f80u;  // (1.0, 1.0) in bf16
+constexpr uint32_t kBf16One = 0x00003f80u;      // (1.0, 0) in bf16
+
+// -x as three bf16 values (hi, mid, lo), hi + mid + lo = -x to about 2^-25
+// relative (each residual is exact in fp32), packed {(hi, mid), (lo, 0)}: in
+// MFMA k-slots 0..2 against (1, 1, 1) (fold_ones()) it subtracts x from
+// every element of an fp32 accumulator row or column.
+__device__ __forceinline__ u32x2 neg_bf16_triple(float x) {
+  const float hi = __uint_as_float(pack_bf16(-x, 0.f) << 16);
+  const float r1 = -x - hi;
+  const float mid = __uint_as_float(pack_bf16(r1, 0.f) << 16);
+  return u32x2{pack_bf16(hi, mid), pack_bf16(r1 - mid, 0.f)};
+}
+
+// MFMA operand of a fold: k-slots 0..2 of lane half 0 hold (1, 1, 1), or the
+// triple t; every other slot is 0.
+__device__ __forceinline__ u32x4 fold_ones(int g) {
+  return u32x4{g == 0 ? kBf16OnePair : 0u, g == 0 ? kBf16One : 0u, 0u, 0u};
+}
+__device__ __forceinline__ u32x4 fold_operand(u32x2 t, int g) {
+  return u32x4{g == 0 ? t[0] : 0u, g == 0 ? t[1] : 0u, 0u, 0u};
+}
 
 // sum += x.lo + x.hi for a packed bf16 pair (v_dot2c_f32_bf16 against (1, 1)).
 __device__ __forceinline__ float add_bf16x2(uint32_t x, float sum) {

@@ -13,19 +13,27 @@
 //   Lane (q, g) of a wave holds the scores of query q against 16 keys per
 //   32-key tile; a row's values are split over lanes q and q + 32.
 //
+// Scores in log2 units: the rotation pass stores q~ already multiplied by
+// softmax_scale * log2(e), so S' = q~ . k~ = S log2(e) and P = exp2(S' - m).
+//
 // Softmax (online, one pass over the keys). The running reference m is the
 // exact row maximum of the first key block. Later blocks are exponentiated
-// against it without computing their maximum: P = exp2(S c - m c), and their
-// sum l_blk is accumulated. Only if some lane's l_blk exceeds 2^16 (a score
-// rose far above m, or exp2 overflowed) does the wave compute the block
-// maximum, raise m, rescale O and l by exp2(m_old - m_new) and redo the
-// block. So every P ever used is at most 2^16, l and O stay far from fp32
-// overflow, and the common block costs one fma, one exp2, one add per score
-// and one conversion per two scores. P is rounded once to bf16 for the MFMA;
-// l sums the fp32 values (summing the bf16 values instead, with dot2, would
-// carry their rounding, up to 2^-8 relative, into the LSE). Keys past the end
-// of the sequence get S = -inf, so P = 0. Epilogue: O = acc / l -> bf16;
-// LSE = (m c + log2 l) ln 2.
+// against it without computing their maximum: P = exp2(S' - m), and their
+// sum l_blk is accumulated. The subtraction of m runs on the matrix core:
+// one more MFMA per 32-key tile multiplies (1, 1, 1) by -m split into three
+// bf16 values (k-slots 0..2), so the accumulator comes out as S' - m and each
+// score costs one exp2, one add and half a conversion on the vector ALU (an
+// MFMA blocks vector issue for fewer cycles than the 16 FMAs it replaces).
+// Only if some lane's l_blk exceeds 2^16 (a score rose far above m, or exp2
+// overflowed) does the wave compute the block maximum, raise m, rescale O
+// and l by exp2(m_old - m_new) and redo the block. So every P ever used is
+// at most 2^16, l and O stay far from fp32 overflow. P is rounded once to
+// bf16 for the MFMA, and l sums exactly those bf16 values (dot2 against
+// (1, 1)), so O is the weighted mean of v under the weights the product
+// used: a dominant key's rounding (up to 2^-8 relative) cancels in O instead
+// of scaling it, and the LSE is the log of that same normaliser, within
+// ln(1 + 2^-8) of the exact one. Keys past the end of the sequence get
+// S' = -inf, so P = 0. Epilogue: O = acc / l -> bf16; LSE = (m + log2 l) ln 2.
 //
 // Tiled attention keeps the L x L matrices on chip (BioNeMo blog, section 2.3
 // describes the idea for another GPU); this kernel is laid out for the 64-wide
@@ -118,11 +126,9 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(AttnArgs a) {
   issue(0, 0);
 
   // queries: B operands (8 d values per k-step); rows past the end are zero.
-  // A negative softmax scale is applied as a sign flip of q~ (exact), so that
-  // scores use |scale|. The loads read a clamped row and are selected away
-  // afterwards: loads under a branch would each be awaited at the branch's
-  // end, one memory round trip per k-step.
-  const uint32_t qflip = a.q_sign < 0.f ? 0x80008000u : 0u;
+  // The loads read a clamped row and are selected away afterwards: loads
+  // under a branch would each be awaited at the branch's end, one memory
+  // round trip per k-step.
   const int qc = min(qi, L - 1);
   u32x4 qreg[C::NS];
 #pragma unroll
@@ -130,17 +136,18 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(AttnArgs a) {
 #pragma unroll
   for (int s = 0; s < C::NS; ++s)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) qreg[s][e] = qi < L ? qreg[s][e] ^ qflip : 0u;
+    for (int e = 0; e < 4; ++e) qreg[s][e] = qi < L ? qreg[s][e] : 0u;
   // Blocks 1 .. NSTAGE-2 are issued after the q~ loads, so that the first
   // wait below (which lets one block's loads stay in flight) covers those.
 #pragma unroll
   for (int j = 1; j < C::NSTAGE - 1; ++j)
     if (j < nkb) issue(j, j);
 
-  const float c = a.c;
   const int xk = swz<D>(prow);  // swizzle of the lane's k~ rows 32t + prow
   const TrRows<D> vread(lane);  // transposed reads of the v tile
-  float m = 0.f, mc = 0.f, l = 0.f;
+  const u32x4 a_one = fold_ones(g);
+  float m = 0.f, l = 0.f;       // m in log2 units
+  u32x4 b_negm = u32x4{0u, 0u, 0u, 0u};  // -m in k-slots 0..2 (0 until block 0 sets m)
   f32x16 oacc[C::ND];
 #pragma unroll
   for (int dt = 0; dt < C::ND; ++dt) oacc[dt] = f32x16{};
@@ -166,14 +173,14 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(AttnArgs a) {
     stage = stage + 1 == C::NSTAGE ? 0 : stage + 1;
     next = next + 1 == C::NSTAGE ? 0 : next + 1;
 
-    // S^T tiles: lane (q = r, g) register i of tile t = key 32t + 16g + i.
-    // Keys past the end of the sequence get S = -inf, so P = 0.
+    // S'^T - m tiles: lane (q = r, g) register i of tile t = key 32t + 16g + i.
+    // Keys past the end of the sequence get -inf, so P = 0.
     const int lim = Lk - kb * C::BN;  // valid keys in this block
     f32x16 sacc[C::NT];
     auto scores = [&]() {
 #pragma unroll
       for (int t = 0; t < C::NT; ++t) {
-        sacc[t] = f32x16{};
+        sacc[t] = mfma32(a_one, b_negm, f32x16{});
         const uint16_t* Kr = Ks + (32 * t + prow) * D;
 #pragma unroll
         for (int s = 0; s < C::NS; ++s)
@@ -195,46 +202,56 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(AttnArgs a) {
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[t][i]);
       return fmaxf(mx, xor32(mx));
     };
-    // P = exp2(S c - m c) in place of S; returns this lane's sum of P
-    auto exponentiate = [&]() {
-      float sum = 0.f;
+    // P = bf16(exp2(acc - shift)) into preg (no subtraction at all on the
+    // common path, NoShift); returns this lane's sum of those bf16 values
+    u32x4 preg[C::NU];
+    auto exponentiate = [&](auto shift) {
+      constexpr bool SHIFT = !std::is_same<decltype(shift), NoShift>::value;
 #pragma unroll
       for (int t = 0; t < C::NT; ++t)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          sacc[t][i] = fast_exp2(fmaf(sacc[t][i], c, -mc));
-          sum += sacc[t][i];
+          float x = sacc[t][i];
+          if constexpr (SHIFT) x -= (float)shift;
+          sacc[t][i] = fast_exp2(x);
         }
+      float sum = 0.f;
+#pragma unroll
+      for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t pp =
+                pack_bf16(sacc[t][8 * hh + 2 * e], sacc[t][8 * hh + 2 * e + 1]);
+            preg[2 * t + hh][e] = pp;
+            sum = add_bf16x2(pp, sum);
+          }
       return sum;
     };
     scores();
-    if (kb == 0) {
+    float lb;
+    if (kb == 0) {  // no reference yet: the accumulator holds S'
       m = block_max();  // block 0 holds key 0, so m is finite
-      mc = m * c;
+      b_negm = fold_operand(neg_bf16_triple(m), g);
+      lb = exponentiate(m);
+    } else {
+      lb = exponentiate(NoShift{});
     }
-    float lb = exponentiate();
     if (wave_any(!(lb <= kLazyBound))) {
-      // rare: recompute S, raise the reference to the new maximum, redo P
+      // rare: recompute S' - m, raise the reference to the new maximum, redo P
       scores();
-      const float mnew = fmaxf(m, block_max());
-      const float alpha = fast_exp2((m - mnew) * c);
-      m = mnew;
-      mc = m * c;
+      const float up = fmaxf(block_max(), 0.f);
+      const float alpha = fast_exp2(-up);
+      m += up;
+      b_negm = fold_operand(neg_bf16_triple(m), g);
       l *= alpha;
 #pragma unroll
       for (int dt = 0; dt < C::ND; ++dt) oacc[dt] *= alpha;
-      lb = exponentiate();
+      lb = exponentiate(up);
     }
     l += lb;
 
-    u32x4 preg[C::NU];
-#pragma unroll
-    for (int t = 0; t < C::NT; ++t)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          preg[2 * t + hh][e] = pack_bf16(sacc[t][8 * hh + 2 * e], sacc[t][8 * hh + 2 * e + 1]);
 #pragma unroll
     for (int dt = 0; dt < C::ND; ++dt) {
       u32x4 av[C::NU];
@@ -266,7 +283,7 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(AttnArgs a) {
       }
       if (g == 0)
         a.lse_part[((int64_t)blockIdx.y * a.H + h) * a.T + it.seq0 + qi] =
-            (mc + __log2f(l)) * kLn2;
+            (m + __log2f(l)) * kLn2;
     }
     return;
   }
@@ -285,7 +302,7 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(AttnArgs a) {
         st16(Og + d0 + 8, pack8(f + 8));
       }
     }
-    if (g == 0) a.lse[(int64_t)h * a.T + it.seq0 + qi] = (mc + __log2f(l)) * kLn2;
+    if (g == 0) a.lse[(int64_t)h * a.T + it.seq0 + qi] = (m + __log2f(l)) * kLn2;
   }
 }
 

@@ -152,15 +152,27 @@ __global__ __launch_bounds__(256, Fp8Cfg<D>::OCC) void fwd_fp8_kernel(AttnArgs a
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[t][i]);
       return fmaxf(mx, xor32(mx));
     };
+    // P = bf16(exp2(S c - m c)) into preg; returns the sum of those bf16
+    // values (l normalises O by the weights its product used, as the bf16
+    // forward does)
+    u32x4 preg[C::NU];
     auto exponentiate = [&]() {
+#pragma unroll
+      for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[t][i] = fast_exp2(fmaf(sacc[t][i], c, -mc));
       float sum = 0.f;
 #pragma unroll
       for (int t = 0; t < C::NT; ++t)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          sacc[t][i] = fast_exp2(fmaf(sacc[t][i], c, -mc));
-          sum += sacc[t][i];
-        }
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t pp =
+                pack_bf16(sacc[t][8 * hh + 2 * e], sacc[t][8 * hh + 2 * e + 1]);
+            preg[2 * t + hh][e] = pp;
+            sum = add_bf16x2(pp, sum);
+          }
       return sum;
     };
     scores();
@@ -181,15 +193,6 @@ __global__ __launch_bounds__(256, Fp8Cfg<D>::OCC) void fwd_fp8_kernel(AttnArgs a
       lb = exponentiate();
     }
     l += lb;
-
-    u32x4 preg[C::NU];
-#pragma unroll
-    for (int t = 0; t < C::NT; ++t)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          preg[2 * t + hh][e] = pack_bf16(sacc[t][8 * hh + 2 * e], sacc[t][8 * hh + 2 * e + 1]);
 #pragma unroll
     for (int dt = 0; dt < C::ND; ++dt) {
       u32x4 av[C::NU];

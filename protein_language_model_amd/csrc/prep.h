@@ -35,6 +35,7 @@ struct RotArgs {
   uint8_t* q8;          // E4M3 quantization: outputs [T][H][d] bytes (packed)
   uint8_t* k8;
   float q_inv, k_inv;   // fl32(1 / scale) of q and k
+  float q_mul;          // fl32(softmax_scale * log2(e)): q~ is stored times this
   const float2* rope;   // [max_seqlen][d/2]
   const int32_t* pos;   // [T] token positions (the plan's)
   const Item* items;

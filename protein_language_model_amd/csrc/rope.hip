@@ -1,13 +1,16 @@
-// Rotary position embedding of q and k, once per token: x~ = bf16(R(p) x).
+// Rotary position embedding of q and k, once per token:
+//   k~ = bf16(R(p) k),   q~ = bf16(fl32(c * fl32(R(p) q))),  c = fl32(scale log2 e).
 // The attention kernels then read q~ and k~ directly (a key block is used by
 // every query block of its sequence, so rotating it inside those kernels
-// would redo the same rotation once per query block).
+// would redo the same rotation once per query block), and q~ . k~ is the
+// score in log2 units, ready for exp2 (the kernels fold the subtraction of
+// the row reference into their MFMAs, so no per-score multiply is left).
 //
 // R(p) turns the pairs (x_j, x_{j+d/2}) by p * theta_j with the float32
 // (cos, sin) table of the plan; products and sums are rounded to float32 one
 // by one (rotate8) and the result is rounded once to bf16 (round to nearest
 // even). Rotary embedding as in RoFormer (Su et al. 2021), with x_j paired
-// with x_{j+d/2}. With no rotary table (rope_base = 0) the kernel copies.
+// with x_{j+d/2}. With no rotary table (rope_base = 0) R is the identity.
 // Every element is read and written by one thread, loads first, so the
 // outputs may be the inputs themselves (rotation in place).
 #include "common.h"
@@ -58,13 +61,19 @@ __global__ __launch_bounds__(256) void rotate_kernel(RotArgs a) {
     const int64_t u = u0 + 256 * x;
     if (u < total) {
       u32x4 q0 = ql[x], q1 = qh[x], k0 = kl[x], k1 = kh[x];
+      float lo[8], hi[8];
+      unpack8(q0, lo);
+      unpack8(q1, hi);
+      if (ROPE) rotate8<false, false>(lo, hi, cs[x]);
+      // q~ = bf16(fl32(q_mul * fl32(R(p) q))): one more fp32 rounding, then one to bf16
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        lo[e] *= a.q_mul;
+        hi[e] *= a.q_mul;
+      }
+      q0 = pack8(lo);
+      q1 = pack8(hi);
       if (ROPE) {
-        float lo[8], hi[8];
-        unpack8(q0, lo);
-        unpack8(q1, hi);
-        rotate8<false, false>(lo, hi, cs[x]);
-        q0 = pack8(lo);
-        q1 = pack8(hi);
         unpack8(k0, lo);
         unpack8(k1, hi);
         rotate8<false, false>(lo, hi, cs[x]);

@@ -96,8 +96,8 @@ def lib():
     L.esm_attn_plan.restype = i32
     L.esm_attn_plan.argtypes = [vp, i32, i32, i32, i32, i32, f32, vp, u64, vp]
     L.esm_attn_rotate_planned.restype = i32
-    L.esm_attn_rotate_planned.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, f32, vp, vp, i32,
-                                          vp, u64, vp]
+    L.esm_attn_rotate_planned.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, f32, f32, vp, vp,
+                                          i32, vp, u64, vp]
     L.esm_attn_fwd_planned.restype = i32
     L.esm_attn_fwd_planned.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp,
                                        u64, vp]
@@ -263,10 +263,12 @@ def esm_attn_plan(cu_seqlens, total_tokens, max_seqlen, num_heads, head_dim,
 
 
 def esm_attn_rotate_planned(q, k, batch, max_seqlen, plan, rope_base=10000.0, q_rot=None,
-                            k_rot=None, stream=None):
-    """q~ = bf16(R(p) q), k~ = bf16(R(p) k) with the plan's rotary table;
-    returns (q_rot, k_rot). q and k may be views of a fused [T, 3, H, d]
-    buffer; q_rot=q, k_rot=k rotates in place."""
+                            k_rot=None, stream=None, *, softmax_scale):
+    """q^ = bf16(c R(p) q) with c = fl32(softmax_scale * log2(e)) and
+    k^ = bf16(R(p) k), with the plan's rotary table; returns (q_rot, k_rot).
+    softmax_scale (keyword, required) must be the one later given to the
+    planned forward and backward on these operands. q and k may be views of a
+    fused [T, 3, H, d] buffer; q_rot=q, k_rot=k rotates in place."""
     T, H, d = q.shape
     ld_in = _row_stride(q, k)
     if q_rot is None:
@@ -275,7 +277,8 @@ def esm_attn_rotate_planned(q, k, batch, max_seqlen, plan, rope_base=10000.0, q_
         k_rot = torch.empty((T, H, d), dtype=k.dtype, device=k.device)
     ld_out = _row_stride(q_rot, k_rot)
     _check(lib().esm_attn_rotate_planned(_ptr(q), _ptr(k), ld_in, int(batch), T,
-                                         int(max_seqlen), H, d, float(rope_base), _ptr(q_rot),
+                                         int(max_seqlen), H, d, float(softmax_scale),
+                                         float(rope_base), _ptr(q_rot),
                                          _ptr(k_rot), ld_out, _ptr(plan), plan.numel(),
                                          _stream(stream)))
     return q_rot, k_rot
@@ -283,9 +286,9 @@ def esm_attn_rotate_planned(q, k, batch, max_seqlen, plan, rope_base=10000.0, q_
 
 def esm_attn_fwd_planned(q_rot, k_rot, v, batch, max_seqlen, plan, softmax_scale=None,
                          out=None, lse=None, stream=None):
-    """Forward on rotated q~, k~ (esm_attn_rotate_planned's outputs) and v,
-    which share one token row stride (e.g. views of a fused [T, 3, H, d]
-    buffer). out: packed [T, H, d]."""
+    """Forward on rotated q^, k^ (esm_attn_rotate_planned's outputs, made
+    with this softmax_scale) and v, which share one token row stride (e.g.
+    views of a fused [T, 3, H, d] buffer). out: packed [T, H, d]."""
     T, H, d = v.shape
     ld = _row_stride(q_rot, k_rot, v)
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
@@ -397,17 +400,18 @@ def esm_attn_fwd_fp8_planned(q8, k8, v, batch, max_seqlen, plan, q_scale, k_scal
 def esm_attn_bwd_planned(q_rot, k_rot, v, o, d_o, lse, batch, max_seqlen, plan,
                          softmax_scale=None, rope_base=10000.0, dq=None, dk=None, dv=None,
                          drow=None, passes=PASS_DQ | PASS_DKV, stream=None):
-    """Backward on rotated q~, k~ (and v, one token row stride, as for the
+    """Backward on rotated q^, k^ (and v, one token row stride, as for the
     forward; o and d_o packed); dq and dk are gradients with respect to the
     pre-rotation q and k. dq, dk, dv share one token row stride (e.g. views
-    of a fused [T, 3, H, d] gradient). drow: fp32 [2, H, T] scratch shared
-    by the passes."""
+    of a fused [T, 3, H, d] gradient). drow: the passes' shared scratch
+    (drow_buffer(H, T, device))."""
     T, H, d = v.shape
     ld = _row_stride(q_rot, k_rot, v)
     _check_packed((T, H, d), d_o, *([o] if passes & PASS_DQ else []))
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     if drow is None:
-        drow = torch.empty((2, H, T), dtype=torch.float32, device=v.device)
+        drow = drow_buffer(H, T, v.device)
+    _check_drow(drow, H, T)
     new = lambda: torch.empty((T, H, d), dtype=v.dtype, device=v.device)
     grads = []
     if passes & PASS_DQ:
@@ -424,6 +428,18 @@ def esm_attn_bwd_planned(q_rot, k_rot, v, o, d_o, lse, batch, max_seqlen, plan,
                                       _ptr(drow), int(passes), _ptr(plan), plan.numel(),
                                       _stream(stream)))
     return dq, dk, dv, drow
+
+
+def drow_buffer(num_heads, total_tokens, device):
+    """Scratch the backward passes share: [2][H][T] entries of 8 bytes (D
+    and LSE log2(e) per row, as fp32 or split into three bf16 values)."""
+    return torch.empty((2, num_heads, total_tokens, 2), dtype=torch.float32, device=device)
+
+
+def _check_drow(drow, H, T):
+    if not (drow.dtype == torch.float32 and drow.is_contiguous() and drow.numel() >= 4 * H * T):
+        raise ValueError("drow must be a contiguous float32 buffer of at least 4*H*T elements "
+                         "(drow_buffer(H, T, device))")
 
 
 def esm_attn_check_cu_seqlens_host(cu, total_tokens, max_seqlen):
@@ -467,7 +483,7 @@ def esm_attn_bucket_batches(lengths, boundaries, budget, padded=False):
 
 
 class _Attention(torch.autograd.Function):
-    """The plan (schedule + rotary table) and the rotated q~, k~ are made once
+    """The plan (schedule + rotary table) and the rotated q^, k^ are made once
     in forward and kept for backward in place of q and k."""
 
     @staticmethod
@@ -475,10 +491,9 @@ class _Attention(torch.autograd.Function):
         T, H, d = _check_qkv(q, k, v)
         B = cu_seqlens.numel() - 1
         plan = esm_attn_plan(cu_seqlens, T, max_seqlen, H, d, rope_base)
-        if rope_base != 0.0:
-            q_rot, k_rot = esm_attn_rotate_planned(q, k, B, max_seqlen, plan, rope_base)
-        else:
-            q_rot, k_rot = q, k
+        # (always: the pass also applies softmax_scale log2(e) to q)
+        q_rot, k_rot = esm_attn_rotate_planned(q, k, B, max_seqlen, plan, rope_base,
+                                               softmax_scale=scale)
         o, lse = esm_attn_fwd_planned(q_rot, k_rot, v, B, max_seqlen, plan, scale)
         ctx.save_for_backward(q_rot, k_rot, v, o, lse, plan)
         ctx.args = (B, max_seqlen, scale, rope_base)
@@ -495,8 +510,9 @@ class _Attention(torch.autograd.Function):
 
 class _AttentionQKV(torch.autograd.Function):
     """Fused layer boundary: q, k, v are views of one projection output
-    qkv [T, 3*H*d]; q and k are rotated in place (the buffer then holds q~,
-    k~, v and is kept for backward in place of any copy), and the backward
+    qkv [T, 3*H*d]; q and k are rotated in place (the buffer then holds q^
+    (scaled by softmax_scale log2(e)), k^, v and is kept for backward in place
+    of any copy), and the backward
     writes dq, dk, dv into one [T, 3*H*d] gradient, the operand of the
     projection's backward GEMMs."""
 
@@ -510,8 +526,8 @@ class _AttentionQKV(torch.autograd.Function):
         B = cu_seqlens.numel() - 1
         if plan is None:
             plan = esm_attn_plan(cu_seqlens, T, max_seqlen, H, d, rope_base)
-        if rope_base != 0.0:
-            esm_attn_rotate_planned(q, k, B, max_seqlen, plan, rope_base, q_rot=q, k_rot=k)
+        esm_attn_rotate_planned(q, k, B, max_seqlen, plan, rope_base, q_rot=q, k_rot=k,
+                                softmax_scale=scale)
         ctx.mark_dirty(qkv)
         o, lse = esm_attn_fwd_planned(q, k, v, B, max_seqlen, plan, scale)
         ctx.save_for_backward(qkv, o, lse, plan)

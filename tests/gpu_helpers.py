@@ -58,7 +58,11 @@ def ulp_bf16(x):
 
 O_ATOL = 1e-2     # max-abs error allowed on O
 G_RELF = 2e-2     # relative Frobenius error allowed on dq, dk, dv
-LSE_ATOL = 2e-3   # max-abs error on LSE (diagnostic bound)
+# max-abs error on LSE (diagnostic; no stated tolerance): the forward's
+# normaliser is the sum of the bf16-rounded probabilities its P V product
+# used, each within 2^-8 relative of exact, so its log is within
+# ln(1 + 2^-8) = 3.9e-3 of the exact LSE; 1e-4 covers the fp32 terms
+LSE_ATOL = math.log1p(2.0 ** -8) + 1e-4
 
 
 def relf(a, b):
@@ -94,7 +98,12 @@ def compare(gpu, inp, seqs=None, heads=None, exact_too=True, scale=None, rope_ba
         report[mode + ".o_maxabs"] = float(err.max()) if err.size else 0.0
         if mode == "bf16_operands":
             bound = O_ATOL + 0.5 * ulp_bf16(orf)
-            assert (err <= bound).all(), (label, mode, float((err - bound).max()))
+            ex = err - bound
+            if ex.size and ex.max() > 0:
+                at = np.unravel_index(int(ex.argmax()), ex.shape)
+                raise AssertionError((label, mode, "excess", float(ex.max()), "at", at,
+                                      "gpu", float(og[at]), "oracle", float(orf[at]),
+                                      "elements over", int((ex > 0).sum()), "of", ex.size))
             lerr = np.abs(gpu["lse"][heads][:, rows] - LSE[heads][:, rows])
             report["lse_maxabs"] = float(lerr.max()) if lerr.size else 0.0
             assert report["lse_maxabs"] <= LSE_ATOL, (label, report)

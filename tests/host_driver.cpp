@@ -236,10 +236,13 @@ static void validation() {
                      esm_attn_fwd_workspace_bytes(1, 8, 8, 1, 64), nullptr) == WS);
   CHECK(esm_attn_plan(cu, 1, 8, 8, 1, 64, 1e4f, p, 16, nullptr) == WS);
   CHECK(esm_attn_plan(cu, 1, 8, 8, 1, 64, nan, p, big, nullptr) == INV);
-  CHECK(esm_attn_rotate_planned(p, p, 63, 1, 8, 8, 1, 64, 1e4f, p, p, 64, p, big, nullptr) == INV);
-  // in place (both outputs on their inputs) needs one stride for both sides
-  CHECK(esm_attn_rotate_planned(p, p + 32, 64, 1, 8, 8, 1, 64, 1e4f, p, p + 32, 72, p, big,
+  CHECK(esm_attn_rotate_planned(p, p, 63, 1, 8, 8, 1, 64, 0.125f, 1e4f, p, p, 64, p, big,
                                 nullptr) == INV);
+  CHECK(esm_attn_rotate_planned(p, p, 64, 1, 8, 8, 1, 64, 3e38f, 1e4f, p, p, 64, p, big,
+                                nullptr) == INV);  // softmax_scale * log2(e) overflows
+  // in place (both outputs on their inputs) needs one stride for both sides
+  CHECK(esm_attn_rotate_planned(p, p + 32, 64, 1, 8, 8, 1, 64, 0.125f, 1e4f, p, p + 32, 72, p,
+                                big, nullptr) == INV);
   CHECK(esm_attn_fwd_planned(p, p, p, 60, 1, 8, 8, 1, 64, 0.1f, p, f, p, big, nullptr) == INV);
   CHECK(esm_attn_fwd_planned(p, p, p, 1 << 20, 1, 1 << 11, 8, 1, 64, 0.1f, p, f, p, big,
                              nullptr) == UNS);  // total_tokens * stride >= 2^31

@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported():
     for n in names:
         assert hasattr(lib, n), n
     assert set(E.EXPORTED) == set(names)
-    assert E.esm_attn_abi_version() == 3
+    assert E.esm_attn_abi_version() == 4
 
 
 def test_single_hip_runtime_is_mapped():
@@ -120,15 +120,15 @@ def test_backward_and_planned_validation():
                                 None)
     assert st == E.ERR_INVALID_ARGUMENT
     # rotation step (q_rot == q and k_rot == k with equal strides: in place)
-    st = L.esm_attn_rotate_planned(p, p, 32, 1, 8, 8, 1, 32, 1e4, p, p, 32, p, 4, None)
+    st = L.esm_attn_rotate_planned(p, p, 32, 1, 8, 8, 1, 32, 0.125, 1e4, p, p, 32, p, 4, None)
     assert st == E.ERR_WORKSPACE_TOO_SMALL
-    st = L.esm_attn_rotate_planned(p, p, 32, 1, 8, 8, 1, 32, -1.0, p, p, 32, p, 1 << 30, None)
+    st = L.esm_attn_rotate_planned(p, p, 32, 1, 8, 8, 1, 32, 0.125, -1.0, p, p, 32, p, 1 << 30, None)
     assert st == E.ERR_INVALID_ARGUMENT
-    st = L.esm_attn_rotate_planned(p, p, 32, 1, 8, 8, 1, 32, 1e4, None, p, 32, p, 1 << 30, None)
+    st = L.esm_attn_rotate_planned(p, p, 32, 1, 8, 8, 1, 32, 0.125, 1e4, None, p, 32, p, 1 << 30, None)
     assert st == E.ERR_INVALID_ARGUMENT
-    st = L.esm_attn_rotate_planned(p, p, 48, 1, 8, 8, 1, 48, 1e4, p, p, 48, p, 1 << 30, None)
+    st = L.esm_attn_rotate_planned(p, p, 48, 1, 8, 8, 1, 48, 0.125, 1e4, p, p, 48, p, 1 << 30, None)
     assert st == E.ERR_UNSUPPORTED
-    assert L.esm_attn_rotate_planned(None, None, 32, 1, 0, 0, 1, 32, 1e4, None, None, 32, None,
+    assert L.esm_attn_rotate_planned(None, None, 32, 1, 0, 0, 1, 32, 0.125, 1e4, None, None, 32, None,
                                      0, None) == E.OK
 
 
@@ -147,7 +147,7 @@ def test_row_stride_validation(call, ld, status):
     L = E.lib()
     p, q, T = 1 << 12, 1 << 13, 8
     if call == "rotate":
-        st = L.esm_attn_rotate_planned(p, p, ld, 1, T, T, 2, 16, 1e4, q, q, 32, p, 1 << 30, None)
+        st = L.esm_attn_rotate_planned(p, p, ld, 1, T, T, 2, 16, 0.125, 1e4, q, q, 32, p, 1 << 30, None)
     elif call == "fwd":
         st = L.esm_attn_fwd_planned(p, p, p, ld, 1, T, T, 2, 16, 0.1, q, q, p, 1 << 30, None)
     else:
@@ -162,13 +162,13 @@ def test_in_place_rotation_rules():
     L = E.lib()
     p, q, r, T = 1 << 12, 1 << 13, 1 << 14, 8
     # q in place, k not
-    assert L.esm_attn_rotate_planned(p, q, 32, 1, T, T, 2, 16, 1e4, p, r, 32, p, 4,
+    assert L.esm_attn_rotate_planned(p, q, 32, 1, T, T, 2, 16, 0.125, 1e4, p, r, 32, p, 4,
                                      None) == E.ERR_INVALID_ARGUMENT
     # in place with different strides
-    assert L.esm_attn_rotate_planned(p, q, 96, 1, T, T, 2, 16, 1e4, p, q, 32, p, 4,
+    assert L.esm_attn_rotate_planned(p, q, 96, 1, T, T, 2, 16, 0.125, 1e4, p, q, 32, p, 4,
                                      None) == E.ERR_INVALID_ARGUMENT
     # in place, one stride: only the (too small) plan is left to reject
-    assert L.esm_attn_rotate_planned(p, q, 96, 1, T, T, 2, 16, 1e4, p, q, 96, p, 4,
+    assert L.esm_attn_rotate_planned(p, q, 96, 1, T, T, 2, 16, 0.125, 1e4, p, q, 96, p, 4,
                                      None) == E.ERR_WORKSPACE_TOO_SMALL
 
 

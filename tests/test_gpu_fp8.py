@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import oracle.fp8 as F8
-from gpu_helpers import say, to_dev, bf16_f64, oracle_inputs, ulp_bf16
+from gpu_helpers import say, to_dev, bf16_f64, oracle_inputs, ulp_bf16, LSE_ATOL
 from protein_language_model_amd import workloads as W
 from protein_language_model_amd import esm_attn as E
 
@@ -81,7 +81,7 @@ def test_fp8_forward_parity(device, d, scale, rope_base):
                                                        base, qs, ks)
             err = np.abs(og[a:e, h] - Oref)
             assert (err <= 1e-2 + 0.5 * ulp_bf16(Oref)).all(), (b, h, float(err.max()))
-            assert np.abs(lg[h, a:e] - lref).max() <= 2e-3
+            assert np.abs(lg[h, a:e] - lref).max() <= LSE_ATOL
             # against the unquantized forward: if quantization moves every
             # logit of a row by at most D, each P changes by a factor within
             # exp(+-2D), so |O - O_exact| <= (exp(2D) - 1) max|v| (plus the

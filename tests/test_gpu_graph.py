@@ -26,7 +26,7 @@ def _buffers(inp, device, n_split):
         qr=bf(), kr=bf(), o=bf(), o2=bf(), dq=bf(), dk=bf(), dv=bf(),
         lse=torch.empty((H, T), dtype=torch.float32, device=device),
         lse2=torch.empty((H, T), dtype=torch.float32, device=device),
-        drow=torch.empty((2, H, T), dtype=torch.float32, device=device),
+        drow=E.drow_buffer(H, T, device),
         op=torch.empty((n_split, T, H, d), dtype=torch.float32, device=device),
         lp=torch.empty((n_split, H, T), dtype=torch.float32, device=device))
 
@@ -37,7 +37,7 @@ def _step(inp, b, n_split):
     s, base = inp["scale"], inp["rope_base"]
     E.esm_attn_plan(b["cu"], T, maxL, H, d, base, plan=b["plan"])
     E.esm_attn_rotate_planned(b["q"], b["k"], B, maxL, b["plan"], base, q_rot=b["qr"],
-                              k_rot=b["kr"])
+                              k_rot=b["kr"], softmax_scale=s)
     E.esm_attn_fwd_planned(b["qr"], b["kr"], b["v"], B, maxL, b["plan"], s, out=b["o"],
                            lse=b["lse"])
     E.esm_attn_bwd_planned(b["qr"], b["kr"], b["v"], b["o"], b["do"], b["lse"], B, maxL,

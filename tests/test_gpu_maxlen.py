@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_helpers import compare, run_gpu, say, oracle_inputs, ulp_bf16
+from gpu_helpers import compare, run_gpu, say, oracle_inputs, ulp_bf16, LSE_ATOL
 from protein_language_model_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -33,7 +33,7 @@ def test_maximum_sequence_length(device, d):
                                              rows)
     og, lg, dqg = gpu["o"][rows, 0], gpu["lse"][0, rows], gpu["dq"][rows, 0]
     assert (np.abs(og - O) <= 1e-2 + 0.5 * ulp_bf16(O)).all(), float(np.abs(og - O).max())
-    assert np.abs(lg - lse).max() <= 2e-3
+    assert np.abs(lg - lse).max() <= LSE_ATOL
     assert np.linalg.norm(dqg - dq) / np.linalg.norm(dq) <= 2e-2
     # identities over all keys of the long sequence (each dv_j, dk_j carries
     # one bf16 rounding, relative 2^-9)

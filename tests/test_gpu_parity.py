@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 from gpu_helpers import compare, run_gpu, say, to_dev, bf16_f64
 from protein_language_model_amd import workloads as W
 from protein_language_model_amd import esm_attn as E
@@ -62,6 +63,34 @@ def test_overflow_scale_qk_x10(device, name, H):
     compare(gpu, inp, exact_too=False, label="qk x10 " + name)
 
 
+@pytest.mark.parametrize("d,scale,base", [(16, None, 10000.0), (64, None, 10000.0),
+                                          (64, -0.2, 10000.0), (64, 0.6, 0.0),
+                                          (128, None, 500.0)])
+def test_rotation_pass_is_bitwise_the_oracle(device, d, scale, base):
+    # q^ = bf16(fl32(c * fl32(R(p) q))), c = fl32(scale * log2 e); k^ = bf16(R(p) k)
+    inp = _case("esm2_650m", lengths=[130, 1, 0, 77], H=3, d=d)
+    s = inp["scale"] if scale is None else scale
+    T, H, B = inp["T"], inp["H"], len(inp["lengths"])
+    maxL = max(inp["lengths"])
+    say("case rotation", d, s, base)
+    q, k = (to_dev(inp[x], device) for x in ("q", "k"))
+    cu = torch.from_numpy(inp["cu_seqlens"]).to(device)
+    plan = E.esm_attn_plan(cu, T, maxL, H, d, base)
+    qr, kr = E.esm_attn_rotate_planned(q, k, B, maxL, plan, base, softmax_scale=s)
+    torch.cuda.synchronize()
+    gq, gk = bf16_f64(qr), bf16_f64(kr)
+    qf, kf = oracle.bf16_bits_to_f64(inp["q"]), oracle.bf16_bits_to_f64(inp["k"])
+    cu_h = inp["cu_seqlens"]
+    for b in range(B):
+        a, e = int(cu_h[b]), int(cu_h[b + 1])
+        pos = np.arange(e - a, dtype=np.float64)
+        for h in range(H):
+            rq = oracle.query_operand_bf16(qf[a:e, h], pos, base, s)
+            rk = oracle.round_to_bf16(oracle.rope_rotate_f32(kf[a:e, h], pos, base))
+            np.testing.assert_array_equal(gq[a:e, h], rq, err_msg="q^ seq %d head %d" % (b, h))
+            np.testing.assert_array_equal(gk[a:e, h], rk, err_msg="k^ seq %d head %d" % (b, h))
+
+
 def test_zero_length_sequences_and_single_tokens(device):
     inp = _case("esm2_650m", lengths=[0, 70, 0, 1, 129, 0, 1], H=2)
     say("case zero-length", inp["lengths"])
@@ -75,7 +104,10 @@ def test_zero_length_sequences_and_single_tokens(device):
         kv = (inp["k"][t].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
         vv = (inp["v"][t].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
         np.testing.assert_array_equal(gpu["o"][t], vv)
-        np.testing.assert_allclose(gpu["lse"][:, t], inp["scale"] * (qv * kv).sum(-1), atol=1e-3)
+        # LSE = scale q.k up to the one bf16 rounding of the scaled query
+        # operand (relative 2^-8 at most per element)
+        tol = 2.0 ** -8 * abs(inp["scale"]) * np.abs(qv * kv).sum(-1) + 1e-5
+        assert (np.abs(gpu["lse"][:, t] - inp["scale"] * (qv * kv).sum(-1)) <= tol).all()
 
 
 @pytest.mark.parametrize("scale,base", [(0.0, 10000.0), (0.125, 0.0), (-0.2, 10000.0),
@@ -184,9 +216,10 @@ def test_planned_path_matches_one_shot(device):
     cu = torch.from_numpy(inp["cu_seqlens"]).to(device)
     ref = run_gpu(inp, device)
     plan = E.esm_attn_plan(cu, T, maxL, H, d, inp["rope_base"])
-    qr, kr = E.esm_attn_rotate_planned(q, k, B, maxL, plan, inp["rope_base"])
+    qr, kr = E.esm_attn_rotate_planned(q, k, B, maxL, plan, inp["rope_base"],
+                                       softmax_scale=inp["scale"])
     o, lse = E.esm_attn_fwd_planned(qr, kr, v, B, maxL, plan, inp["scale"])
-    drow = torch.empty((2, H, T), dtype=torch.float32, device=device)
+    drow = E.drow_buffer(H, T, device)
     dq, _, _, _ = E.esm_attn_bwd_planned(qr, kr, v, o, do, lse, B, maxL, plan, inp["scale"],
                                          inp["rope_base"], drow=drow, passes=E.PASS_DQ)
     _, dk, dv, _ = E.esm_attn_bwd_planned(qr, kr, v, o, do, lse, B, maxL, plan, inp["scale"],
@@ -212,7 +245,8 @@ def test_repeated_calls_on_one_plan(device, d):
     q, k, v, do = (to_dev(inp[x], device) for x in ("q", "k", "v", "do"))
     cu = torch.from_numpy(inp["cu_seqlens"]).to(device)
     plan = E.esm_attn_plan(cu, T, maxL, H, d, inp["rope_base"])
-    qr, kr = E.esm_attn_rotate_planned(q, k, B, maxL, plan, inp["rope_base"])
+    qr, kr = E.esm_attn_rotate_planned(q, k, B, maxL, plan, inp["rope_base"],
+                                       softmax_scale=inp["scale"])
     outs = []
     for _ in range(3):
         o, lse = E.esm_attn_fwd_planned(qr, kr, v, B, maxL, plan, inp["scale"])
@@ -250,7 +284,8 @@ def test_fused_qkv_layout(device, d, pad):
     assert qf.stride(0) == ld
     cu = torch.from_numpy(inp["cu_seqlens"]).to(device)
     plan = E.esm_attn_plan(cu, T, maxL, H, d, base)
-    qr, kr = E.esm_attn_rotate_planned(qf, kf, B, maxL, plan, base, q_rot=qf, k_rot=kf)
+    qr, kr = E.esm_attn_rotate_planned(qf, kf, B, maxL, plan, base, q_rot=qf, k_rot=kf,
+                                       softmax_scale=scale)
     assert qr.data_ptr() == qf.data_ptr() and kr.data_ptr() == kf.data_ptr()
     o, lse = E.esm_attn_fwd_planned(qf, kf, vf, B, maxL, plan, scale)
     gbuf = torch.full((T * ld + 64,), float("nan"), dtype=torch.bfloat16, device=device)
@@ -263,7 +298,7 @@ def test_fused_qkv_layout(device, d, pad):
         np.testing.assert_array_equal(bf16_f64(t), ref[n], err_msg=n)
     np.testing.assert_array_equal(lse.cpu().numpy().astype(np.float64), ref["lse"])
     # the rotated q~, k~ sit in the q and k slots; v and the padding are untouched
-    qr2, kr2 = E.esm_attn_rotate_planned(q, k, B, maxL, plan, base)
+    qr2, kr2 = E.esm_attn_rotate_planned(q, k, B, maxL, plan, base, softmax_scale=scale)
     torch.cuda.synchronize()
     assert torch.equal(qf, qr2) and torch.equal(kf, kr2) and torch.equal(vf, v)
     if pad:

@@ -162,17 +162,26 @@ def test_precision_modes():
     L, d = 30, 16
     bits = lambda x: oracle.round_to_bf16(x)
     q, k, v = bits(_rand(rng, L, d)), bits(_rand(rng, L, d)), _rand(rng, L, d)
-    # without rotation the operands are already bf16 values: modes agree
-    a, _ = oracle.attention_forward_slice(q, k, v, 0.25, 0.0, mode="exact")
-    b, _ = oracle.attention_forward_slice(q, k, v, 0.25, 0.0, mode="bf16_operands")
-    np.testing.assert_array_equal(a, b)
+    # a scale whose c = fl32(scale * fl32(log2 e)) is exactly 1/4: without
+    # rotation c * q is then exact in bf16, so the two modes compute the same
+    # scores up to the float32 rounding of the scale itself (a wrong factor,
+    # log2 e for ln 2, or a dropped scale would show here)
+    s = np.float32(0.25 / np.log2(np.e))
+    while np.float32(s) * np.float32(np.log2(np.e)) != np.float32(0.25):
+        s = np.nextafter(s, np.float32(1.0))
+    a, la = oracle.attention_forward_slice(q, k, v, float(s), 0.0, mode="exact")
+    b, lb = oracle.attention_forward_slice(q, k, v, float(s), 0.0, mode="bf16_operands")
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-6)
+    np.testing.assert_allclose(la, lb, rtol=0, atol=1e-6)
     # with rotation they differ by the rounding of the rotated operands only
     a, _ = oracle.attention_forward_slice(q, k, v, 0.25, BASE, mode="exact")
     b, _ = oracle.attention_forward_slice(q, k, v, 0.25, BASE, mode="bf16_operands")
     assert 0 < np.abs(a - b).max() < 0.05
     *_, it = oracle.attention_backward_slice(q, k, v, v, 0.25, BASE,
                                              return_intermediates=True)
-    np.testing.assert_array_equal(it["q_rot"], oracle.round_to_bf16(it["q_rot"]))
+    qhat = it["q_scaled"] / np.log(2.0)
+    np.testing.assert_allclose(qhat, oracle.round_to_bf16(qhat), rtol=1e-15, atol=0)
+    np.testing.assert_array_equal(it["k_rot"], oracle.round_to_bf16(it["k_rot"]))
     with pytest.raises(ValueError):
         oracle.attention_forward_slice(q, k, v, 0.25, BASE, mode="fp8")
 
