@@ -248,14 +248,8 @@ struct DkvCfg {
   static constexpr int NT = BQ / 32;
   static constexpr bool FOLD = drow_split<D>();  // S' - lse2 and dP - D folded into MFMAs
   static constexpr int TILE = BQ * D;           // q~ tile, then dO tile
-  // With FOLD the D row starts DOFF 8-byte entries after the lse2 row's
-  // start: BQ + 8, so that a lane's two entries (read together, one
-  // ds_read2) sit 64 bytes apart on disjoint banks for every 16-lane group
-  // (BQ entries alone would put them 512 bytes apart, on the same banks);
-  // the region is padded to 2 BQ + 32 entries to keep stages 256-byte aligned.
-  static constexpr int DOFF = FOLD ? BQ + 8 : BQ;
   // + the lse2 and D rows of the block: fp32, or split (8 bytes) with FOLD
-  static constexpr int STAGE = 2 * TILE + (FOLD ? 4 * (2 * BQ + 32) : 4 * BQ);
+  static constexpr int STAGE = 2 * TILE + (FOLD ? 8 : 4) * BQ;
   static constexpr int NSTAGE = 3;              // LDS ring of query blocks
   static constexpr int EPI = BK * (D + 4) * 2;
   static constexpr int LDS = NSTAGE * STAGE > EPI ? NSTAGE * STAGE : EPI;
@@ -293,7 +287,7 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkv_kernel(AttnArgs a
   auto issue = [&](int qb, int stage) {
     const int q0 = qb * C::BQ, lim = L - q0;
     uint16_t* Qs = lds + stage * C::STAGE;
-    float* Fs = reinterpret_cast<float*>(Qs + 2 * C::TILE) + (w < 2 ? 0 : RW * C::DOFF);
+    float* Fs = reinterpret_cast<float*>(Qs + 2 * C::TILE) + (w < 2 ? 0 : RW * C::BQ);
     loader.load(Qg + (int64_t)q0 * rs, rs, dOg + (int64_t)q0 * rso, rso, lim, Qs, Qs + C::TILE,
                 w);
     load_half_row_f32(Fg + RW * q0, RW * C::BQ, RW * lim, Fs, w & 1);
@@ -363,7 +357,7 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkv_kernel(AttnArgs a
       if (C::FOLD) {  // the A rows (queries 32t + prow) bring -lse2 and -D
         const u32x2* F8 = reinterpret_cast<const u32x2*>(Fs);
         sacc = mfma32(fold_operand(F8[32 * t + prow], g), b_one, sacc);
-        pacc = mfma32(fold_operand(F8[C::DOFF + 32 * t + prow], g), b_one, pacc);
+        pacc = mfma32(fold_operand(F8[C::BQ + 32 * t + prow], g), b_one, pacc);
       }
 #pragma unroll
       for (int s = 0; s < C::NS; ++s) {
