@@ -64,6 +64,10 @@ struct DqCfg {
   static constexpr int LOADS = Loader::LOADS_PER_WAVE;  // per wave and block
 };
 
+// (Unlike the other passes, the dq pass does not skip the work of waves whose
+// rows all lie past the end: the early exit raised its register use at
+// d = 64 from 152 to 174 VGPRs, three resident waves per SIMD to two, and
+// slowed it by 10 % even on batches without such waves.)
 template <int D, bool ROPE>
 __global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(AttnArgs a) {
   using C = DqCfg<D>;
@@ -297,6 +301,7 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkv_kernel(AttnArgs a
 
   // ---- prologue: this lane's key k~ and v (B operands)
   const int kj = k0 + w * 32 + r;
+  const bool live = k0 + w * 32 < L;  // wave-uniform
   // (branch-free loads of a clamped row, zeroed past the end: see the dq pass)
   const int kc = min(kj, L - 1);
   u32x4 kreg[C::NS], vreg[C::NS];
@@ -345,6 +350,10 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkv_kernel(AttnArgs a
     const uint16_t* Os = Qs + C::TILE;
     stage = stage + 1 == C::NSTAGE ? 0 : stage + 1;
     next = next + 1 == C::NSTAGE ? 0 : next + 1;
+    // a wave whose 32 rows all lie past the end of the sequence (the last,
+    // partly filled item of a sequence) only takes part in the copies and the
+    // barrier: its MFMA and vector work would produce nothing that is stored
+    if (!live) return;
     const float* Fs = reinterpret_cast<const float*>(Qs + 2 * C::TILE);
     const int lim = L - qb * C::BQ;  // valid queries in this block
 

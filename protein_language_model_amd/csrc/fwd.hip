@@ -98,6 +98,7 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(AttnArgs a) {
   const uint16_t* __restrict__ Kg = a.k + base + (int64_t)kbase * rs;
   const uint16_t* __restrict__ Vg = a.v + base + (int64_t)kbase * rs;
   const int qi = q0 + w * 32 + r;  // this lane's query
+  const bool live = q0 + w * 32 < L;  // wave-uniform
   if (SPLIT && Lk <= 0) {  // empty chunk: O_y = 0, LSE_y = -inf
     if (qi < L) {
       float* Op = a.o_part + (((int64_t)blockIdx.y * a.T + it.seq0 + qi) * a.H + h) * D;
@@ -172,6 +173,10 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(AttnArgs a) {
     const uint16_t* Vs = Ks + C::TILE;
     stage = stage + 1 == C::NSTAGE ? 0 : stage + 1;
     next = next + 1 == C::NSTAGE ? 0 : next + 1;
+    // a wave whose 32 rows all lie past the end of the sequence (the last,
+    // partly filled item of a sequence) only takes part in the copies and the
+    // barrier: its MFMA and vector work would produce nothing that is stored
+    if (!live) return;
 
     // S'^T - m tiles: lane (q = r, g) register i of tile t = key 32t + 16g + i.
     // Keys past the end of the sequence get -inf, so P = 0.

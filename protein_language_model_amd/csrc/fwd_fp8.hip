@@ -81,6 +81,7 @@ __global__ __launch_bounds__(256, Fp8Cfg<D>::OCC) void fwd_fp8_kernel(AttnArgs a
   // queries: 32 bytes per k-step (d values 64s + 32g ..), zero past the end;
   // a negative softmax scale flips the sign bit of every q8 byte (exact)
   const int qi = q0 + w * 32 + r;
+  const bool live = q0 + w * 32 < L;  // wave-uniform
   // (branch-free loads of a clamped row, as in the bf16 forward)
   const uint32_t qflip = a.q_sign < 0.f ? 0x80808080u : 0u;
   const int qc = min(qi, L - 1);
@@ -120,6 +121,10 @@ __global__ __launch_bounds__(256, Fp8Cfg<D>::OCC) void fwd_fp8_kernel(AttnArgs a
     const uint16_t* Vs = Ks + C::KTILE;
     stage = stage + 1 == C::NSTAGE ? 0 : stage + 1;
     next = next + 1 == C::NSTAGE ? 0 : next + 1;
+    // a wave whose 32 rows all lie past the end of the sequence (the last,
+    // partly filled item of a sequence) only takes part in the copies and the
+    // barrier: its MFMA and vector work would produce nothing that is stored
+    if (!live) return;
 
     const int lim = L - kb * C::BN;
     f32x16 sacc[C::NT];
