@@ -291,8 +291,8 @@ esm_attn_status_t esm_attn_merge_partials(
  * grad_row_stride (they may interleave in one [T][3][H][d] gradient; they
  * must not overlap any input). softmax_scale: the one q_rot was made with.
  * drow: caller-provided device buffer of 16 * H * T bytes, 16-byte aligned
- * ([2][H][T] entries of 8 bytes: D = rowsum(dO * O), then LSE * log2(e),
- * each as fp32 or as its three-way bf16 split, by head_dim). passes is a
+ * ([2][H][T] entries of 8 bytes: -D = -rowsum(dO * O), then -LSE * log2(e),
+ * each split into three bf16 values). passes is a
  * bit mask: ESM_ATTN_PASS_DQ runs the dq pass (reads o and lse, writes dq and
  * drow), ESM_ATTN_PASS_DKV the dk/dv pass (reads drow, writes dk and dv);
  * both bits give the full backward. Running the dk/dv pass alone requires a

@@ -42,7 +42,7 @@ esm_attn_status_t check_sizes(int32_t B, int32_t T, int32_t maxL, int32_t H, int
 
 // Plan = rotary table + schedule. The one-shot calls append the rotated q~
 // and k~ ([T][H][d] bf16 each) and, for the backward, drow ([2][H][T]
-// entries of 8 bytes: fp32 values, or their three-way bf16 split).
+// entries of 8 bytes: -D and -LSE log2 e split into three bf16 values).
 Layout make_layout(int32_t B, int32_t T, int32_t maxL, int32_t H, int32_t d, bool bwd) {
   Layout l;
   l.n_chunks = (int32_t)schedule_num_chunks(B, H);

@@ -20,9 +20,7 @@
 // FMA or subtraction per score: an MFMA blocks vector issue for fewer cycles
 // than the 16 vector instructions of a 32x32 tile. In the dkv pass the
 // values vary along the lane's 16 rows, so the dq pass stores them already
-// split (8 bytes per row) and the dkv pass reads them from LDS; at d = 128 the
-// dkv pass keeps plain fp32 rows and vector subtractions (the extra operand
-// registers would spill there).
+// split (8 bytes per row, drow) and the dkv pass reads them from LDS.
 // q~ and k~ come rotated from the rotation pass. The streamed operands (k~
 // and v in the dq pass; q~, dO, LSE and D in the dkv pass) are copied from
 // global memory into swizzled LDS tiles by global_load_lds, in a ring of
@@ -34,14 +32,6 @@
 #include "tile.h"
 
 namespace esm {
-
-// The dq pass hands the dkv pass D and LSE log2 e per row in drow: split into
-// three bf16 values (8 bytes, -x as in neg_bf16_triple) where the dkv pass
-// folds them into its MFMAs, as fp32 otherwise.
-template <int D>
-constexpr bool drow_split() {
-  return D <= 64;
-}
 
 // =========================================================================
 // dq pass
@@ -143,15 +133,10 @@ __global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(AttnArgs a) 
   const u32x4 a_one = fold_ones(g);
   const u32x2 tlse = neg_bf16_triple(lse2), td = neg_bf16_triple(Dq);
   const u32x4 b_neglse = fold_operand(tlse, g), b_negd = fold_operand(td, g);
-  if (qvalid && g == 0) {
-    if (drow_split<D>()) {  // split values for the dkv pass's folds
-      u32x2* R = reinterpret_cast<u32x2*>(a.drow);
-      R[rowidx] = td;
-      R[(int64_t)a.H * a.T + rowidx] = tlse;
-    } else {
-      a.drow[rowidx] = Dq;
-      a.drow[(int64_t)a.H * a.T + rowidx] = lse2;
-    }
+  if (qvalid && g == 0) {  // -D and -lse2, split, for the dkv pass's folds
+    u32x2* R = reinterpret_cast<u32x2*>(a.drow);
+    R[rowidx] = td;
+    R[(int64_t)a.H * a.T + rowidx] = tlse;
   }
 
   // blocks 1 .. NSTAGE-2 after the prologue's global loads (see the wait below)
@@ -250,10 +235,9 @@ struct DkvCfg {
   static constexpr int NS = D / 16;
   static constexpr int ND = D >= 32 ? D / 32 : 1;
   static constexpr int NT = BQ / 32;
-  static constexpr bool FOLD = drow_split<D>();  // S' - lse2 and dP - D folded into MFMAs
   static constexpr int TILE = BQ * D;           // q~ tile, then dO tile
-  // + the lse2 and D rows of the block: fp32, or split (8 bytes) with FOLD
-  static constexpr int STAGE = 2 * TILE + (FOLD ? 8 : 4) * BQ;
+  // + the block's -lse2 and -D rows, split into three bf16 values (8 bytes)
+  static constexpr int STAGE = 2 * TILE + 8 * BQ;
   static constexpr int NSTAGE = 3;              // LDS ring of query blocks
   static constexpr int EPI = BK * (D + 4) * 2;
   static constexpr int LDS = NSTAGE * STAGE > EPI ? NSTAGE * STAGE : EPI;
@@ -282,7 +266,7 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkv_kernel(AttnArgs a
   const uint16_t* __restrict__ dOg = a.dout + (int64_t)it.seq0 * rso + (int64_t)h * D;
   const int64_t row0 = (int64_t)h * a.T + it.seq0;
   // waves 0-1 copy halves of the lse2 row, waves 2-3 halves of the D row
-  constexpr int RW = C::FOLD ? 2 : 1;  // 4-byte words per lse2 / D entry
+  constexpr int RW = 2;  // 4-byte words per lse2 / D entry
   const float* __restrict__ Fg =
       a.drow + RW * ((w < 2 ? (int64_t)a.H * a.T : (int64_t)0) + row0);
 
@@ -363,7 +347,7 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkv_kernel(AttnArgs a
     for (int t = 0; t < C::NT; ++t) {
       f32x16 sacc = f32x16{}, pacc = f32x16{};
       const int rowoff = (32 * t + prow) * D;
-      if (C::FOLD) {  // the A rows (queries 32t + prow) bring -lse2 and -D
+      {  // the A rows (queries 32t + prow) bring -lse2 and -D
         const u32x2* F8 = reinterpret_cast<const u32x2*>(Fs);
         sacc = mfma32(fold_operand(F8[32 * t + prow], g), b_one, sacc);
         pacc = mfma32(fold_operand(F8[C::BQ + 32 * t + prow], g), b_one, pacc);
@@ -375,24 +359,10 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkv_kernel(AttnArgs a
         pacc = mfma32(ld16(Os + off), vreg[s], pacc);
       }
       // queries 32t + 16g + i, i = 0..15; P and dS overwrite S' and dP
-      if (C::FOLD) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          sacc[i] = fast_exp2(sacc[i]);
-          pacc[i] = sacc[i] * pacc[i];
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const u32x4 x = ld16(&Fs[32 * t + 16 * g + 4 * j]);
-          const u32x4 y = ld16(&Fs[C::BQ + 32 * t + 16 * g + 4 * j]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 4 * j + e;
-            sacc[i] = fast_exp2(sacc[i] - __uint_as_float(x[e]));
-            pacc[i] = sacc[i] * (pacc[i] - __uint_as_float(y[e]));
-          }
-        }
+      for (int i = 0; i < 16; ++i) {
+        sacc[i] = fast_exp2(sacc[i]);
+        pacc[i] = sacc[i] * pacc[i];
       }
       if (!FULL) {  // queries past the end (copies of the last row): P = dS = 0
 #pragma unroll

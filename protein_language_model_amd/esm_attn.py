@@ -431,8 +431,8 @@ def esm_attn_bwd_planned(q_rot, k_rot, v, o, d_o, lse, batch, max_seqlen, plan,
 
 
 def drow_buffer(num_heads, total_tokens, device):
-    """Scratch the backward passes share: [2][H][T] entries of 8 bytes (D
-    and LSE log2(e) per row, as fp32 or split into three bf16 values)."""
+    """Scratch the backward passes share: [2][H][T] entries of 8 bytes (-D
+    and -LSE log2(e) per row, each split into three bf16 values)."""
     return torch.empty((2, num_heads, total_tokens, 2), dtype=torch.float32, device=device)
 
 
