@@ -97,12 +97,7 @@ void fill_common(AttnArgs* a, int32_t T, int32_t H, float scale) {
   a->T = T;
   a->H = H;
   a->scale = scale;
-  a->scale_abs = fabsf(scale);
-  a->q_sign = scale < 0.f ? -1.f : 1.f;
-  // exp2 scale. A floor of 1e-30 keeps it positive, so that masked scores
-  // (-inf) still give exp2(-inf) = 0 when softmax_scale is 0; below the floor
-  // every |S c| rounds exp2 to exactly 1 either way.
-  a->c = fmaxf(fabsf(scale) * kLog2e, 1e-30f);
+  a->q_sign = scale < 0.f ? -1.f : 1.f;  // (the bf16 kernels' q~ carries the sign)
 }
 
 esm_attn_status_t run_prep(const int32_t* cu, int32_t B, int32_t T, int32_t maxL, int32_t H,
@@ -374,7 +369,10 @@ esm_attn_status_t esm_attn_fwd_fp8_planned(const uint8_t* q8, const uint8_t* k8,
   a.lse = lse;
   a.items = reinterpret_cast<const Item*>(ws + l.items);
   fill_common(&a, total_tokens, num_heads, softmax_scale);
-  // scores come out of the E4M3 products in units of 1 / (s_q s_k)
+  // scores come out of the E4M3 products in units of 1 / (s_q s_k). A floor
+  // of 1e-30 keeps the exp2 factor positive, so that masked scores (-inf)
+  // still give exp2(-inf) = 0 when softmax_scale is 0; below the floor every
+  // |S c| rounds exp2 to exactly 1 either way.
   a.c = fmaxf(fabsf(softmax_scale) * kLog2e * q_scale * k_scale, 1e-30f);
   if (launch_fwd_fp8(head_dim, a, l.n_slots, reinterpret_cast<hipStream_t>(stream)) !=
       hipSuccess)

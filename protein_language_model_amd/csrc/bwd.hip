@@ -49,6 +49,8 @@ struct DqCfg {
   static constexpr int NSTAGE = 3;              // LDS ring of key blocks
   static constexpr int EPI = BM * (D + 4) * 2;  // fp32 tile, in uint16 units
   static constexpr int LDS = NSTAGE * STAGE > EPI ? NSTAGE * STAGE : EPI;
+  // launch bound (minimum workgroups per CU the register budget must allow);
+  // up to d = 64 the pass fits three per CU anyway (152 VGPRs at d = 64)
   static constexpr int OCC = 2;
   using Loader = TilePair<D, BN>;
   static constexpr int LOADS = Loader::LOADS_PER_WAVE;  // per wave and block

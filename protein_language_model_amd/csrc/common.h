@@ -113,13 +113,6 @@ __device__ __forceinline__ void rotate8(float* lo, float* hi, const float2* cs) 
   }
 }
 
-// Rotation with a run-time sign (q is negated when the softmax scale is
-// negative, so that scores can use |scale|).
-__device__ __forceinline__ void rotate8_signed(float* lo, float* hi, const float2* cs, bool neg) {
-  if (neg) rotate8<false, true>(lo, hi, cs);
-  else rotate8<false, false>(lo, hi, cs);
-}
-
 // Loads (cos, sin) for the angles p * theta_{j0 .. j0+7}: 64 contiguous bytes.
 __device__ __forceinline__ void load_cs8(const float2* rope, int64_t idx, float2* cs) {
   const u32x4* p = reinterpret_cast<const u32x4*>(rope + idx);
@@ -158,13 +151,6 @@ __device__ __forceinline__ u32x4 ld_tr8(const uint16_t* T, int pitch, int k0, in
   return out;
 }
 
-// -x as a pair of bf16 values (hi, lo) with hi + lo = -x to about 2^-17
-// relative, packed low half first: one MFMA k-slot pair against (1, 1)
-// subtracts x from an fp32 accumulator.
-__device__ __forceinline__ uint32_t neg_bf16_pair(float x) {
-  const float hi = __uint_as_float(pack_bf16(-x, 0.f) << 16);
-  return pack_bf16(hi, -x - hi);
-}
 constexpr uint32_t kBf16OnePair = 0x3f803f80u;  // (1.0, 1.0) in bf16
 constexpr uint32_t kBf16One = 0x00003f80u;      // (1.0, 0) in bf16
 

@@ -62,14 +62,13 @@ struct AttnArgs {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
-  float* drow;          // backward: [2][H][T]: D = rowsum(dO * O), then LSE * log2(e)
+  float* drow;          // backward: [2][H][T] x 8 bytes: -D, then -LSE log2(e), split in 3 bf16
   const float2* rope;   // [max_seqlen][d/2]
   const Item* items;
   int32_t T, H;
-  float c;              // |softmax_scale| * log2(e)
-  float q_sign;         // sign applied to rotated q so that scores use |scale|
-  float scale;          // softmax_scale (signed)
-  float scale_abs;
+  float c;              // FP8 forward: |softmax_scale| q_scale k_scale log2(e)
+  float q_sign;         // FP8 forward: sign applied to the E4M3 query bytes
+  float scale;          // softmax_scale (signed): dq = R(-p) (scale dQ~)
   int32_t ld_qkv;       // elements between consecutive tokens' rows of q~, k~, v
   int32_t ld_grad;      // ... of dq, dk, dv (o, dO: H * d)
   int32_t n_items;      // split forward: slots with an item record (the grid may be wider)
