@@ -23,8 +23,8 @@ struct PrepArgs {
 
 hipError_t launch_prep(const PrepArgs& a, hipStream_t stream);
 
-// Rotation pass: q_rot = bf16(R(p) q), k_rot = bf16(R(p) k), or copies when
-// rope is null.
+// Rotation pass: q_rot = bf16(fl32(q_mul * fl32(R(p) q))), k_rot = bf16(R(p) k);
+// R(p) is the identity when rope is null.
 struct RotArgs {
   const uint16_t* q;    // may equal q_rot (in place, same row stride)
   const uint16_t* k;    // may equal k_rot

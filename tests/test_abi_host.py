@@ -50,7 +50,7 @@ def test_workspace_sizes():
     plan = E.esm_attn_plan_bytes(16, 16384, 1024, 20, 64)
     qk = 2 * 16384 * 20 * 64 * 2            # rotated q~ and k~, bf16
     assert fwd >= plan + qk
-    assert bwd >= fwd + 2 * 16384 * 20 * 4  # drow: D and LSE log2(e), fp32
+    assert bwd >= fwd + 2 * 16384 * 20 * 8  # drow: -D and -LSE log2(e), 8 bytes each
     assert plan >= 1024 * 32 * 8            # rotary table
     assert E.esm_attn_plan_bytes(16, 16384, 1024, 20, 48) == 0
     assert E.esm_attn_fwd_workspace_bytes(16, 16384, 1024, 20, 48) == 0   # bad head_dim
@@ -277,3 +277,19 @@ def test_schedule_edge_cases():
         if r[1] > 0 and r[3] == 0:
             seen.append(-(-r[1] // 128))
     assert seen == sorted(seen, reverse=True)
+
+
+def test_drow_buffer_and_size_check():
+    """The binding's drow scratch: [2][H][T] entries of 8 bytes; a smaller or
+    non-float32 buffer is refused before anything reaches the library."""
+    import torch
+    d = E.drow_buffer(3, 10, "cpu")
+    assert d.dtype == torch.float32 and d.numel() * 4 == 2 * 3 * 10 * 8
+    E._check_drow(d, 3, 10)
+    E._check_drow(torch.empty(4 * 3 * 10), 3, 10)
+    with pytest.raises(ValueError):
+        E._check_drow(torch.empty(4 * 3 * 10 - 1), 3, 10)
+    with pytest.raises(ValueError):
+        E._check_drow(torch.empty(2, 3, 10), 3, 10)          # the old fp32 [2][H][T] size
+    with pytest.raises(ValueError):
+        E._check_drow(torch.empty(4 * 3 * 10, dtype=torch.float64), 3, 10)
