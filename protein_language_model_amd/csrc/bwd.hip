@@ -207,8 +207,24 @@ __global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(AttnArgs a) 
     }
   };
   const int nfull = L / C::BN;
-  for (int kb = 0; kb < nfull; ++kb) block(kb, Full{});
-  if (nfull < nkb) block(nfull, Ragged{});
+  if (q0 + w * 32 < L) {
+    for (int kb = 0; kb < nfull; ++kb) block(kb, Full{});
+    if (nfull < nkb) block(nfull, Ragged{});
+  } else {
+    // a wave whose 32 queries all lie past the end of the sequence only takes
+    // part in the copies and the barriers (the same waits, barriers and
+    // issues as block(), one per key block); kept out of block() because an
+    // early exit there raised the pass's register use by an occupancy level
+    for (int kb = 0; kb < nkb; ++kb) {
+      if (C::NSTAGE == 3 && kb + 1 < nkb)
+        wait_vmem<C::LOADS>();
+      else
+        wait_vmem<0>();
+      block_barrier();
+      if (kb + C::NSTAGE - 1 < nkb) issue(kb + C::NSTAGE - 1, next);
+      next = next + 1 == C::NSTAGE ? 0 : next + 1;
+    }
+  }
   __syncthreads();  // every wave is done with the tiles
 
   // ---- epilogue: dq~ (fp32) -> LDS -> inverse rotation -> bf16
