@@ -26,3 +26,4 @@ from .attention import (  # noqa: F401
     forward,
     backward,
 )
+from . import tolerances  # noqa: F401

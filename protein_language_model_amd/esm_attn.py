@@ -161,13 +161,33 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _on_gpu(device, *ts):
+    """Every tensor given (None skipped) lives on `device`, a GPU: the library
+    dereferences the pointers in its kernels, so a host pointer would fault."""
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("expected GPU tensors, got one on %s" % t.device)
+        if t.device != device:
+            raise ValueError("tensors on different devices (%s and %s)" % (t.device, device))
+
+
+def _check_cu(cu, device):
+    """cu_seqlens: 1-D contiguous int32 on the same GPU as the operands (an
+    int64 tensor would be read as pairs of int32 values)."""
+    if cu.dtype != torch.int32 or cu.dim() != 1 or not cu.is_contiguous() or cu.numel() < 2:
+        raise ValueError("cu_seqlens must be a contiguous 1-D int32 tensor of batch+1 entries")
+    _on_gpu(device, cu)
+    return cu.numel() - 1
+
+
 def _check_qkv(*ts):
     T, H, d = ts[0].shape
     for t in ts:
         if t.dtype != torch.bfloat16 or t.shape != (T, H, d) or not t.is_contiguous():
             raise ValueError("expected contiguous bf16 tensors of shape [T, H, d]")
-        if t.device != ts[0].device:
-            raise ValueError("tensors on different devices")
+    _on_gpu(ts[0].device, *ts)
     return T, H, d
 
 
@@ -186,11 +206,10 @@ def _row_stride(*ts):
     for t in ts:
         if t.dtype != torch.bfloat16 or t.shape != (T, H, d):
             raise ValueError("expected bf16 tensors of shape [T, H, d]")
-        if t.device != ts[0].device:
-            raise ValueError("tensors on different devices")
         if t.stride(2) != 1 or (H > 1 and t.stride(1) != d):
             raise ValueError("expected rows with packed (H, d) (strides (ld, d, 1))")
         strides.add(t.stride(0))
+    _on_gpu(ts[0].device, *ts)
     if T <= 1:
         return H * d
     if len(strides) != 1:
@@ -201,27 +220,47 @@ def _row_stride(*ts):
 
 def _workspace(nbytes, device, workspace):
     if workspace is not None:
+        if not workspace.is_contiguous():
+            raise ValueError("a workspace or plan buffer must be contiguous")
+        _on_gpu(device, workspace)
         return workspace
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def _check_plan(plan, device):
+    """A plan from esm_attn_plan: a contiguous buffer on the operands' GPU."""
+    if not plan.is_contiguous():
+        raise ValueError("plan must be a contiguous buffer (esm_attn_plan's result)")
+    _on_gpu(device, plan)
+
+
+def _check_lse(lse, H, T):
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (H, T) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous fp32 [H, T]")
 
 
 def esm_attn_fwd(q, k, v, cu_seqlens, max_seqlen, softmax_scale=None, rope_base=10000.0,
                  out=None, lse=None, workspace=None, stream=None):
     """Forward: returns (o bf16 [T,H,d], lse fp32 [H,T])."""
     T, H, d = _check_qkv(q, k, v)
-    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
-        raise ValueError("cu_seqlens must be a 1-D int32 tensor")
-    B = cu_seqlens.numel() - 1
+    B = _check_cu(cu_seqlens, q.device)
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    _check_packed((T, H, d), out)
+    _check_lse(lse, H, T)
+    _on_gpu(q.device, out, lse)
     nbytes = esm_attn_fwd_workspace_bytes(B, T, int(max_seqlen), H, d)
     ws = _workspace(nbytes, q.device, workspace)
     _check(lib().esm_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), B, T,
                               int(max_seqlen), H, d, scale, float(rope_base), _ptr(out),
-                              _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)))
+                              _ptr(lse), _ptr(ws), _nbytes(ws), _stream(stream)))
     return out, lse
 
 
@@ -229,19 +268,20 @@ def esm_attn_bwd(q, k, v, o, d_o, lse, cu_seqlens, max_seqlen, softmax_scale=Non
                  rope_base=10000.0, dq=None, dk=None, dv=None, workspace=None, stream=None):
     """Backward: returns (dq, dk, dv), bf16 [T,H,d]."""
     T, H, d = _check_qkv(q, k, v, o, d_o)
-    if lse.dtype != torch.float32 or lse.shape != (H, T) or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous fp32 [H, T]")
-    B = cu_seqlens.numel() - 1
+    _check_lse(lse, H, T)
+    B = _check_cu(cu_seqlens, q.device)
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    _check_packed((T, H, d), dq, dk, dv)
+    _on_gpu(q.device, lse, dq, dk, dv)
     nbytes = esm_attn_bwd_workspace_bytes(B, T, int(max_seqlen), H, d)
     ws = _workspace(nbytes, q.device, workspace)
     _check(lib().esm_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse),
                               _ptr(cu_seqlens), B, T, int(max_seqlen), H, d, scale,
                               float(rope_base), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
-                              ws.numel(), _stream(stream)))
+                              _nbytes(ws), _stream(stream)))
     return dq, dk, dv
 
 
@@ -253,11 +293,11 @@ def esm_attn_plan(cu_seqlens, total_tokens, max_seqlen, num_heads, head_dim,
                   rope_base=10000.0, plan=None, stream=None):
     """Builds the schedule + rotary table for one batch; returns the plan
     buffer (a uint8 device tensor) for the planned calls."""
-    B = cu_seqlens.numel() - 1
+    B = _check_cu(cu_seqlens, cu_seqlens.device)
     nbytes = esm_attn_plan_bytes(B, int(total_tokens), int(max_seqlen), num_heads, head_dim)
     plan = _workspace(nbytes, cu_seqlens.device, plan)
     _check(lib().esm_attn_plan(_ptr(cu_seqlens), B, int(total_tokens), int(max_seqlen),
-                               num_heads, head_dim, float(rope_base), _ptr(plan), plan.numel(),
+                               num_heads, head_dim, float(rope_base), _ptr(plan), _nbytes(plan),
                                _stream(stream)))
     return plan
 
@@ -276,10 +316,12 @@ def esm_attn_rotate_planned(q, k, batch, max_seqlen, plan, rope_base=10000.0, q_
     if k_rot is None:
         k_rot = torch.empty((T, H, d), dtype=k.dtype, device=k.device)
     ld_out = _row_stride(q_rot, k_rot)
+    _on_gpu(q.device, q_rot, k_rot)
+    _check_plan(plan, q.device)
     _check(lib().esm_attn_rotate_planned(_ptr(q), _ptr(k), ld_in, int(batch), T,
                                          int(max_seqlen), H, d, float(softmax_scale),
                                          float(rope_base), _ptr(q_rot),
-                                         _ptr(k_rot), ld_out, _ptr(plan), plan.numel(),
+                                         _ptr(k_rot), ld_out, _ptr(plan), _nbytes(plan),
                                          _stream(stream)))
     return q_rot, k_rot
 
@@ -297,9 +339,12 @@ def esm_attn_fwd_planned(q_rot, k_rot, v, batch, max_seqlen, plan, softmax_scale
     _check_packed((T, H, d), out)
     if lse is None:
         lse = torch.empty((H, T), dtype=torch.float32, device=v.device)
+    _check_lse(lse, H, T)
+    _on_gpu(v.device, out, lse)
+    _check_plan(plan, v.device)
     _check(lib().esm_attn_fwd_planned(_ptr(q_rot), _ptr(k_rot), _ptr(v), ld, int(batch), T,
                                       int(max_seqlen), H, d, scale, _ptr(out), _ptr(lse),
-                                      _ptr(plan), plan.numel(), _stream(stream)))
+                                      _ptr(plan), _nbytes(plan), _stream(stream)))
     return out, lse
 
 
@@ -323,10 +368,13 @@ def esm_attn_fwd_split_planned(q_rot, k_rot, v, batch, max_seqlen, plan, n_split
     if lse_part is None:
         lse_part = torch.empty((n_split, H, T), dtype=torch.float32, device=dev)
     _check_partials(o_part, lse_part, n_split, T, H, d)
+    _check_lse(lse, H, T)
+    _on_gpu(dev, out, lse, o_part, lse_part)
+    _check_plan(plan, dev)
     _check(lib().esm_attn_fwd_split_planned(_ptr(q_rot), _ptr(k_rot), _ptr(v), ld, int(batch), T,
                                             int(max_seqlen), H, d, scale, int(n_split),
                                             _ptr(o_part), _ptr(lse_part), _ptr(out), _ptr(lse),
-                                            _ptr(plan), plan.numel(), _stream(stream)))
+                                            _ptr(plan), _nbytes(plan), _stream(stream)))
     return out, lse, o_part, lse_part
 
 
@@ -350,6 +398,8 @@ def esm_attn_merge_partials(o_part, lse_part, out=None, lse=None, stream=None):
     _check_packed((T, H, d), out)
     if lse is None:
         lse = torch.empty((H, T), dtype=torch.float32, device=o_part.device)
+    _check_lse(lse, H, T)
+    _on_gpu(o_part.device, lse_part, out, lse)
     _check(lib().esm_attn_merge_partials(_ptr(o_part), _ptr(lse_part), R, T, H, d, _ptr(out),
                                          _ptr(lse), _stream(stream)))
     return out, lse
@@ -368,10 +418,12 @@ def esm_attn_quantize_fp8_planned(q, k, batch, max_seqlen, plan, q_scale, k_scal
     for t in (q8, k8):
         if t.dtype != torch.uint8 or tuple(t.shape) != (T, H, d) or not t.is_contiguous():
             raise ValueError("q8, k8 must be contiguous uint8 [T, H, d]")
+    _on_gpu(q.device, q8, k8)
+    _check_plan(plan, q.device)
     _check(lib().esm_attn_quantize_fp8_planned(_ptr(q), _ptr(k), ld, int(batch), T,
                                                int(max_seqlen), H, d, float(rope_base),
                                                float(q_scale), float(k_scale), _ptr(q8), _ptr(k8),
-                                               _ptr(plan), plan.numel(), _stream(stream)))
+                                               _ptr(plan), _nbytes(plan), _stream(stream)))
     return q8, k8
 
 
@@ -390,10 +442,13 @@ def esm_attn_fwd_fp8_planned(q8, k8, v, batch, max_seqlen, plan, q_scale, k_scal
     _check_packed((T, H, d), out)
     if lse is None:
         lse = torch.empty((H, T), dtype=torch.float32, device=v.device)
+    _check_lse(lse, H, T)
+    _on_gpu(v.device, q8, k8, out, lse)
+    _check_plan(plan, v.device)
     _check(lib().esm_attn_fwd_fp8_planned(_ptr(q8), _ptr(k8), _ptr(v), ldv, int(batch), T,
                                           int(max_seqlen), H, d, scale, float(q_scale),
                                           float(k_scale), _ptr(out), _ptr(lse), _ptr(plan),
-                                          plan.numel(), _stream(stream)))
+                                          _nbytes(plan), _stream(stream)))
     return out, lse
 
 
@@ -422,10 +477,14 @@ def esm_attn_bwd_planned(q_rot, k_rot, v, o, d_o, lse, batch, max_seqlen, plan,
         dv = new() if dv is None else dv
         grads += [dk, dv]
     ld_grad = _row_stride(*grads)
+    if passes & PASS_DQ:
+        _check_lse(lse, H, T)
+    _on_gpu(v.device, o, d_o, lse, drow, *grads)
+    _check_plan(plan, v.device)
     _check(lib().esm_attn_bwd_planned(_ptr(q_rot), _ptr(k_rot), _ptr(v), ld, _ptr(o), _ptr(d_o),
                                       _ptr(lse), int(batch), T, int(max_seqlen), H, d, scale,
                                       float(rope_base), _ptr(dq), _ptr(dk), _ptr(dv), ld_grad,
-                                      _ptr(drow), int(passes), _ptr(plan), plan.numel(),
+                                      _ptr(drow), int(passes), _ptr(plan), _nbytes(plan),
                                       _stream(stream)))
     return dq, dk, dv, drow
 
@@ -489,7 +548,7 @@ class _Attention(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, cu_seqlens, max_seqlen, scale, rope_base):
         T, H, d = _check_qkv(q, k, v)
-        B = cu_seqlens.numel() - 1
+        B = _check_cu(cu_seqlens, q.device)
         plan = esm_attn_plan(cu_seqlens, T, max_seqlen, H, d, rope_base)
         # (always: the pass also applies softmax_scale log2(e) to q)
         q_rot, k_rot = esm_attn_rotate_planned(q, k, B, max_seqlen, plan, rope_base,
@@ -523,7 +582,7 @@ class _AttentionQKV(torch.autograd.Function):
         d = qkv.shape[1] // (3 * H)
         view = qkv.view(T, 3, H, d)
         q, k, v = view[:, 0], view[:, 1], view[:, 2]
-        B = cu_seqlens.numel() - 1
+        B = _check_cu(cu_seqlens, qkv.device)
         if plan is None:
             plan = esm_attn_plan(cu_seqlens, T, max_seqlen, H, d, rope_base)
         esm_attn_rotate_planned(q, k, B, max_seqlen, plan, rope_base, q_rot=q, k_rot=k,
@@ -563,6 +622,8 @@ def attention_qkv(qkv, cu_seqlens, max_seqlen, num_heads, softmax_scale=None,
     `plan` may be a plan built once for the batch and shared by every layer."""
     if qkv.dim() != 2 or qkv.dtype != torch.bfloat16 or not qkv.is_contiguous():
         raise ValueError("qkv must be a contiguous bf16 [T, 3*H*d] tensor")
+    _on_gpu(qkv.device, qkv)
+    _check_cu(cu_seqlens, qkv.device)
     if qkv.shape[1] % (3 * num_heads) != 0:
         raise ValueError("qkv width must be 3 * num_heads * head_dim")
     d = qkv.shape[1] // (3 * num_heads)

@@ -8,6 +8,7 @@ import numpy as np
 import torch
 
 import oracle
+from oracle import tolerances as T
 from protein_language_model_amd import esm_attn as E
 
 
@@ -49,73 +50,63 @@ def oracle_inputs(inp):
     return tuple(oracle.bf16_bits_to_f64(inp[n]) for n in ("q", "k", "v", "do"))
 
 
-def ulp_bf16(x):
-    """Spacing of the bf16 grid at |x| (2^(e-7) for |x| in [2^e, 2^(e+1)))."""
-    ax = np.abs(x)
-    e = np.floor(np.log2(np.maximum(ax, 2.0 ** -126)))
-    return 2.0 ** (e - 7)
+ulp_bf16 = T.ulp_bf16
+relf = T.relf
+O_ATOL, G_RELF, LSE_ATOL = T.O_ATOL, T.G_RELF, T.LSE_ATOL
 
 
-O_ATOL = 1e-2     # max-abs error allowed on O
-G_RELF = 2e-2     # relative Frobenius error allowed on dq, dk, dv
-# max-abs error on LSE (diagnostic; no stated tolerance): the forward's
-# normaliser is the sum of the bf16-rounded probabilities its P V product
-# used, each within 2^-8 relative of exact, so its log is within
-# ln(1 + 2^-8) = 3.9e-3 of the exact LSE; 1e-4 covers the fp32 terms
-LSE_ATOL = math.log1p(2.0 ** -8) + 1e-4
+def compare(gpu, inp, seqs=None, heads=None, sharpened=False, grads_exact=True, scale=None,
+            rope_base=None, with_bwd=True, label=""):
+    """Oracle on the listed (sequence, head) slices; asserts the bounds of
+    oracle.tolerances against both precision modes of the oracle.
 
-
-def relf(a, b):
-    n = np.linalg.norm(b)
-    return np.linalg.norm(a - b) / (n if n > 0 else 1.0)
-
-
-def compare(gpu, inp, seqs=None, heads=None, exact_too=True, scale=None, rope_base=None,
-            with_bwd=True, label=""):
-    """Oracle on the listed (sequence, head) slices; asserts the tolerances.
-    O: |O_gpu - O_ref| <= 1e-2 + ulp/2 elementwise against the bf16-operand
-    oracle (bf16 storage of O alone can err by half an ulp); dq/dk/dv: relative
-    Frobenius <= 2e-2. The exact-rotation oracle is always reported; with
-    exact_too the literal bounds must also hold against it."""
+    exact (float64 operands, the definition):
+      dq, dk, dv: relative Frobenius <= 2e-2 (unless grads_exact is False);
+      O: max-abs <= 1e-2, except on a sharpened softmax (sharpened=True:
+      q, k x 3 or a scale several times 1/sqrt(d)), where rounding the
+      rotated operands to bf16 alone moves O by about 0.1 for any kernel that
+      feeds bf16 matrix units; there the exact-mode O error is reported, not
+      asserted.
+    bf16_operands (the operands rounded as the kernels round them):
+      O elementwise <= 1e-2 + ulp/2; LSE max-abs <= ln(1 + 2^-8) + 1e-4;
+      dq, dk, dv relative Frobenius <= 2e-2."""
     for name, t in gpu.items():   # NaN / Inf scan of every output, compared rows or not
         assert np.isfinite(t).all(), (label, name)
     q, k, v, do = oracle_inputs(inp)
     cu = inp["cu_seqlens"]
     s = inp["scale"] if scale is None else scale
     base = inp["rope_base"] if rope_base is None else rope_base
-    modes = ["bf16_operands", "exact"]
-    T = inp["T"]
+    Tn = inp["T"]
     seqs = list(range(len(cu) - 1)) if seqs is None else list(seqs)
     heads = list(range(inp["H"])) if heads is None else list(heads)
-    rows = np.zeros(T, bool)
+    rows = np.zeros(Tn, bool)
     for b in seqs:
         rows[cu[b]:cu[b + 1]] = True
     report = {}
-    for mode in modes:
+    for mode in ("exact", "bf16_operands"):
         O, LSE = oracle.forward(q, k, v, cu, s, base, mode=mode, seqs=seqs, heads=heads)
         og, orf = gpu["o"][rows][:, heads], O[rows][:, heads]
         err = np.abs(og - orf)
         report[mode + ".o_maxabs"] = float(err.max()) if err.size else 0.0
+        lerr = np.abs(gpu["lse"][heads][:, rows] - LSE[heads][:, rows])
+        report[mode + ".lse_maxabs"] = float(lerr.max()) if lerr.size else 0.0
         if mode == "bf16_operands":
-            bound = O_ATOL + 0.5 * ulp_bf16(orf)
-            ex = err - bound
+            ex = err - T.o_bound(orf)
             if ex.size and ex.max() > 0:
                 at = np.unravel_index(int(ex.argmax()), ex.shape)
                 raise AssertionError((label, mode, "excess", float(ex.max()), "at", at,
                                       "gpu", float(og[at]), "oracle", float(orf[at]),
                                       "elements over", int((ex > 0).sum()), "of", ex.size))
-            lerr = np.abs(gpu["lse"][heads][:, rows] - LSE[heads][:, rows])
-            report["lse_maxabs"] = float(lerr.max()) if lerr.size else 0.0
-            assert report["lse_maxabs"] <= LSE_ATOL, (label, report)
-        elif exact_too:
+            assert report[mode + ".lse_maxabs"] <= LSE_ATOL, (label, report)
+        elif not sharpened:
             assert report[mode + ".o_maxabs"] <= O_ATOL, (label, mode, report)
         if with_bwd:
             dq, dk, dv = oracle.backward(q, k, v, do, cu, s, base, mode=mode, seqs=seqs,
                                          heads=heads)
             for name, ref in (("dq", dq), ("dk", dk), ("dv", dv)):
                 e = relf(gpu[name][rows][:, heads], ref[rows][:, heads])
-                report["%s.%s_relf" % (mode, name)] = float(e)
-                if mode == "bf16_operands" or exact_too:
-                    assert e <= G_RELF, (label, mode, name, e)
+                report["%s.%s_relf" % (mode, name)] = e
+                if mode == "bf16_operands" or grads_exact:
+                    assert e <= G_RELF, (label, mode, name, e, report)
     say(label, {k_: "%.3g" % v_ for k_, v_ in report.items()})
     return report

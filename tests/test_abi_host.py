@@ -293,3 +293,68 @@ def test_drow_buffer_and_size_check():
         E._check_drow(torch.empty(2, 3, 10), 3, 10)          # the old fp32 [2][H][T] size
     with pytest.raises(ValueError):
         E._check_drow(torch.empty(4 * 3 * 10, dtype=torch.float64), 3, 10)
+
+
+# ---------------------------------------------------------------- binding checks
+# The binding refuses, before any library call, operands the kernels would
+# misread (int64 cu_seqlens read as int32 pairs) or fault on (host pointers).
+
+def _bf(T=8, H=2, d=64):
+    return torch.zeros((T, H, d), dtype=torch.bfloat16)
+
+
+def test_binding_rejects_wrong_cu_seqlens_dtype_and_shape():
+    q = _bf()
+    for cu in (torch.tensor([0, 8], dtype=torch.int64), torch.tensor([[0, 8]], dtype=torch.int32),
+               torch.tensor([0], dtype=torch.int32),
+               torch.tensor([0, 0, 8, 8], dtype=torch.int32)[::2]):
+        with pytest.raises(ValueError):
+            E.esm_attn_fwd(q, q, q, cu, 8)
+        # the dtype and shape checks come before the device check
+        with pytest.raises(ValueError, match="cu_seqlens"):
+            E._check_cu(cu, q.device)
+    lse = torch.zeros((2, 8), dtype=torch.float32)
+    with pytest.raises(ValueError, match="GPU|cu_seqlens"):
+        E.esm_attn_bwd(q, q, q, q, q, lse, torch.tensor([0, 8], dtype=torch.int64), 8)
+
+
+def test_binding_rejects_host_tensors():
+    q = _bf()
+    cu = torch.tensor([0, 8], dtype=torch.int32)
+    lse = torch.zeros((2, 8), dtype=torch.float32)
+    with pytest.raises(ValueError, match="GPU"):
+        E.esm_attn_fwd(q, q, q, cu, 8)
+    with pytest.raises(ValueError, match="GPU"):
+        E.esm_attn_bwd(q, q, q, q, q, lse, cu, 8)
+    with pytest.raises(ValueError, match="GPU"):
+        E.esm_attn_plan(cu, 8, 8, 2, 64)
+    plan = torch.zeros(64, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="GPU"):
+        E.esm_attn_rotate_planned(q, q, 1, 8, plan, softmax_scale=0.125)
+    with pytest.raises(ValueError, match="GPU"):
+        E.esm_attn_fwd_planned(q, q, q, 1, 8, plan)
+    with pytest.raises(ValueError, match="GPU"):
+        E.esm_attn_bwd_planned(q, q, q, q, q, lse, 1, 8, plan,
+                               drow=torch.zeros(4 * 2 * 8, dtype=torch.float32))
+    with pytest.raises(ValueError, match="GPU"):
+        E.esm_attn_merge_partials(torch.zeros((2, 8, 2, 64)), torch.zeros((2, 2, 8)))
+    with pytest.raises(ValueError, match="GPU"):
+        E.attention(q, q, q, cu, 8)
+    with pytest.raises(ValueError, match="GPU"):
+        E.attention_qkv(torch.zeros((8, 3 * 2 * 64), dtype=torch.bfloat16), cu, 8, 2)
+
+
+def test_binding_rejects_malformed_outputs():
+    # (shape and dtype checks; the calls run them after the device checks)
+    with pytest.raises(ValueError, match="lse"):
+        E._check_lse(torch.zeros((8, 2), dtype=torch.float32), 2, 8)
+    with pytest.raises(ValueError, match="lse"):
+        E._check_lse(torch.zeros((2, 8), dtype=torch.float64), 2, 8)
+    with pytest.raises(ValueError, match="bf16"):
+        E._check_packed((8, 2, 64), torch.zeros((8, 2, 64), dtype=torch.float16))
+    with pytest.raises(ValueError, match="contiguous"):
+        E._workspace(32, torch.device("cpu"), torch.zeros(64, dtype=torch.uint8)[::2])
+    with pytest.raises(ValueError, match="GPU"):
+        E._workspace(32, torch.device("cpu"), torch.zeros(64, dtype=torch.uint8))
+    assert E._nbytes(torch.zeros(10, dtype=torch.float32)) == 40
+

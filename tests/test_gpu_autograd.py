@@ -1,13 +1,15 @@
 """The autograd wrappers: `attention` (packed q, k, v) equals the one-shot
 calls bit for bit, forward and backward; `attention_qkv` (fused projection
-output, rotated in place) gives the same output and the same gradients of
-the projection's input and weight as the packed path."""
+output, rotated in place) meets the oracle bounds on the projection's q, k, v
+(output and dq, dk, dv, read back from the fused gradient) and gives the same
+output and the same gradients of the projection's input and weight as the
+packed path."""
 
 import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import say, to_dev
+from gpu_helpers import bf16_f64, compare, say, to_dev
 from protein_language_model_amd import workloads as W
 from protein_language_model_amd import esm_attn as E
 
@@ -43,11 +45,15 @@ def test_attention_qkv_in_a_projection(device, d):
     do = torch.from_numpy(rng.standard_normal((T, H, d)).astype(np.float32)).to(device)
     x0, w0, do = x0.to(torch.bfloat16), w0.to(torch.bfloat16), do.to(torch.bfloat16)
 
+    seen = {}
+
     def run(fused):
         x = x0.clone().requires_grad_(True)
         w = w0.clone().requires_grad_(True)
         qkv = x @ w.t()
         if fused:
+            seen["qkv"] = qkv.detach().clone()   # before the in-place rotation
+            qkv.register_hook(lambda g: seen.__setitem__("dqkv", g.detach().clone()))
             o = E.attention_qkv(qkv, cu, maxL, H)
         else:
             q, k, v = (qkv.view(T, 3, H, d)[:, i].contiguous() for i in range(3))
@@ -58,6 +64,22 @@ def test_attention_qkv_in_a_projection(device, d):
 
     of, xf, wf = run(True)
     op, xp, wp = run(False)
+    # the fused path against the oracle on the projection's own q, k, v
+    bits = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    q3 = seen["qkv"].view(T, 3, H, d)
+    inp = dict(q=bits(q3[:, 0]), k=bits(q3[:, 1]), v=bits(q3[:, 2]), do=bits(do),
+               cu_seqlens=W.cu_from_lengths(lengths), lengths=lengths, T=T, H=H, d=d,
+               scale=1.0 / np.sqrt(d), rope_base=W.ROPE_BASE)
+    g3 = seen["dqkv"].view(T, 3, H, d)
+    gpu = dict(o=bf16_f64(of), dq=bf16_f64(g3[:, 0]), dk=bf16_f64(g3[:, 1]),
+               dv=bf16_f64(g3[:, 2]))
+    plan = E.esm_attn_plan(cu, T, maxL, H, d)
+    qr, kr = E.esm_attn_rotate_planned(q3[:, 0], q3[:, 1], len(lengths), maxL, plan,
+                                       softmax_scale=inp["scale"])
+    _, lse = E.esm_attn_fwd_planned(qr, kr, q3[:, 2].contiguous(), len(lengths), maxL, plan)
+    gpu["lse"] = lse.cpu().numpy().astype(np.float64)
+    compare(gpu, inp, label="attention_qkv d%d" % d)
+    # and bitwise the packed path
     assert torch.equal(of, op)
     assert torch.equal(xf, xp) and torch.equal(wf, wp)
 

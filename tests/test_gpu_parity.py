@@ -48,7 +48,9 @@ def test_sharpened_qk_parity(device):
     inp = _case("esm2_3b", lengths=[300, 1024, 45], H=3)
     say("case sharpened", inp["lengths"])
     gpu = run_gpu(inp, device)
-    compare(gpu, inp, exact_too=False, label="sharpened")
+    # O against the exact oracle is the stated exception of a sharpened
+    # softmax (reported); gradients meet the exact-oracle bound
+    compare(gpu, inp, sharpened=True, label="sharpened")
 
 
 @pytest.mark.parametrize("name,H", [("esm2_650m", 1), ("esm2_15b", 2)])
@@ -60,7 +62,11 @@ def test_overflow_scale_qk_x10(device, name, H):
     inp = W.make_inputs(w, lengths=[1, 130, 1024, 77, 0, 256], num_heads=H)
     say("case qk x10", name, inp["lengths"], H, inp["d"])
     gpu = run_gpu(inp, device)
-    compare(gpu, inp, exact_too=False, label="qk x10 " + name)
+    # logits spread over hundreds: rounding the rotated operands to bf16 moves
+    # them by O(1), so no bf16-operand kernel comes near the exact oracle here
+    # (0.17 relative Frobenius on dq for the oracle's own bf16-operand mode);
+    # this case checks overflow handling against the operand-rounded oracle
+    compare(gpu, inp, sharpened=True, grads_exact=False, label="qk x10 " + name)
 
 
 @pytest.mark.parametrize("d,scale,base", [(16, None, 10000.0), (64, None, 10000.0),
@@ -117,8 +123,8 @@ def test_scale_and_rope_variants(device, scale, base):
     say("case scale/base", scale, base)
     gpu = run_gpu(inp, device, scale=scale, rope_base=base)
     # scale 0.6 (about 5x 1/sqrt(d)) sharpens the softmax like the 3B workload's
-    # q,k x3: only the bf16-operand bound is attainable there
-    compare(gpu, inp, scale=scale, rope_base=base, exact_too=abs(scale) <= 0.2,
+    # q,k x3: O against the exact oracle is reported there, not asserted
+    compare(gpu, inp, scale=scale, rope_base=base, sharpened=abs(scale) > 0.2,
             label="s=%g base=%g" % (scale, base))
 
 
@@ -265,7 +271,8 @@ def test_repeated_calls_on_one_plan(device, d):
 def test_fused_qkv_layout(device, d, pad):
     """Strided operands: q, k, v as views of one [T, 3, H, d] projection
     output (token row stride 3*H*d + pad), rotated in place, and dq, dk, dv
-    written into one fused gradient. Bitwise equal to the packed layout."""
+    written into one fused gradient. Within the oracle bounds, and bitwise
+    equal to the packed layout."""
     name = {16: "esm2_8m", 32: "esm2_150m", 64: "esm2_650m", 128: "esm2_15b"}[d]
     inp = _case(name, lengths=[300, 1, 129, 64, 0, 77], H=3)
     T, H, B = inp["T"], inp["H"], len(inp["lengths"])
@@ -294,6 +301,11 @@ def test_fused_qkv_layout(device, d, pad):
     dq, dk, dv, _ = E.esm_attn_bwd_planned(qf, kf, vf, o, do, lse, B, maxL, plan, scale, base,
                                            dq=gview(0), dk=gview(1), dv=gview(2))
     torch.cuda.synchronize()
+    # the strided outputs against the oracle, at the bounds of every layout
+    fused = {n: bf16_f64(t) for n, t in (("o", o), ("dq", dq), ("dk", dk), ("dv", dv))}
+    fused["lse"] = lse.cpu().numpy().astype(np.float64)
+    compare(fused, inp, label="fused d%d pad %d" % (d, pad))
+    # and bitwise equal to the packed layout
     for n, t in (("o", o), ("dq", dq), ("dk", dk), ("dv", dv)):
         np.testing.assert_array_equal(bf16_f64(t), ref[n], err_msg=n)
     np.testing.assert_array_equal(lse.cpu().numpy().astype(np.float64), ref["lse"])
@@ -321,21 +333,34 @@ def test_many_short_sequences(device):
 
 # ---------------------------------------------------------------- full sizes
 
-FULL = [
-    ("esm2_8m", None, None),
-    ("esm2_150m", [0, 31], [0, 19]),
-    ("esm2_650m", [0, 15], [0, 7, 19]),
-    ("esm2_3b", [0, 1], [0, 39]),
-    ("esm2_15b", [0], [0, 23]),
-    ("esm2_15b_ragged", [0, 1, 2], [5]),
-]
+def _full_size_samples(name, inp):
+    """(sequences, heads) compared at full size: the first and last sequences
+    of the batch, the longest and shortest ones (the schedule runs sequences
+    longest first, so these sit at both ends of its order) and one from the
+    middle; heads at both ends and one between."""
+    L = np.diff(inp["cu_seqlens"])
+    B, H = len(L), inp["H"]
+    if name == "esm2_8m":
+        return None, None
+    if name.startswith("esm2_15b"):   # 8192-token slices: a few suffice
+        return [0, B - 1], [0, H - 1]
+    order = np.argsort(-L, kind="stable")
+    seqs = {0, 1, B // 2, B - 1} | set(order[:2].tolist()) | set(order[-2:].tolist())
+    return sorted(seqs), sorted({0, H // 2 - 3, H - 1})
 
 
-@pytest.mark.parametrize("name,seqs,heads", FULL, ids=[f[0] for f in FULL])
-def test_full_size_sampled_parity(device, name, seqs, heads):
+FULL = ["esm2_8m", "esm2_150m", "esm2_650m", "esm2_3b", "esm2_15b", "esm2_15b_ragged"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled_parity(device, name):
     inp = W.make_inputs(name)
-    say("full", name, "B=%d T=%d H=%d d=%d" % (len(inp["lengths"]), inp["T"], inp["H"], inp["d"]))
+    seqs, heads = _full_size_samples(name, inp)
+    say("full", name, "B=%d T=%d H=%d d=%d" % (len(inp["lengths"]), inp["T"], inp["H"], inp["d"]),
+        "seqs", seqs, "heads", heads)
     gpu = run_gpu(inp, device)
     for key in ("o", "lse", "dq", "dk", "dv"):
         assert np.isfinite(gpu[key]).all(), key
-    compare(gpu, inp, seqs=seqs, heads=heads, exact_too=(name != "esm2_3b"), label=name)
+    # the 3B-shaped workload multiplies q and k by 3 (sharpened softmax): its
+    # O against the exact oracle is reported, its gradients are asserted
+    compare(gpu, inp, seqs=seqs, heads=heads, sharpened=(name == "esm2_3b"), label=name)

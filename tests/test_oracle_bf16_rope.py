@@ -167,3 +167,77 @@ def test_float32_rotation_matches_torch_float32_and_fp64_bounds():
     # position 0 and base 0 are exact identities
     np.testing.assert_array_equal(oracle.rope_rotate_f32(x[:1], [0.0], 10000.0), x[:1])
     np.testing.assert_array_equal(oracle.rope_rotate_f32(x, pos, 0.0), x)
+
+
+# ---------------------------------------------------------------- query operand
+
+_L2E = float(np.log2(np.e))
+
+
+def _torch_query_operand(q, pos, base, scale):
+    """q^ from torch float32 elementwise ops (each product, sum and the scale
+    product rounded to float32 separately; no fused multiply-add across torch
+    ops) and torch's float32 -> bf16 conversion (round to nearest even)."""
+    d = q.shape[-1]
+    h = d // 2
+    t = torch.from_numpy(np.asarray(q, np.float64).astype(np.float32))
+    if base != 0:
+        th = float(base) ** (-2.0 * np.arange(h) / d)
+        ang = np.asarray(pos, np.float64)[:, None] * th[None, :]
+        shape = (t.shape[0],) + (1,) * (t.dim() - 2) + (h,)
+        c = torch.from_numpy(np.cos(ang).astype(np.float32)).reshape(shape)
+        s = torch.from_numpy(np.sin(ang).astype(np.float32)).reshape(shape)
+        lo, hi = t[..., :h], t[..., h:]
+        t = torch.cat([lo * c - hi * s, hi * c + lo * s], dim=-1)
+    cf = torch.tensor(scale, dtype=torch.float32) * torch.tensor(_L2E, dtype=torch.float32)
+    return (t * cf).to(torch.bfloat16).double().numpy()
+
+
+@pytest.mark.parametrize("scale,base", [(0.125, 10000.0), (48 ** -0.5, 10000.0),
+                                        (-0.2, 10000.0), (0.6, 0.0), (1e-3, 500.0)])
+def test_query_operand_matches_torch_float32(scale, base):
+    rng = np.random.default_rng(21)
+    x = oracle.round_to_bf16(rng.standard_normal((512, 4, 64)) * 3)
+    pos = np.arange(512, dtype=np.float64)
+    np.testing.assert_array_equal(oracle.query_operand_bf16(x, pos, base, scale),
+                                  _torch_query_operand(x, pos, base, scale))
+
+
+def test_query_operand_pin_rejects_plausible_variants():
+    """Each plausible mistake in the rounding recipe, planted in a copy of the
+    oracle function, disagrees with the torch pin on a sample of 2^20 rotated
+    values (the recipe's roundings differ only near bf16 ties, about 1e-5 of
+    entries, so the sample must be large)."""
+    rng = np.random.default_rng(22)
+    x = oracle.round_to_bf16(rng.standard_normal((4096, 4, 64)) * 3)
+    pos = np.arange(4096, dtype=np.float64)
+    base = 10000.0
+    scale = 48 ** -0.5   # fl32(fl32(s) fl32(log2 e)) != fl32(s log2 e) here
+    assert np.float32(np.float32(scale) * np.float32(_L2E)) != np.float32(scale * _L2E)
+    pin = _torch_query_operand(x, pos, base, scale)
+    np.testing.assert_array_equal(oracle.query_operand_bf16(x, pos, base, scale), pin)
+
+    rot = oracle.rope_rotate_f32(x, pos, base)           # float32 values
+    c32 = np.float32(scale) * np.float32(_L2E)
+    bf = oracle.round_to_bf16
+    f32 = lambda a: np.asarray(a, np.float64).astype(np.float32).astype(np.float64)
+    # 1. c rounded once from the float64 product scale * log2 e
+    m_c_once = bf(f32(rot * np.float64(np.float32(scale * _L2E))))
+    # 2. c and the scaling product kept in float64
+    m_c_fp64 = bf(rot * (scale * _L2E))
+    # 3. bf16 rounding of the rotated value before the scaling
+    m_round_first = bf(f32(bf(rot) * np.float64(c32)))
+    # 4. rotation contracted to fused multiply-adds (x c - y s with one rounding)
+    th = base ** (-2.0 * np.arange(32) / 64)
+    ang = pos[:, None] * th[None, :]
+    cs = np.cos(ang).astype(np.float32).astype(np.float64)[:, None, :]
+    sn = np.sin(ang).astype(np.float32).astype(np.float64)[:, None, :]
+    lo, hi = x[..., :32], x[..., 32:]
+    fma = np.concatenate([f32(lo * cs - f32(hi * sn)), f32(hi * cs + f32(lo * sn))], axis=-1)
+    m_fma = bf(f32(fma * np.float64(c32)))
+    # 5. sine with the wrong sign (rotation by -p)
+    m_sign = bf(f32(oracle.rope_rotate_f32(x, -pos, base) * np.float64(c32)))
+    for name, m in (("c rounded once", m_c_once), ("c in float64", m_c_fp64),
+                    ("round before scale", m_round_first), ("fused multiply-add", m_fma),
+                    ("inverse rotation", m_sign)):
+        assert (m != pin).any(), name
