@@ -17,6 +17,18 @@ records add idle gaps between the kernels, so that pass's step time,
 kernel with its average launch time from that pass; `cpu_baseline` times
 the float64 oracle on a bounded sample on the host.
 
+Extra fields, all measured after the timed region (which is untouched by
+them): `step_us_spread` (per-step times from one event per step boundary:
+median, p10, p90 and the means of the first and last five steps, which show
+the clock ramp that a short warmup leaves in the timed steps);
+`ms_per_step_settled` / `tflops_settled` (K more event-free steps once the
+process has run at least 150 steps, when the clocks are steady); `fwd_us` and
+`bwd_us` (plan + rotation + forward, and the two backward passes: median,
+p10, p90) and `kernels_us_pct`; `flushed` (each step preceded by an untimed
+512 MiB write that evicts the 256 MB last-level cache, with the step's
+algorithmic HBM bytes over its median time); `graph_replay_ms_per_step` (the
+step captured once in a HIP graph and replayed K times).
+
     python bench.py [--gpus 1] [--steps 50] [--warmup 100] [--workload esm2_650m] [--seed S]
                     [--no-cpu-baseline] [--cpu-seconds 15]
 
@@ -58,6 +70,14 @@ import numpy as np
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
 PEAK_HBM_GBS = 8000.0
+SETTLE_STEPS = 150          # steps of sustained load after which the clocks are steady
+
+
+def pct(xs):
+    """median, p10 and p90 of a list of times (us), rounded."""
+    a = np.asarray(xs, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 2), "p10": round(float(np.percentile(a, 10)), 2),
+            "p90": round(float(np.percentile(a, 90)), 2)}
 
 
 def parse():
@@ -581,6 +601,27 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    # per-step spread: K more steps with one event at each step boundary
+    # (K + 1 records), then the same after the clocks have settled
+    def step_times(n):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        evs[0].record(stream)
+        for i in range(n):
+            step()
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        return [evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(n)]  # us
+
+    spread = step_times(args.steps)
+    for _ in range(max(0, SETTLE_STEPS - args.warmup - 2 * args.steps)):
+        step()
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for i in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall_settled = time.perf_counter() - t2
+
     # instrumented pass, K more steps: events around every call give the
     # per-kernel times (kernels_us) and the dominant kernel's launch time
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
@@ -598,9 +639,48 @@ def main():
             per[n].append(ev[j].elapsed_time(ev[j + 1]) * 1e3)  # us
     avg = {n: float(np.mean(x)) for n, x in per.items()}
     step_ms = wall / args.steps * 1e3
+    fwd_us = [ev[0].elapsed_time(ev[3]) * 1e3 for ev in events]   # plan, rotation, forward
+    bwd_us = [ev[3].elapsed_time(ev[5]) * 1e3 for ev in events]   # dq pass, dk/dv pass
+
+    # flushed: a 512 MiB write (untimed, outside the events) before each step
+    # evicts the 256 MB last-level cache, so every input comes from HBM
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    fl = []
+    for i in range(args.steps):
+        flush.fill_(i & 0xFF)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        fl.append(e0.elapsed_time(e1) * 1e3)
+    del flush
+
+    # the same step captured once in a HIP graph and replayed K times
+    graph_ms = None
+    try:
+        g = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        t3 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t3) / args.steps * 1e3
+        del g
+    except RuntimeError as exc:   # capture unsupported: reported, not hidden
+        graph_ms = "capture failed: %s" % (str(exc).splitlines()[0],)
 
     fwd_f, bwd_f = W.counted_flops(inp["lengths"], H, d)
     total_f = fwd_f + bwd_f
+    # algorithmic HBM bytes of one step: forward reads q, k, v and writes o
+    # and the LSE; backward reads q, k, v, o, dO and the LSE and writes dq,
+    # dk, dv and D
+    alg_bytes = 24 * T * H * d + 12 * T * H
     tflops = total_f / (step_ms * 1e-3) / 1e12
     s2 = float(sum(L * L for L in inp["lengths"]))
     # algorithmic flops of each kernel: the method's matrix products it runs
@@ -634,6 +714,22 @@ def main():
         "tokens_per_s": round(T / (step_ms * 1e-3), 1),
         "kernels_us": {n: round(x, 2) for n, x in avg.items()},
         "ms_per_step_with_events": round(wall_events / args.steps * 1e3, 4),
+        # clock ramp: the timed steps above follow the requested warmup; the
+        # chip's clocks settle after about 40 steps of sustained load
+        "step_us_spread": dict(pct(spread), first5=round(float(np.mean(spread[:5])), 1),
+                               last5=round(float(np.mean(spread[-5:])), 1)),
+        "ms_per_step_settled": round(wall_settled / args.steps * 1e3, 4),
+        "settled_after_steps": max(SETTLE_STEPS, args.warmup + 2 * args.steps),
+        "tflops_settled": round(total_f / (wall_settled / args.steps) / 1e12, 2),
+        "fwd_us": pct(fwd_us),
+        "bwd_us": pct(bwd_us),
+        "kernels_us_pct": {n: pct(x) for n, x in per.items()},
+        "flushed": {"step_us": pct(fl),
+                    "algorithmic_bytes": alg_bytes,
+                    "hbm_gbs_median": round(alg_bytes / (float(np.median(fl)) * 1e-6) / 1e9, 1),
+                    "peak_gbs": PEAK_HBM_GBS},
+        "graph_replay_ms_per_step": (round(graph_ms, 4) if isinstance(graph_ms, float)
+                                     else graph_ms),
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
