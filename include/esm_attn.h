@@ -52,6 +52,8 @@
  * Ownership and execution
  *   The caller allocates every buffer (inputs, outputs, workspace); the library
  *   never allocates or frees memory and keeps no pointer after a call returns.
+ *   (One exception: esm_attn_fwd_noalloc works in a fixed buffer the library
+ *   itself holds in device global memory, see there.)
  *   Calls are enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *   return without waiting; there is no host-device synchronisation and no
  *   device read on the host, so the calls can be captured in a HIP graph.
@@ -93,7 +95,7 @@
 extern "C" {
 #endif
 
-#define ESM_ATTN_ABI_VERSION 4
+#define ESM_ATTN_ABI_VERSION 5
 
 typedef int32_t esm_attn_status_t;
 #define ESM_ATTN_OK 0
@@ -101,6 +103,7 @@ typedef int32_t esm_attn_status_t;
 #define ESM_ATTN_ERR_UNSUPPORTED 2
 #define ESM_ATTN_ERR_WORKSPACE_TOO_SMALL 3
 #define ESM_ATTN_ERR_HIP 4
+#define ESM_ATTN_ERR_SCRATCH_TOO_SMALL 5
 
 /* ESM_ATTN_ABI_VERSION of the built library. */
 int32_t esm_attn_abi_version(void);
@@ -133,6 +136,32 @@ esm_attn_status_t esm_attn_fwd(
     float softmax_scale, float rope_base,
     uint16_t* o, float* lse,
     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation as esm_attn_fwd, with the same arguments minus the
+ * workspace, which is instead a library-owned buffer of
+ * ESM_ATTN_NOALLOC_SCRATCH_BYTES (128 MiB) in device global memory, one copy
+ * per GPU, held from the library's load on that GPU until the process ends.
+ * The call allocates nothing (no hipMalloc, no allocating library routine);
+ * its first call on a GPU looks up that GPU's copy of the buffer.
+ * ESM_ATTN_ERR_SCRATCH_TOO_SMALL when esm_attn_fwd_workspace_bytes() of
+ * these sizes exceeds the buffer (it holds the plan and the rotated q^, k^:
+ * T*H*d up to about 33 million elements minus the plan); the other errors
+ * as for esm_attn_fwd. Every call on one
+ * GPU uses that GPU's one buffer, whose contents persist between calls:
+ * calls that overlap on one GPU (different streams, or different host
+ * threads without stream ordering) race and give wrong results; calls
+ * ordered on one stream are safe. Nothing in the buffer needs to start at
+ * zero (each call writes every byte it later reads). */
+#define ESM_ATTN_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+esm_attn_status_t esm_attn_fwd_noalloc(
+    const uint16_t* q, const uint16_t* k, const uint16_t* v,
+    const int32_t* cu_seqlens,
+    int32_t batch, int32_t total_tokens, int32_t max_seqlen,
+    int32_t num_heads, int32_t head_dim,
+    float softmax_scale, float rope_base,
+    uint16_t* o, float* lse, void* stream);
 
 /* Backward. q, k, v as given to the forward; o and lse as it returned them;
  * d_o: gradient of the loss with respect to o, bf16 [T][H][d].

@@ -21,7 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libesm_attn.so")
-SOURCES = ["api.hip", "prep.hip", "rope.hip", "fwd.hip", "bwd.hip", "batching.hip",
+SOURCES = ["api.hip", "prep.hip", "rope.hip", "fwd.hip", "bwd.hip", "batching.hip", "noalloc.hip",
            "merge.hip", "fwd_fp8.hip"]
 ARCH = "gfx950"
 

@@ -135,6 +135,8 @@ const char* esm_attn_status_string(esm_attn_status_t s) {
     case ESM_ATTN_ERR_UNSUPPORTED: return "esm_attn: unsupported size or head_dim";
     case ESM_ATTN_ERR_WORKSPACE_TOO_SMALL: return "esm_attn: workspace too small";
     case ESM_ATTN_ERR_HIP: return "esm_attn: HIP launch failed";
+    case ESM_ATTN_ERR_SCRATCH_TOO_SMALL:
+      return "esm_attn: problem larger than the 128 MiB no-allocation scratch buffer";
     default: return "esm_attn: unknown status";
   }
 }

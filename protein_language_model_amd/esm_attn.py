@@ -8,6 +8,7 @@ library is missing, every call raises; there is no fallback.
 Functions keep the C names:
   esm_attn_fwd(q, k, v, cu_seqlens, max_seqlen, softmax_scale, rope_base)
       -> (o, lse)
+  esm_attn_fwd_noalloc(...) -> (o, lse)   (same, in the library's own buffer)
   esm_attn_bwd(q, k, v, o, d_o, lse, cu_seqlens, max_seqlen, softmax_scale,
                rope_base) -> (dq, dk, dv)
 the planned steps (esm_attn_plan, esm_attn_rotate_planned,
@@ -28,7 +29,9 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libesm_attn.so")
 
-OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_HIP = range(5)
+(OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_HIP,
+ ERR_SCRATCH_TOO_SMALL) = range(6)
+NOALLOC_SCRATCH_BYTES = 128 << 20   # ESM_ATTN_NOALLOC_SCRATCH_BYTES
 
 EXPORTED = (
     "esm_attn_abi_version",
@@ -36,6 +39,7 @@ EXPORTED = (
     "esm_attn_fwd_workspace_bytes",
     "esm_attn_bwd_workspace_bytes",
     "esm_attn_fwd",
+    "esm_attn_fwd_noalloc",
     "esm_attn_bwd",
     "esm_attn_plan_bytes",
     "esm_attn_plan",
@@ -90,6 +94,9 @@ def lib():
     L.esm_attn_fwd.restype = i32
     L.esm_attn_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, f32, vp, vp, vp,
                                u64, vp]
+    L.esm_attn_fwd_noalloc.restype = i32
+    L.esm_attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, f32, vp,
+                                       vp, vp]
     L.esm_attn_bwd.restype = i32
     L.esm_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, f32,
                                vp, vp, vp, vp, u64, vp]
@@ -261,6 +268,27 @@ def esm_attn_fwd(q, k, v, cu_seqlens, max_seqlen, softmax_scale=None, rope_base=
     _check(lib().esm_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), B, T,
                               int(max_seqlen), H, d, scale, float(rope_base), _ptr(out),
                               _ptr(lse), _ptr(ws), _nbytes(ws), _stream(stream)))
+    return out, lse
+
+
+def esm_attn_fwd_noalloc(q, k, v, cu_seqlens, max_seqlen, softmax_scale=None,
+                         rope_base=10000.0, out=None, lse=None, stream=None):
+    """Forward in the library's own fixed device buffer (no workspace; the C
+    call allocates nothing). Pass out and lse to allocate nothing here either.
+    Returns (o bf16 [T,H,d], lse fp32 [H,T])."""
+    T, H, d = _check_qkv(q, k, v)
+    B = _check_cu(cu_seqlens, q.device)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    _check_packed((T, H, d), out)
+    _check_lse(lse, H, T)
+    _on_gpu(q.device, out, lse)
+    _check(lib().esm_attn_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), B, T,
+                                      int(max_seqlen), H, d, scale, float(rope_base), _ptr(out),
+                                      _ptr(lse), _stream(stream)))
     return out, lse
 
 

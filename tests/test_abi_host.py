@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported():
     for n in names:
         assert hasattr(lib, n), n
     assert set(E.EXPORTED) == set(names)
-    assert E.esm_attn_abi_version() == 4
+    assert E.esm_attn_abi_version() == 5
 
 
 def test_single_hip_runtime_is_mapped():
@@ -39,7 +39,7 @@ def test_single_hip_runtime_is_mapped():
 
 
 def test_status_strings():
-    for s in range(5):
+    for s in range(6):
         assert E.status_string(s).startswith("esm_attn:")
     assert "unknown" in E.status_string(99)
 
@@ -358,3 +358,28 @@ def test_binding_rejects_malformed_outputs():
         E._workspace(32, torch.device("cpu"), torch.zeros(64, dtype=torch.uint8))
     assert E._nbytes(torch.zeros(10, dtype=torch.float32)) == 40
 
+
+def _noalloc(**kw):
+    args = dict(q=1 << 12, k=1 << 12, v=1 << 12, cu=1 << 12, B=1, T=8, maxL=8, H=1, d=64,
+                scale=0.125, base=10000.0, o=1 << 12, lse=1 << 12, stream=NULL)
+    args.update(kw)
+    a = args
+    return E.lib().esm_attn_fwd_noalloc(a["q"], a["k"], a["v"], a["cu"], a["B"], a["T"],
+                                        a["maxL"], a["H"], a["d"], a["scale"], a["base"], a["o"],
+                                        a["lse"], a["stream"])
+
+
+def test_noalloc_forward_rejects_before_touching_the_gpu():
+    assert _noalloc(d=48) == E.ERR_UNSUPPORTED
+    assert _noalloc(B=0) == E.ERR_INVALID_ARGUMENT
+    assert _noalloc(scale=float("nan")) == E.ERR_INVALID_ARGUMENT
+    assert _noalloc(T=0) == E.OK
+    assert _noalloc(q=None) == E.ERR_INVALID_ARGUMENT
+    assert _noalloc(o=(1 << 12) + 4) == E.ERR_INVALID_ARGUMENT     # misaligned
+    # sizes whose workspace exceeds the fixed buffer: a clear error, nothing enqueued
+    T, H, d = 262144, 4, 128            # 2 * T*H*d*2 bytes of rotated q, k = 512 MiB
+    assert E.esm_attn_fwd_workspace_bytes(64, T, 4096, H, d) > E.NOALLOC_SCRATCH_BYTES
+    assert _noalloc(B=64, T=T, maxL=4096, H=H, d=d) == E.ERR_SCRATCH_TOO_SMALL
+    assert "no-allocation" in E.status_string(E.ERR_SCRATCH_TOO_SMALL)
+    # the 650M-shaped training batch fits
+    assert E.esm_attn_fwd_workspace_bytes(16, 16384, 1024, 20, 64) <= E.NOALLOC_SCRATCH_BYTES
