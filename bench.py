@@ -3,7 +3,9 @@
 A step is one pass of the whole path over one packed batch held in HBM:
 plan (varlen schedule + rotary table), rotation of q and k, forward (O, LSE),
 backward dq pass (with D = rowsum(dO*O) and the inverse-rotation finalize)
-and dk/dv pass.
+and dk/dv pass. A batch whose sequences all fit one 128-row work item
+(max_seqlen <= 128, d <= 64) takes the library's small-batch path instead:
+esm_attn_fwd and esm_attn_bwd, one launch each.
 The default workload is the ESM-2-650M-shaped dense batch: 16 sequences of
 1024 tokens, 20 heads, head dim 64, bf16, RoPE base 10000.
 
@@ -568,13 +570,27 @@ def main():
     drow = E.drow_buffer(H, T, dev)
     plan = torch.empty(E.esm_attn_plan_bytes(B, T, maxL, H, d), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
-    names = ["plan", "rotate", "fwd", "bwd_dq", "bwd_dkv"]
+    # batches whose sequences all fit one 128-row work item (d <= 64) take the
+    # library's small-batch path: the one-shot calls, one launch each way
+    small = maxL <= 128 and d <= 64
+    names = ["fwd", "bwd"] if small else ["plan", "rotate", "fwd", "bwd_dq", "bwd_dkv"]
+    ws_f = torch.empty(E.esm_attn_fwd_workspace_bytes(B, T, maxL, H, d), dtype=torch.uint8,
+                       device=dev)
+    ws_b = torch.empty(E.esm_attn_bwd_workspace_bytes(B, T, maxL, H, d), dtype=torch.uint8,
+                       device=dev)
 
     def step(ev=None):
         def mark(j):
             if ev is not None:
                 ev[j].record(stream)
         mark(0)
+        if small:
+            E.esm_attn_fwd(q, k, v, cu, maxL, scale, base, out=o, lse=lse, workspace=ws_f)
+            mark(1)
+            E.esm_attn_bwd(q, k, v, o, do, lse, cu, maxL, scale, base, dq=dq, dk=dk, dv=dv,
+                           workspace=ws_b)
+            mark(2)
+            return
         E.esm_attn_plan(cu, T, maxL, H, d, base, plan=plan)
         mark(1)
         E.esm_attn_rotate_planned(q, k, B, maxL, plan, base, q_rot=qr, k_rot=kr,
@@ -639,8 +655,9 @@ def main():
             per[n].append(ev[j].elapsed_time(ev[j + 1]) * 1e3)  # us
     avg = {n: float(np.mean(x)) for n, x in per.items()}
     step_ms = wall / args.steps * 1e3
-    fwd_us = [ev[0].elapsed_time(ev[3]) * 1e3 for ev in events]   # plan, rotation, forward
-    bwd_us = [ev[3].elapsed_time(ev[5]) * 1e3 for ev in events]   # dq pass, dk/dv pass
+    nf = 1 if small else 3   # events: forward = plan, rotation, forward; then the backward
+    fwd_us = [ev[0].elapsed_time(ev[nf]) * 1e3 for ev in events]
+    bwd_us = [ev[nf].elapsed_time(ev[len(names)]) * 1e3 for ev in events]
 
     # flushed: a 512 MiB write (untimed, outside the events) before each step
     # evicts the 256 MB last-level cache, so every input comes from HBM
@@ -686,11 +703,12 @@ def main():
     # algorithmic flops of each kernel: the method's matrix products it runs
     kernel_flops = {"fwd": 4 * s2 * H * d,            # S = QK^T, O = PV
                     "bwd_dq": 6 * s2 * H * d,         # S, dP = dO V^T, dQ = dS K
-                    "bwd_dkv": 8 * s2 * H * d}        # S, dP, dV = P^T dO, dK = dS^T Q
-    dom = max(kernel_flops, key=lambda n: avg[n])
+                    "bwd_dkv": 8 * s2 * H * d,        # S, dP, dV = P^T dO, dK = dS^T Q
+                    "bwd": 10 * s2 * H * d}           # small path: the five products at once
+    dom = max([n for n in names if n in kernel_flops], key=lambda n: avg[n])
     achieved = kernel_flops[dom] / (avg[dom] * 1e-6) / 1e12
     kernel_symbol = {"fwd": "fwd_kernel<%d" % d, "bwd_dq": "bwd_dq_kernel<%d" % d,
-                     "bwd_dkv": "bwd_dkv_kernel<%d" % d}[dom]
+                     "bwd_dkv": "bwd_dkv_kernel<%d" % d, "bwd": "bwd_dkv_kernel<%d" % d}[dom]
     traffic = measured_traffic(args.workload, kernel_symbol)
 
     out = {
@@ -708,6 +726,8 @@ def main():
         "data": "synthetic (seeded N(0,1) bf16 activations, packed varlen batch)",
         "config": {"workload": "%s: %d sequences, %d tokens, H=%d, d=%d, RoPE base %g"
                                % (inp["name"], B, T, H, d, base),
+                   "path": ("small-batch (one launch forward, one backward)" if small else
+                            "planned (plan, rotation, forward, dq pass, dk/dv pass)"),
                    "global_batch": B, "seq_len": maxL, "tokens": T, "seed": seed,
                    "parallelism": "single GPU"},
         "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),

@@ -115,8 +115,8 @@ const char* esm_attn_status_string(esm_attn_status_t status);
  * (a pure host computation; 0 for arguments the calls would reject). The
  * workspace holds the plan (rotary cos/sin table and work-item schedule), the
  * rotated q^ and k^ (bf16 [T][H][d] each) and, for the backward, drow
- * ([2][H][T] entries of 8 bytes: the row sums D = rowsum(dO * O), then
- * LSE * log2(e)). */
+ * ([H][T] entries of 16 bytes: LSE * log2(e) and the row sum
+ * D = rowsum(dO * O), each negated and split into three bf16 values). */
 size_t esm_attn_fwd_workspace_bytes(int32_t batch, int32_t total_tokens,
                                     int32_t max_seqlen, int32_t num_heads,
                                     int32_t head_dim);
@@ -320,7 +320,7 @@ esm_attn_status_t esm_attn_merge_partials(
  * grad_row_stride (they may interleave in one [T][3][H][d] gradient; they
  * must not overlap any input). softmax_scale: the one q_rot was made with.
  * drow: caller-provided device buffer of 16 * H * T bytes, 16-byte aligned
- * ([2][H][T] entries of 8 bytes: -D = -rowsum(dO * O), then -LSE * log2(e),
+ * ([H][T] entries of 16 bytes: -LSE * log2(e), then -D = -rowsum(dO * O),
  * each split into three bf16 values). passes is a
  * bit mask: ESM_ATTN_PASS_DQ runs the dq pass (reads o and lse, writes dq and
  * drow), ESM_ATTN_PASS_DKV the dk/dv pass (reads drow, writes dk and dv);

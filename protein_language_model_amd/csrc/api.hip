@@ -15,7 +15,7 @@ using namespace esm;
 
 constexpr size_t kAlign = 256;
 constexpr int32_t kMaxSplit = 64;  // key chunks / partials per merge
-constexpr size_t kDrowEntryBytes = 8;  // per row of drow (see bwd.hip)
+constexpr size_t kDrowEntryBytes = 16;  // per row of drow (see bwd.hip)
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
@@ -41,8 +41,8 @@ esm_attn_status_t check_sizes(int32_t B, int32_t T, int32_t maxL, int32_t H, int
 }
 
 // Plan = rotary table + schedule. The one-shot calls append the rotated q~
-// and k~ ([T][H][d] bf16 each) and, for the backward, drow ([2][H][T]
-// entries of 8 bytes: -D and -LSE log2 e split into three bf16 values).
+// and k~ ([T][H][d] bf16 each) and, for the backward, drow ([H][T] entries
+// of 16 bytes: -LSE log2 e, then -D, each split into three bf16 values).
 Layout make_layout(int32_t B, int32_t T, int32_t maxL, int32_t H, int32_t d, bool bwd) {
   Layout l;
   l.n_chunks = (int32_t)schedule_num_chunks(B, H);
@@ -62,7 +62,7 @@ Layout make_layout(int32_t B, int32_t T, int32_t maxL, int32_t H, int32_t d, boo
   const size_t elems = (size_t)T * H * d;
   l.qrot = take(elems * sizeof(uint16_t));
   l.krot = take(elems * sizeof(uint16_t));
-  if (bwd) l.drow = take((size_t)2 * T * H * kDrowEntryBytes);
+  if (bwd) l.drow = take((size_t)T * H * kDrowEntryBytes);
   l.total = off;
   return l;
 }
@@ -98,6 +98,29 @@ void fill_common(AttnArgs* a, int32_t T, int32_t H, float scale) {
   a->H = H;
   a->scale = scale;
   a->q_sign = scale < 0.f ? -1.f : 1.f;  // (the bf16 kernels' q~ carries the sign)
+}
+
+// The one-shot calls take the small-batch path (one launch each, no plan,
+// no rotation pass) when every sequence fits one 128-row work item.
+bool small_path(int32_t max_seqlen, int32_t head_dim) {
+  return max_seqlen <= kSmallMaxLen && head_dim <= 64;
+}
+
+AttnArgs small_args(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* cu,
+                    int32_t B, int32_t T, int32_t maxL, int32_t H, int32_t d, float scale,
+                    float rope_base) {
+  AttnArgs a = {};
+  a.q = q;  // raw q and k: the small-path kernels rotate them
+  a.k = k;
+  a.v = v;
+  a.cu = cu;
+  a.B = B;
+  a.max_seqlen = maxL;
+  a.rope_base = rope_base;
+  a.q_mul = scale * kLog2e;  // as in esm_attn_rotate_planned
+  a.ld_qkv = H * d;
+  fill_common(&a, T, H, scale);
+  return a;
 }
 
 esm_attn_status_t run_prep(const int32_t* cu, int32_t B, int32_t T, int32_t maxL, int32_t H,
@@ -468,6 +491,15 @@ esm_attn_status_t esm_attn_fwd(const uint16_t* q, const uint16_t* k, const uint1
   const Layout l = make_layout(batch, total_tokens, max_seqlen, num_heads, head_dim, false);
   if (workspace_bytes < l.total) return ESM_ATTN_ERR_WORKSPACE_TOO_SMALL;
   if (max_seqlen == 0) return ESM_ATTN_OK;
+  if (small_path(max_seqlen, head_dim)) {
+    AttnArgs a = small_args(q, k, v, cu_seqlens, batch, total_tokens, max_seqlen, num_heads,
+                            head_dim, softmax_scale, rope_base);
+    a.out = o;
+    a.lse = lse;
+    return launch_fwd_small(head_dim, a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+               ? ESM_ATTN_OK
+               : ESM_ATTN_ERR_HIP;
+  }
   char* ws = static_cast<char*>(workspace);
   uint16_t* qr = reinterpret_cast<uint16_t*>(ws + l.qrot);
   uint16_t* kr = reinterpret_cast<uint16_t*>(ws + l.krot);
@@ -503,6 +535,20 @@ esm_attn_status_t esm_attn_bwd(const uint16_t* q, const uint16_t* k, const uint1
   const Layout l = make_layout(batch, total_tokens, max_seqlen, num_heads, head_dim, true);
   if (workspace_bytes < l.total) return ESM_ATTN_ERR_WORKSPACE_TOO_SMALL;
   if (max_seqlen == 0) return ESM_ATTN_OK;
+  if (small_path(max_seqlen, head_dim)) {
+    AttnArgs a = small_args(q, k, v, cu_seqlens, batch, total_tokens, max_seqlen, num_heads,
+                            head_dim, softmax_scale, rope_base);
+    a.o = o;
+    a.dout = d_o;
+    a.lse_in = lse;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.ld_grad = num_heads * head_dim;
+    return launch_bwd_small(head_dim, a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+               ? ESM_ATTN_OK
+               : ESM_ATTN_ERR_HIP;
+  }
   char* ws = static_cast<char*>(workspace);
   uint16_t* qr = reinterpret_cast<uint16_t*>(ws + l.qrot);
   uint16_t* kr = reinterpret_cast<uint16_t*>(ws + l.krot);

@@ -20,7 +20,8 @@
 // FMA or subtraction per score: an MFMA blocks vector issue for fewer cycles
 // than the 16 vector instructions of a 32x32 tile. In the dkv pass the
 // values vary along the lane's 16 rows, so the dq pass stores them already
-// split (8 bytes per row, drow) and the dkv pass reads them from LDS.
+// split (drow: one 16-byte entry per row, -lse2 then -D) and the dkv pass
+// reads them from LDS.
 // q~ and k~ come rotated from the rotation pass. The streamed operands (k~
 // and v in the dq pass; q~, dO, LSE and D in the dkv pass) are copied from
 // global memory into swizzled LDS tiles by global_load_lds, in a ring of
@@ -29,6 +30,7 @@
 // dO^T) read the same row-major tiles with the LDS transpose load.
 #include "common.h"
 #include "prep.h"
+#include "schedule.h"
 #include "tile.h"
 
 namespace esm {
@@ -51,15 +53,18 @@ struct DqCfg {
   static constexpr int LDS = NSTAGE * STAGE > EPI ? NSTAGE * STAGE : EPI;
   // launch bound (minimum workgroups per CU the register budget must allow);
   // up to d = 64 the pass fits three per CU anyway (152 VGPRs at d = 64)
-  static constexpr int OCC = 2;
+  static constexpr int OCC = D == 128 ? 2 : 3;
   using Loader = TilePair<D, BN>;
   static constexpr int LOADS = Loader::LOADS_PER_WAVE;  // per wave and block
+  // k-steps per batch of A-row reads (k~ and v rows, one wait per batch); at
+  // d = 128 the rows are read one k-step at a time (no registers to spare)
+  static constexpr int RB = D == 128 ? 0 : (NS < 4 ? NS : 4);
 };
 
-// (Unlike the other passes, the dq pass does not skip the work of waves whose
-// rows all lie past the end: the early exit raised its register use at
-// d = 64 from 152 to 174 VGPRs, three resident waves per SIMD to two, and
-// slowed it by 10 % even on batches without such waves.)
+// (A wave whose rows all lie past the end skips the block work through a
+// separate copies-and-barriers loop after the prologue, not an early exit
+// inside the block body: that exit raised the pass's register use at d = 64
+// from 152 to 174 VGPRs, three resident waves per SIMD to two.)
 template <int D, bool ROPE>
 __global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(AttnArgs a) {
   using C = DqCfg<D>;
@@ -135,11 +140,8 @@ __global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(AttnArgs a) 
   const u32x4 a_one = fold_ones(g);
   const u32x2 tlse = neg_bf16_triple(lse2), td = neg_bf16_triple(Dq);
   const u32x4 b_neglse = fold_operand(tlse, g), b_negd = fold_operand(td, g);
-  if (qvalid && g == 0) {  // -D and -lse2, split, for the dkv pass's folds
-    u32x2* R = reinterpret_cast<u32x2*>(a.drow);
-    R[rowidx] = td;
-    R[(int64_t)a.H * a.T + rowidx] = tlse;
-  }
+  if (qvalid && g == 0)  // -lse2 and -D, split, for the dkv pass's folds
+    reinterpret_cast<u32x4*>(a.drow)[rowidx] = u32x4{tlse[0], tlse[1], td[0], td[1]};
 
   // blocks 1 .. NSTAGE-2 after the prologue's global loads (see the wait below)
 #pragma unroll
@@ -147,6 +149,10 @@ __global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(AttnArgs a) 
     if (j < nkb) issue(j, j);
 
   const int xk = swz<D>(prow);
+  // byte offset in a tile of the lane's A-operand row chunk for k-step s
+  uint32_t lrow[C::NS];
+#pragma unroll
+  for (int s = 0; s < C::NS; ++s) lrow[s] = 2 * (prow * D + 8 * ((2 * s + g) ^ xk));
   const TrRows<D> kread(lane);  // transposed reads of the k~ tile
   f32x16 dqacc[C::ND];
 #pragma unroll
@@ -165,23 +171,31 @@ __global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(AttnArgs a) 
       wait_vmem<0>();
     block_barrier();
     if (kb + C::NSTAGE - 1 < nkb) issue(kb + C::NSTAGE - 1, next);
-    const uint16_t* Ks = lds + stage * C::STAGE;
-    const uint16_t* Vs = Ks + C::TILE;
+    const uint16_t* Ks = lds + stage * C::STAGE;  // then the v tile (+ TILE)
     stage = stage + 1 == C::NSTAGE ? 0 : stage + 1;
     next = next + 1 == C::NSTAGE ? 0 : next + 1;
     const int lim = L - kb * C::BN;  // valid keys in this block
 
     u32x4 dsreg[C::NU];
+    // lane addresses of the A rows (keys prow of tile 0) of each k-step
+    uint32_t arow[C::NS];
 #pragma unroll
-    for (int t = 0; t < C::NT; ++t) {
+    for (int s = 0; s < C::NS; ++s) arow[s] = lds_addr(Ks) + lrow[s];
+    auto tile = [&](auto tt) {
+      constexpr int t = decltype(tt)::value;
       f32x16 sacc = mfma32(a_one, b_neglse, f32x16{});  // -lse2, then + S'
       f32x16 pacc = f32x16{};
-      const int rowoff = (32 * t + prow) * D;
+      // S'^T += K~ Q~^T and dP^T += V dO^T: k~ rows of tile t, v rows (the next tile)
+      if constexpr (C::RB > 0) {
+        mfma_rows2<C::NS, C::RB, 64 * D * t, 2 * C::TILE + 64 * D * t>(arow, qreg, doreg, sacc,
+                                                                        pacc);
+      } else {
 #pragma unroll
-      for (int s = 0; s < C::NS; ++s) {
-        const int off = rowoff + 8 * ((2 * s + g) ^ xk);
-        sacc = mfma32(ld16(Ks + off), qreg[s], sacc);
-        pacc = mfma32(ld16(Vs + off), doreg[s], pacc);
+        for (int s = 0; s < C::NS; ++s) {
+          const int off = (32 * t + prow) * D + 8 * ((2 * s + g) ^ xk);
+          sacc = mfma32(ld16(Ks + off), qreg[s], sacc);
+          pacc = mfma32(ld16(Ks + C::TILE + off), doreg[s], pacc);
+        }
       }
       pacc = mfma32(a_one, b_negd, pacc);  // pacc = dP - D
       float dsv[16];
@@ -197,7 +211,9 @@ __global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(AttnArgs a) 
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           dsreg[2 * t + hh][e] = pack_bf16(dsv[8 * hh + 2 * e], dsv[8 * hh + 2 * e + 1]);
-    }
+    };
+    tile(std::integral_constant<int, 0>{});
+    if constexpr (C::NT == 2) tile(std::integral_constant<int, 1>{});
 #pragma unroll
     for (int dt = 0; dt < C::ND; ++dt) {
       u32x4 at[C::NU];
@@ -261,15 +277,123 @@ struct DkvCfg {
   static constexpr int LDS = NSTAGE * STAGE > EPI ? NSTAGE * STAGE : EPI;
   static constexpr int OCC = D == 128 ? 2 : 3;
   using Loader = TilePair<D, BQ>;
-  static constexpr int LOADS = Loader::LOADS_PER_WAVE + 1;  // + a half row of lse2 or D
+  static constexpr int LOADS = Loader::LOADS_PER_WAVE + 1;  // + a quarter of the drow entries
+  // k-steps per batch of A-row reads (q~ and dO rows, one wait per batch); at
+  // d = 128 the rows are read one k-step at a time (no registers to spare)
+  static constexpr int RB = D == 128 ? 0 : 1;
 };
 
-template <int D, bool ROPE>
-__global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkv_kernel(AttnArgs a) {
-  using C = DkvCfg<D>;
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[C::LDS];
+// Small-batch prologue of the dk/dv kernel (see SMALL below): the rotary
+// table of positions 0 .. L-1 in LDS; for every row p < 128 the rotated
+// q~ (times q_mul, as the rotation pass makes it) and dO into query stage
+// p / 64, the rotated k~ into the k~ tile; the dS tile cleared; and per
+// query row the fold operands -lse2 and -D formed exactly as the dq pass
+// forms them (D = dO . O summed over d = 16 s + e, then over d = 16 s + 8 + e,
+// then the two parts added). Rows past the end are zero.
+template <int D, typename C>
+__device__ __forceinline__ void small_prologue(const AttnArgs& a, uint16_t* lds, uint16_t* KTs,
+                                               uint16_t* DSs, int L, int seq0, int h, int tid) {
+  float2* tab = reinterpret_cast<float2*>(DSs + kSmallMaxLen * kSmallMaxLen);
+  const bool rope = a.rope_base != 0.f;
+  for (int i = tid; i < L * (D / 2); i += 256)
+    tab[i] = rope ? rope_cs(i / (D / 2), i % (D / 2), D, (double)a.rope_base)
+                  : make_float2(1.f, 0.f);
+  for (int i = tid; i < kSmallMaxLen * kSmallMaxLen / 8; i += 256) st16(DSs + 8 * i, zero4());
+  __syncthreads();
+  const int rs = a.ld_qkv, rso = a.H * D;
+  const uint16_t* __restrict__ Qg = a.q + (int64_t)seq0 * rs + (int64_t)h * D;
+  const uint16_t* __restrict__ Kg = a.k + (int64_t)seq0 * rs + (int64_t)h * D;
+  const uint16_t* __restrict__ dOg = a.dout + (int64_t)seq0 * rso + (int64_t)h * D;
+  const uint16_t* __restrict__ Og = a.o + (int64_t)seq0 * rso + (int64_t)h * D;
+  for (int u = tid; u < kSmallMaxLen * (D / 16); u += 256) {
+    const int p = u / (D / 16), c = u % (D / 16), j0 = 8 * c;
+    u32x4 ql = zero4(), qh = zero4(), kl = zero4(), kh = zero4(), ol = zero4(), oh = zero4();
+    if (p < L) {
+      ql = ld16(Qg + p * rs + j0);
+      qh = ld16(Qg + p * rs + j0 + D / 2);
+      kl = ld16(Kg + p * rs + j0);
+      kh = ld16(Kg + p * rs + j0 + D / 2);
+      ol = ld16(dOg + p * rso + j0);
+      oh = ld16(dOg + p * rso + j0 + D / 2);
+      float lo[8], hi[8];
+      unpack8(ql, lo);
+      unpack8(qh, hi);
+      if (rope) rotate8<false, false>(lo, hi, tab + p * (D / 2) + j0);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        lo[e] *= a.q_mul;
+        hi[e] *= a.q_mul;
+      }
+      ql = pack8(lo);
+      qh = pack8(hi);
+      if (rope) {
+        unpack8(kl, lo);
+        unpack8(kh, hi);
+        rotate8<false, false>(lo, hi, tab + p * (D / 2) + j0);
+        kl = pack8(lo);
+        kh = pack8(hi);
+      }
+    }
+    uint16_t* Qs = lds + (p / C::BQ) * C::STAGE;
+    const int row = p % C::BQ;
+    st16(Qs + tile_off<D>(row, c), ql);
+    st16(Qs + tile_off<D>(row, c + D / 16), qh);
+    st16(Qs + C::TILE + tile_off<D>(row, c), ol);
+    st16(Qs + C::TILE + tile_off<D>(row, c + D / 16), oh);
+    st16(KTs + tile_off<D>(p, c), kl);
+    st16(KTs + tile_off<D>(p, c + D / 16), kh);
+  }
+  for (int p = tid; p < kSmallMaxLen; p += 256) {
+    float lse2 = 0.f, Dq = 0.f;
+    if (p < L) {
+      float part[2] = {0.f, 0.f};
+#pragma unroll
+      for (int gg = 0; gg < 2; ++gg)
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) {
+          float fo[8], fd[8];
+          unpack8(ld16(Og + p * rso + 16 * s + 8 * gg), fo);
+          unpack8(ld16(dOg + p * rso + 16 * s + 8 * gg), fd);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) part[gg] = fmaf(fd[e], fo[e], part[gg]);
+        }
+      Dq = part[0] + part[1];
+      lse2 = a.lse_in[(int64_t)h * a.T + seq0 + p] * kLog2e;
+    }
+    const u32x2 tl = neg_bf16_triple(lse2), td = neg_bf16_triple(Dq);
+    float* Fs = reinterpret_cast<float*>(lds + (p / C::BQ) * C::STAGE + 2 * C::TILE);
+    reinterpret_cast<u32x4*>(Fs)[entry_slot(p % C::BQ)] = u32x4{tl[0], tl[1], td[0], td[1]};
+  }
+  __syncthreads();
+}
 
-  const Item it = a.items[blockIdx.x];
+// SMALL: the small-batch path (every sequence at most 128 tokens, d <= 64):
+// one workgroup per (sequence, head), read from cu_seqlens, computes dq as
+// well, so no dq pass runs. q and k are the raw inputs, rotated here as the
+// rotation pass does (rotary table in LDS); the prologue also forms D and
+// the fold operands the dq pass would have stored. The bf16 dS of every
+// (key, query) pair is kept in an LDS tile [128 keys][128 queries]; after
+// the query loop wave w computes dQ~^T of queries 32w .. 32w+31 as
+// K~^T dS^T over all 128 keys, in the key order of the dq pass.
+template <int D, bool ROPE, bool SMALL = false>
+__global__ __launch_bounds__(256, SMALL ? 1 : DkvCfg<D>::OCC) void bwd_dkv_kernel(AttnArgs a) {
+  using C = DkvCfg<D>;
+  static_assert(!SMALL || (C::BQ == 64 && C::BK == kSmallMaxLen && C::NSTAGE >= 2), "small path");
+  constexpr int KT = SMALL ? kSmallMaxLen * D : 0;                    // k~ tile [128][D]
+  constexpr int DS = SMALL ? kSmallMaxLen * kSmallMaxLen : 0;         // dS tile [128][128]
+  constexpr int TAB = SMALL ? kSmallMaxLen * (D / 2) * 4 : 0;         // float2 [128][D/2]
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[C::LDS + KT + DS + TAB];
+
+  Item it;
+  if constexpr (SMALL) {
+    const int b = (int)blockIdx.x / a.H;
+    it.head = (int)blockIdx.x - b * a.H;
+    it.blk = 0;
+    seq_bounds(a.cu, b, a.T, a.max_seqlen, &it.seq0, &it.len);
+    it.len = min(it.len, kSmallMaxLen);
+  } else {
+    it = a.items[blockIdx.x];
+  }
   if (it.len <= 0) return;
   const int L = it.len, h = it.head, k0 = it.blk * C::BK;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -283,23 +407,25 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkv_kernel(AttnArgs a
   const uint16_t* __restrict__ Vg = a.v + base;
   const uint16_t* __restrict__ dOg = a.dout + (int64_t)it.seq0 * rso + (int64_t)h * D;
   const int64_t row0 = (int64_t)h * a.T + it.seq0;
-  // waves 0-1 copy halves of the lse2 row, waves 2-3 halves of the D row
-  constexpr int RW = 2;  // 4-byte words per lse2 / D entry
-  const float* __restrict__ Fg =
-      a.drow + RW * ((w < 2 ? (int64_t)a.H * a.T : (int64_t)0) + row0);
+  const float* __restrict__ Fg = a.drow + 4 * row0;  // 16-byte (-lse2, -D) entries
 
   // q~, dO, lse2 and D rows of query block qb -> LDS stage `stage`
   const typename C::Loader loader(w, lane);
   auto issue = [&](int qb, int stage) {
+    if constexpr (SMALL) return;  // every block is in LDS from the prologue
     const int q0 = qb * C::BQ, lim = L - q0;
     uint16_t* Qs = lds + stage * C::STAGE;
-    float* Fs = reinterpret_cast<float*>(Qs + 2 * C::TILE) + (w < 2 ? 0 : RW * C::BQ);
+    float* Fs = reinterpret_cast<float*>(Qs + 2 * C::TILE);
     loader.load(Qg + (int64_t)q0 * rs, rs, dOg + (int64_t)q0 * rso, rso, lim, Qs, Qs + C::TILE,
                 w);
-    load_half_row_f32(Fg + RW * q0, RW * C::BQ, RW * lim, Fs, w & 1);
+    load_entries16(Fg + 4 * q0, C::BQ, lim, Fs, w);
   };
   const int nqb = (L + C::BQ - 1) / C::BQ;
-  issue(0, 0);
+  uint16_t* const KTs = lds + C::LDS;            // small path: k~ tile
+  uint16_t* const DSs = KTs + KT;                // small path: dS tile
+  const float2* const tab = reinterpret_cast<const float2*>(DSs + DS);
+  if constexpr (SMALL) small_prologue<D, C>(a, lds, KTs, DSs, L, it.seq0, it.head, tid);
+  else issue(0, 0);
 
   // ---- prologue: this lane's key k~ and v (B operands)
   const int kj = k0 + w * 32 + r;
@@ -309,7 +435,7 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkv_kernel(AttnArgs a
   u32x4 kreg[C::NS], vreg[C::NS];
 #pragma unroll
   for (int s = 0; s < C::NS; ++s) {
-    kreg[s] = ld16(Kg + kc * rs + 16 * s + 8 * g);
+    kreg[s] = SMALL ? ld16(KTs + tile_off<D>(kj, 2 * s + g)) : ld16(Kg + kc * rs + 16 * s + 8 * g);
     vreg[s] = ld16(Vg + kc * rs + 16 * s + 8 * g);
   }
 #pragma unroll
@@ -326,6 +452,10 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkv_kernel(AttnArgs a
     if (j < nqb) issue(j, j);
 
   const int xq = swz<D>(prow);
+  // byte offset in a tile of the lane's A-operand row chunk for k-step s
+  uint32_t lrow[C::NS];
+#pragma unroll
+  for (int s = 0; s < C::NS; ++s) lrow[s] = 2 * (prow * D + 8 * ((2 * s + g) ^ xq));
   const TrRows<D> tread(lane);  // transposed reads of the q~ and dO tiles
   const u32x4 b_one = fold_ones(g);
   f32x16 dvacc[C::ND], dkacc[C::ND];
@@ -359,22 +489,32 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkv_kernel(AttnArgs a
     const float* Fs = reinterpret_cast<const float*>(Qs + 2 * C::TILE);
     const int lim = L - qb * C::BQ;  // valid queries in this block
 
+    // lane addresses of the A rows (queries prow of tile 0) of each k-step
+    uint32_t arow[C::NS];
+#pragma unroll
+    for (int s = 0; s < C::NS; ++s) arow[s] = lds_addr(Qs) + lrow[s];
+
     // One 32-query tile at a time: S and dP, then P and dS, then the tile's
     // dV / dK products (keeps one tile's P and dS live, not the block's).
-#pragma unroll
-    for (int t = 0; t < C::NT; ++t) {
+    auto tile = [&](auto tt) {
+      constexpr int t = decltype(tt)::value;
       f32x16 sacc = f32x16{}, pacc = f32x16{};
-      const int rowoff = (32 * t + prow) * D;
       {  // the A rows (queries 32t + prow) bring -lse2 and -D
-        const u32x2* F8 = reinterpret_cast<const u32x2*>(Fs);
-        sacc = mfma32(fold_operand(F8[32 * t + prow], g), b_one, sacc);
-        pacc = mfma32(fold_operand(F8[C::BQ + 32 * t + prow], g), b_one, pacc);
+        const u32x4 e = reinterpret_cast<const u32x4*>(Fs)[32 * t + entry_slot(prow)];
+        sacc = mfma32(fold_operand(u32x2{e[0], e[1]}, g), b_one, sacc);
+        pacc = mfma32(fold_operand(u32x2{e[2], e[3]}, g), b_one, pacc);
       }
+      // S' += Q~ K~^T and dP += dO V^T: q~ rows of tile t, dO rows (the next tile)
+      if constexpr (C::RB > 0) {
+        mfma_rows2<C::NS, C::RB, 64 * D * t, 2 * C::TILE + 64 * D * t>(arow, kreg, vreg, sacc,
+                                                                        pacc);
+      } else {
 #pragma unroll
-      for (int s = 0; s < C::NS; ++s) {
-        const int off = rowoff + 8 * ((2 * s + g) ^ xq);
-        sacc = mfma32(ld16(Qs + off), kreg[s], sacc);
-        pacc = mfma32(ld16(Os + off), vreg[s], pacc);
+        for (int s = 0; s < C::NS; ++s) {
+          const int off = (32 * t + prow) * D + 8 * ((2 * s + g) ^ xq);
+          sacc = mfma32(ld16(Qs + off), kreg[s], sacc);
+          pacc = mfma32(ld16(Os + off), vreg[s], pacc);
+        }
       }
       // queries 32t + 16g + i, i = 0..15; P and dS overwrite S' and dP
 #pragma unroll
@@ -398,6 +538,13 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkv_kernel(AttnArgs a
           preg[hh][e] = pack_bf16(sacc[8 * hh + 2 * e], sacc[8 * hh + 2 * e + 1]);
           dsreg[hh][e] = pack_bf16(pacc[8 * hh + 2 * e], pacc[8 * hh + 2 * e + 1]);
         }
+      if constexpr (SMALL) {  // dS of key kj, queries 64 qb + 32 t + 16 g + 0..15
+        if (kj < L) {
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh)
+            st16(DSs + tile_off<kSmallMaxLen>(kj, 8 * qb + 4 * t + 2 * g + hh), dsreg[hh]);
+        }
+      }
       // rows 32t .. 32t + 31 of the dO and q~ tiles, read along the rows
       const uint32_t orow = lds_addr(Os) + 32 * t * 2 * D, qrow = lds_addr(Qs) + 32 * t * 2 * D;
 #pragma unroll
@@ -410,16 +557,57 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkv_kernel(AttnArgs a
 #pragma unroll
         for (int u = 0; u < 2; ++u) dkacc[dt] = mfma32(aq[u], dsreg[u], dkacc[dt]);
       }
-    }
+    };
+    tile(std::integral_constant<int, 0>{});
+    if constexpr (C::NT == 2) tile(std::integral_constant<int, 1>{});
   };
   const int nfull = L / C::BQ;
   for (int qb = 0; qb < nfull; ++qb) block(qb, Full{});
   if (nfull < nqb) block(nfull, Ragged{});
   __syncthreads();  // every wave is done with the tiles
 
-  // ---- epilogue: dk = R(-p) ln2 dK~ (q~ carries softmax_scale log2 e), dv
   float* F = reinterpret_cast<float*>(lds);
   constexpr int FP = D + 4;
+  const float2* const rope = SMALL ? tab : a.rope;
+  if constexpr (SMALL) {
+    // dQ~^T of queries 32 w + perm_row(r) (B columns read through the
+    // transposed dS tile) = K~^T dS^T over keys 0..63, then 64..127
+    f32x16 qacc[C::ND];
+#pragma unroll
+    for (int dt = 0; dt < C::ND; ++dt) qacc[dt] = f32x16{};
+    if (32 * w < L) {
+      const TrRows<kSmallMaxLen> dsread(lane);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        u32x4 bs[4];
+        dsread.template read<4>(lds_addr(DSs) + kb * 64 * 2 * kSmallMaxLen, w, bs);
+#pragma unroll
+        for (int dt = 0; dt < C::ND; ++dt) {
+          u32x4 ak[4];
+          tread.template read<4>(lds_addr(KTs) + kb * 64 * 2 * D, dt, ak);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) qacc[dt] = mfma32(ak[u], bs[u], qacc[dt]);
+        }
+      }
+    }
+    __syncthreads();  // the tiles under F are no longer read
+#pragma unroll
+    for (int dt = 0; dt < C::ND; ++dt) {
+      const int d0 = 32 * dt + 16 * g;
+      if (d0 < D) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          F[(w * 32 + perm_row(r)) * FP + d0 + i] = qacc[dt][i] * a.scale;
+      }
+    }
+    __syncthreads();
+    store_rows<D, ROPE>(F, kSmallMaxLen, 0, L,
+                        a.dq + (int64_t)it.seq0 * a.ld_grad + (int64_t)h * D, a.ld_grad, rope,
+                        true, tid);
+    __syncthreads();
+  }
+
+  // ---- epilogue: dk = R(-p) ln2 dK~ (q~ carries softmax_scale log2 e), dv
 #pragma unroll
   for (int dt = 0; dt < C::ND; ++dt) {
     const int d0 = 32 * dt + 16 * g;
@@ -430,7 +618,7 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkv_kernel(AttnArgs a
   }
   __syncthreads();
   const int64_t baseg = (int64_t)it.seq0 * a.ld_grad + (int64_t)h * D;
-  store_rows<D, ROPE>(F, C::BK, k0, L, a.dk + baseg, a.ld_grad, a.rope, true, tid);
+  store_rows<D, ROPE>(F, C::BK, k0, L, a.dk + baseg, a.ld_grad, rope, true, tid);
   __syncthreads();
 #pragma unroll
   for (int dt = 0; dt < C::ND; ++dt) {
@@ -441,7 +629,28 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkv_kernel(AttnArgs a
     }
   }
   __syncthreads();
-  store_rows<D, ROPE>(F, C::BK, k0, L, a.dv + baseg, a.ld_grad, a.rope, false, tid);
+  store_rows<D, ROPE>(F, C::BK, k0, L, a.dv + baseg, a.ld_grad, rope, false, tid);
+}
+
+hipError_t launch_bwd_small(int head_dim, const AttnArgs& a, hipStream_t st) {
+  const unsigned n = (unsigned)((int64_t)a.B * a.H);
+  const bool rope = a.rope_base != 0.f;
+  switch (head_dim) {
+    case 16:
+      if (rope) bwd_dkv_kernel<16, true, true><<<n, 256, 0, st>>>(a);
+      else bwd_dkv_kernel<16, false, true><<<n, 256, 0, st>>>(a);
+      break;
+    case 32:
+      if (rope) bwd_dkv_kernel<32, true, true><<<n, 256, 0, st>>>(a);
+      else bwd_dkv_kernel<32, false, true><<<n, 256, 0, st>>>(a);
+      break;
+    case 64:
+      if (rope) bwd_dkv_kernel<64, true, true><<<n, 256, 0, st>>>(a);
+      else bwd_dkv_kernel<64, false, true><<<n, 256, 0, st>>>(a);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 template <int D, bool ROPE>

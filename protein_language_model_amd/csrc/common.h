@@ -113,6 +113,14 @@ __device__ __forceinline__ void rotate8(float* lo, float* hi, const float2* cs) 
   }
 }
 
+// (cos, sin) of the angle p * theta_j, theta_j = base^(-2j/d), evaluated in
+// float64 and rounded to float32: the entries of the plan's rotary table.
+__device__ __forceinline__ float2 rope_cs(int p, int j, int d, double base) {
+  const double theta = pow(base, -2.0 * (double)j / (double)d);
+  const double ang = (double)p * theta;
+  return make_float2((float)cos(ang), (float)sin(ang));
+}
+
 // Loads (cos, sin) for the angles p * theta_{j0 .. j0+7}: 64 contiguous bytes.
 __device__ __forceinline__ void load_cs8(const float2* rope, int64_t idx, float2* cs) {
   const u32x4* p = reinterpret_cast<const u32x4*>(rope + idx);
@@ -202,6 +210,16 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float 
   return (uint32_t)v;
 }
 
+// Issue priority of the wave among the waves of its SIMD (s_setprio; 0 is
+// the default). The attention kernels raise it for their MFMA phases, so
+// that a wave which reaches its matrix products issues them ahead of the
+// other waves' vector work and the matrix pipe is fed while those waves
+// exponentiate.
+template <int P>
+__device__ __forceinline__ void wave_priority() {
+  __builtin_amdgcn_s_setprio(P);
+}
+
 // True if any lane of the wave has pred set (wave-uniform result).
 __device__ __forceinline__ bool wave_any(bool pred) { return __ballot(pred) != 0ull; }
 
@@ -209,14 +227,20 @@ __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<
 __device__ __forceinline__ void st16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 // Cooperative epilogue: fp32 tile F[rows][D + 4] in LDS (row = position
-// pos0 + row inside the sequence) -> optional inverse rotation -> bf16 global.
+// pos0 + row inside the sequence; rows a multiple of 16) -> optional inverse
+// rotation -> bf16 global. Unit u (8 rotary pairs of one row) is row
+// u % 16 + 16 (u / (16 NU)), pair block (u / 16) % NU: the 16 lanes that one
+// ds_read_b128 cycle serves read 16 consecutive rows at one column, which
+// the row pitch of D + 4 floats (4 mod 64 banks at d = 64 and 128, 36 at
+// d = 32, 20 at d = 16) places on 16 disjoint groups of 4 banks.
 template <int D, bool ROPE>
 __device__ __forceinline__ void store_rows(const float* F, int rows, int pos0, int L,
                                            uint16_t* G, int rs, const float2* rope,
                                            bool rotate, int tid) {
   constexpr int FP = D + 4;
-  for (int u = tid; u < rows * (D / 16); u += 256) {
-    const int row = u / (D / 16), j0 = (u % (D / 16)) * 8, pos = pos0 + row;
+  constexpr int NU = D / 16;  // units per row
+  for (int u = tid; u < rows * NU; u += 256) {
+    const int row = (u & 15) + 16 * (u / (16 * NU)), j0 = ((u >> 4) % NU) * 8, pos = pos0 + row;
     if (pos >= L) continue;
     float lo[8], hi[8];
 #pragma unroll

@@ -6,8 +6,12 @@
 //   global memory into the MFMA B-operand registers, kept for the whole item.
 //   For each block of 64 keys (32 at d = 128) the k~ and v rows are copied
 //   from global memory into swizzled LDS tiles by global_load_lds (no register
-//   staging, no vector instructions), in a ring of three LDS stages: the copy
-//   of block kb + 2 is issued right after the barrier that opens block kb.
+//   staging, no vector instructions), in a ring of two LDS stages: the copy
+//   of block kb + 1 is issued right after the barrier that opens block kb.
+//   With two 16 KB stages and at most 128 VGPRs, four workgroups (four waves
+//   per SIMD) are resident per CU at d <= 64. The MFMA phases (scores, P V)
+//   run at raised wave priority, so a wave that reaches its matrix products
+//   issues them ahead of the other waves' exponentials.
 //   S^T = K~ Q~^T reads k~ rows; O^T += V^T P^T reads the v tile along its
 //   key (row) axis with the LDS transpose load.
 //   Lane (q, g) of a wave holds the scores of query q against 16 keys per
@@ -40,6 +44,7 @@
 // wavefronts, 32x32x16 bf16 MFMA, LDS DMA and LDS transpose loads of CDNA4.
 #include "common.h"
 #include "prep.h"
+#include "schedule.h"
 #include "tile.h"
 
 namespace esm {
@@ -54,10 +59,14 @@ struct FwdCfg {
   static constexpr int NU = BN / 16;              // k-steps over keys
   static constexpr int TILE = BN * D;             // elements of one k~ or v tile
   static constexpr int STAGE = 2 * TILE;
-  static constexpr int NSTAGE = 3;                // LDS ring of key blocks
+  static constexpr int NSTAGE = 2;                // LDS ring of key blocks
   static constexpr int LDS = NSTAGE * STAGE;
-  static constexpr int OCC = D == 128 ? 2 : 3;    // workgroups per CU
+  // workgroups per CU: four at d <= 64 (two LDS stages of 16 KB, at most 128
+  // VGPRs), two at d = 128
+  static constexpr int OCC = D == 128 ? 2 : 4;
   using Loader = TilePair<D, BN>;
+  // k-steps per batch of k~ row reads (both tiles' rows, one wait per batch)
+  static constexpr int RB = NS < 2 ? NS : 2;
 };
 
 constexpr float kLazyBound = 65536.0f;  // 2^16: largest block sum of P kept
@@ -73,13 +82,33 @@ constexpr float kLazyBound = 65536.0f;  // 2^16: largest block sum of P kept
 // dispatch chunk y of (sequence, head) group g runs on XCD (g + y*B*H) mod 8:
 // few groups still spread over all eight XCDs, and each chunk's keys stay in
 // one XCD's L2.
-template <int D, bool SPLIT>
-__global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(AttnArgs a) {
+//
+// SMALL: the small-batch path (every sequence at most 128 tokens, d <= 64),
+// one launch with no plan: workgroup x is (sequence x / H, head x % H), read
+// from cu_seqlens; q, k are the raw inputs, rotated here exactly as the
+// rotation pass does (the rotary table built in LDS with the plan's formula),
+// and the at most two key blocks of the sequence sit in the two LDS stages
+// for the whole item.
+template <int D, bool SPLIT, bool SMALL = false>
+__global__ __launch_bounds__(256, SMALL ? 2 : FwdCfg<D>::OCC) void fwd_kernel(AttnArgs a) {
   using C = FwdCfg<D>;
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[C::LDS];
+  static_assert(!(SPLIT && SMALL), "one mode");
+  static_assert(!SMALL || (C::BN == 64 && C::NSTAGE * C::BN >= kSmallMaxLen), "small path");
+  // (the small path adds the rotary table of its positions: float2 [128][D/2])
+  constexpr int TAB = SMALL ? kSmallMaxLen * (D / 2) * 4 : 0;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[C::LDS + TAB];
 
   if (SPLIT && (int)blockIdx.x >= a.n_items) return;  // grid padding
-  const Item it = a.items[blockIdx.x];
+  Item it;
+  if constexpr (SMALL) {
+    const int b = (int)blockIdx.x / a.H;
+    it.head = (int)blockIdx.x - b * a.H;
+    it.blk = 0;
+    seq_bounds(a.cu, b, a.T, a.max_seqlen, &it.seq0, &it.len);
+    it.len = min(it.len, kSmallMaxLen);
+  } else {
+    it = a.items[blockIdx.x];
+  }
   if (it.len <= 0) return;
   const int L = it.len, h = it.head, q0 = it.blk * C::BM;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -115,6 +144,7 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(AttnArgs a) {
   const typename C::Loader loader(w, lane);
   const typename C::Loader::Offsets koff = loader.offsets(rs, w);
   auto issue = [&](int kb, int stage) {
+    if constexpr (SMALL) return;  // every block is in LDS from the prologue
     const int k0 = kb * C::BN;
     uint16_t* Ks = lds + stage * C::STAGE;
     if (k0 + C::BN <= Lk)
@@ -124,7 +154,43 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(AttnArgs a) {
                               Ks + C::TILE, w);
   };
   const int nkb = (Lk + C::BN - 1) / C::BN;
-  issue(0, 0);
+  const float2* tab = reinterpret_cast<const float2*>(lds + C::LDS);
+  if constexpr (SMALL) {
+    // rotary table of positions 0 .. L-1, then the rotated k~ rows and the v
+    // rows of key block kb into stage kb (rows past the end zero)
+    float2* tw = reinterpret_cast<float2*>(lds + C::LDS);
+    const bool rope = a.rope_base != 0.f;
+    for (int i = tid; i < L * (D / 2); i += 256)
+      tw[i] = rope ? rope_cs(i / (D / 2), i % (D / 2), D, (double)a.rope_base)
+                   : make_float2(1.f, 0.f);
+    __syncthreads();
+    for (int u = tid; u < nkb * C::BN * (D / 16); u += 256) {
+      const int p = u / (D / 16), c = u % (D / 16), j0 = 8 * c;
+      uint16_t* Ks = lds + (p / C::BN) * C::STAGE;
+      const int row = p % C::BN;
+      u32x4 kl = zero4(), kh = zero4(), vl = zero4(), vh = zero4();
+      if (p < L) {
+        kl = ld16(Kg + p * rs + j0);
+        kh = ld16(Kg + p * rs + j0 + D / 2);
+        vl = ld16(Vg + p * rs + j0);
+        vh = ld16(Vg + p * rs + j0 + D / 2);
+        if (rope) {
+          float lo[8], hi[8];
+          unpack8(kl, lo);
+          unpack8(kh, hi);
+          rotate8<false, false>(lo, hi, tab + p * (D / 2) + j0);
+          kl = pack8(lo);
+          kh = pack8(hi);
+        }
+      }
+      st16(Ks + tile_off<D>(row, c), kl);
+      st16(Ks + tile_off<D>(row, c + D / 16), kh);
+      st16(Ks + C::TILE + tile_off<D>(row, c), vl);
+      st16(Ks + C::TILE + tile_off<D>(row, c + D / 16), vh);
+    }
+  } else {
+    issue(0, 0);
+  }
 
   // queries: B operands (8 d values per k-step); rows past the end are zero.
   // The loads read a clamped row and are selected away afterwards: loads
@@ -134,6 +200,43 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(AttnArgs a) {
   u32x4 qreg[C::NS];
 #pragma unroll
   for (int s = 0; s < C::NS; ++s) qreg[s] = ld16(Qg + qc * rs + 16 * s + 8 * g);
+  if constexpr (SMALL) {
+    // q~ = bf16(fl32(q_mul fl32(R(p) q))), as the rotation pass computes it;
+    // lane (r, g) holds d = 16 s + 8 g + e, whose rotary partner d + D/2 is
+    // in k-step s + NS/2 of the same lane (d >= 32) or in lane ^ 32 (d = 16)
+    const bool rope = a.rope_base != 0.f;
+#pragma unroll
+    for (int s = 0; s < (C::NS + 1) / 2; ++s) {
+      u32x4 xl = qreg[s], xh;
+      if constexpr (C::NS == 1) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xh[e] = __shfl_xor(xl[e], 32);
+        if (g == 1) {
+          const u32x4 t = xl;
+          xl = xh;
+          xh = t;
+        }
+      } else {
+        xh = qreg[s + C::NS / 2];
+      }
+      float lo[8], hi[8];
+      unpack8(xl, lo);
+      unpack8(xh, hi);
+      if (rope) rotate8<false, false>(lo, hi, tab + qc * (D / 2) + (C::NS == 1 ? 0 : 16 * s + 8 * g));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        lo[e] *= a.q_mul;
+        hi[e] *= a.q_mul;
+      }
+      if constexpr (C::NS == 1) {
+        qreg[0] = g == 0 ? pack8(lo) : pack8(hi);
+      } else {
+        qreg[s] = pack8(lo);
+        qreg[s + C::NS / 2] = pack8(hi);
+      }
+    }
+    __syncthreads();  // the prologue's LDS tiles are complete
+  }
 #pragma unroll
   for (int s = 0; s < C::NS; ++s)
 #pragma unroll
@@ -145,6 +248,10 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(AttnArgs a) {
     if (j < nkb) issue(j, j);
 
   const int xk = swz<D>(prow);  // swizzle of the lane's k~ rows 32t + prow
+  // byte offset in the k~ tile of the lane's A-operand row chunk for k-step s
+  uint32_t lrow[C::NS];
+#pragma unroll
+  for (int s = 0; s < C::NS; ++s) lrow[s] = 2 * (prow * D + 8 * ((2 * s + g) ^ xk));
   const TrRows<D> vread(lane);  // transposed reads of the v tile
   const u32x4 a_one = fold_ones(g);
   float m = 0.f, l = 0.f;       // m in log2 units
@@ -183,13 +290,23 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(AttnArgs a) {
     const int lim = Lk - kb * C::BN;  // valid keys in this block
     f32x16 sacc[C::NT];
     auto scores = [&]() {
+      if constexpr (C::NT == 2) {
+        // both 32-key tiles at once: k~ rows prow and 32 + prow of each k-step
+        uint32_t arow[C::NS];
 #pragma unroll
-      for (int t = 0; t < C::NT; ++t) {
-        sacc[t] = mfma32(a_one, b_negm, f32x16{});
-        const uint16_t* Kr = Ks + (32 * t + prow) * D;
+        for (int s = 0; s < C::NS; ++s) arow[s] = lds_addr(Ks) + lrow[s];
+        sacc[0] = mfma32(a_one, b_negm, f32x16{});
+        sacc[1] = sacc[0];
+        mfma_rows2<C::NS, C::RB, 0, 64 * D>(arow, qreg, qreg, sacc[0], sacc[1]);
+      } else {
 #pragma unroll
-        for (int s = 0; s < C::NS; ++s)
-          sacc[t] = mfma32(ld16(Kr + 8 * ((2 * s + g) ^ xk)), qreg[s], sacc[t]);
+        for (int t = 0; t < C::NT; ++t) {
+          sacc[t] = mfma32(a_one, b_negm, f32x16{});
+          const uint16_t* Kr = Ks + (32 * t + prow) * D;
+#pragma unroll
+          for (int s = 0; s < C::NS; ++s)
+            sacc[t] = mfma32(ld16(Kr + 8 * ((2 * s + g) ^ xk)), qreg[s], sacc[t]);
+        }
       }
       if (!FULL) {
 #pragma unroll
@@ -234,7 +351,9 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(AttnArgs a) {
           }
       return sum;
     };
+    wave_priority<1>();  // (MFMA phases at raised priority, see below)
     scores();
+    wave_priority<0>();
     float lb;
     if (kb == 0) {  // no reference yet: the accumulator holds S'
       m = block_max();  // block 0 holds key 0, so m is finite
@@ -257,6 +376,7 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(AttnArgs a) {
     }
     l += lb;
 
+    wave_priority<1>();
 #pragma unroll
     for (int dt = 0; dt < C::ND; ++dt) {
       u32x4 av[C::NU];
@@ -264,6 +384,7 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(AttnArgs a) {
 #pragma unroll
       for (int u = 0; u < C::NU; ++u) oacc[dt] = mfma32(av[u], preg[u], oacc[dt]);
     }
+    wave_priority<0>();
   };
   const int nfull = Lk / C::BN;
   for (int kb = 0; kb < nfull; ++kb) block(kb, Full{});
@@ -317,6 +438,17 @@ static void launch_fwd_d(const AttnArgs& a, unsigned n, int n_split, hipStream_t
     fwd_kernel<D, true><<<dim3(n, (unsigned)n_split), 256, 0, stream>>>(a);
   else
     fwd_kernel<D, false><<<n, 256, 0, stream>>>(a);
+}
+
+hipError_t launch_fwd_small(int head_dim, const AttnArgs& a, hipStream_t stream) {
+  const unsigned n = (unsigned)((int64_t)a.B * a.H);
+  switch (head_dim) {
+    case 16: fwd_kernel<16, false, true><<<n, 256, 0, stream>>>(a); break;
+    case 32: fwd_kernel<32, false, true><<<n, 256, 0, stream>>>(a); break;
+    case 64: fwd_kernel<64, false, true><<<n, 256, 0, stream>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_fwd(int head_dim, const AttnArgs& a, int64_t n_slots, bool split,

@@ -62,7 +62,7 @@ struct AttnArgs {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
-  float* drow;          // backward: [2][H][T] x 8 bytes: -D, then -LSE log2(e), split in 3 bf16
+  float* drow;          // backward: [H][T] x 16 bytes: -LSE log2(e), then -D, each split in 3 bf16
   const float2* rope;   // [max_seqlen][d/2]
   const Item* items;
   int32_t T, H;
@@ -78,11 +78,27 @@ struct AttnArgs {
   const uint8_t* q8;    // FP8 forward: E4M3 q~, k~ [T][H][d] bytes, row stride ld8
   const uint8_t* k8;
   int32_t ld8;
+  // small-batch path (every sequence at most kSmallMaxLen tokens, d <= 64):
+  // one workgroup per (sequence, head) decoded from cu_seqlens, q and k
+  // rotated inside the attention kernels (q, k are then the raw inputs)
+  const int32_t* cu;    // [B + 1]
+  int32_t B, max_seqlen;
+  float rope_base;      // 0 = no rotation
+  float q_mul;          // fl32(softmax_scale * log2(e)), as in the rotation pass
 };
+
+// Longest sequence of the small-batch path (one 128-row work item).
+constexpr int kSmallMaxLen = 128;
 
 hipError_t launch_fwd(int head_dim, const AttnArgs& a, int64_t n_slots, bool split,
                       hipStream_t stream);
 hipError_t launch_fwd_fp8(int head_dim, const AttnArgs& a, int64_t n_slots, hipStream_t stream);
+// Small-batch path (max_seqlen <= kSmallMaxLen, head_dim <= 64): one
+// workgroup per (sequence, head), B * H of them, no plan, q and k rotated
+// inside the kernels. The forward writes o and lse; the backward writes
+// dq, dk and dv in one pass (dQ from the dS tile kept in LDS).
+hipError_t launch_fwd_small(int head_dim, const AttnArgs& a, hipStream_t stream);
+hipError_t launch_bwd_small(int head_dim, const AttnArgs& a, hipStream_t stream);
 
 // O = sum_r exp(LSE_r - LSE) O_r, LSE = log sum_r exp(LSE_r) over n_parts
 // partials o_part [n_parts][T][H][d] (fp32), lse_part [n_parts][H][T];

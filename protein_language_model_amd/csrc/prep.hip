@@ -167,13 +167,7 @@ __global__ __launch_bounds__(256) void schedule_fill_kernel(
     if (rope == nullptr || i >= (int64_t)max_seqlen * half) return;
     const int32_t p = (int32_t)(i / half);
     const int32_t j = (int32_t)(i - (int64_t)p * half);
-    float2 v = make_float2(1.0f, 0.0f);
-    if (rope_base != 0.0) {
-      const double theta = pow(rope_base, -2.0 * (double)j / (double)head_dim);
-      const double a = (double)p * theta;
-      v = make_float2((float)cos(a), (float)sin(a));
-    }
-    rope[i] = v;
+    rope[i] = rope_base != 0.0 ? rope_cs(p, j, head_dim, rope_base) : make_float2(1.0f, 0.0f);
   }
 }
 

@@ -191,16 +191,22 @@ struct TilePair {
   }
 };
 
-// Loads n <= 128 consecutive floats src[min(i, lim-1)], i < n, into LDS
-// F[0..n): wave w takes the part [w_part * n/2, (w_part + 1) * n/2) with one
-// global_load_lds_dword (4 bytes per lane).
-__device__ __forceinline__ void load_half_row_f32(const float* __restrict__ src, int n, int lim,
-                                                  float* F, int w_part) {
+// LDS slot of 16-byte row entry i (i < 32 within each group of 32): entries
+// 16..31 swap their halves of 8, so that the 16 lanes one ds_read_b128 cycle
+// serves, which read entries perm_row(r) (r < 16 or r >= 16), land on 16
+// disjoint groups of 4 banks.
+__device__ __forceinline__ int entry_slot(int i) { return i ^ ((i & 16) >> 1); }
+
+// Copies the R 16-byte entries src[min(i, lim - 1)], i < R (R = 32 or 64),
+// into LDS F at slots entry_slot(i) (4 R dwords): wave w fills dwords
+// [w R, w R + R) with one global_load_lds_dword (4 bytes per lane, lanes < R).
+__device__ __forceinline__ void load_entries16(const float* __restrict__ src, int R, int lim,
+                                               float* F, int w) {
   const int lane = lane_id_here();
-  const int half = n / 2, i = w_part * half + lane;
-  if (lane < half) {
-    const char* p = reinterpret_cast<const char*>(src) + 4u * (uint32_t)min(i, lim - 1);
-    __builtin_amdgcn_global_load_lds((gptr_t)p, (lptr_t)(F + w_part * half), 4, 0, 0);
+  if (lane < R) {
+    const int dd = w * R + lane, e = min(entry_slot(dd >> 2), lim - 1);
+    const char* p = reinterpret_cast<const char*>(src) + 4u * (uint32_t)(4 * e + (dd & 3));
+    __builtin_amdgcn_global_load_lds((gptr_t)p, (lptr_t)(F + w * R), 4, 0, 0);
   }
 }
 
@@ -209,6 +215,78 @@ __device__ __forceinline__ void load_half_row_f32(const float* __restrict__ src,
 template <int D>
 __device__ __forceinline__ u32x4 ld_row(const uint16_t* T, int row, int c) {
   return ld16(T + tile_off<D>(row, c));
+}
+
+// MFMA operand rows (ds_read_b128) in one batch: 2*NA reads, a[i] + OA and
+// a[i] + OB (immediate byte offsets) for i < NA, into out[0 .. NA) and
+// out[NA .. 2 NA), then one wait. Issuing them back to back exposes the LDS
+// latency once per batch instead of once per read (left to itself, the
+// compiler reuses one 4-register buffer and waits before every MFMA). Inline
+// assembly for the same reason as TrRows::read: the compiler would otherwise
+// wait for the global_load_lds copies still in flight first; the block waits
+// for its own reads (lgkmcnt(0)) before it ends.
+template <int NA, int OA, int OB>
+__device__ __forceinline__ void lds_rows(const uint32_t (&a)[NA], u32x4 (&out)[2 * NA]) {
+  static_assert(OA >= 0 && OB >= 0 && OA < 65536 && OB < 65536, "ds offset field");
+  if constexpr (NA == 4) {
+    asm volatile(
+        "ds_read_b128 %0, %8 offset:%12\n\t"
+        "ds_read_b128 %4, %8 offset:%13\n\t"
+        "ds_read_b128 %1, %9 offset:%12\n\t"
+        "ds_read_b128 %5, %9 offset:%13\n\t"
+        "ds_read_b128 %2, %10 offset:%12\n\t"
+        "ds_read_b128 %6, %10 offset:%13\n\t"
+        "ds_read_b128 %3, %11 offset:%12\n\t"
+        "ds_read_b128 %7, %11 offset:%13\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(out[0]), "=&v"(out[1]), "=&v"(out[2]), "=&v"(out[3]), "=&v"(out[4]),
+          "=&v"(out[5]), "=&v"(out[6]), "=&v"(out[7])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(OA), "i"(OB)
+        : "memory");
+  } else if constexpr (NA == 2) {
+    asm volatile(
+        "ds_read_b128 %0, %4 offset:%6\n\t"
+        "ds_read_b128 %2, %4 offset:%7\n\t"
+        "ds_read_b128 %1, %5 offset:%6\n\t"
+        "ds_read_b128 %3, %5 offset:%7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(out[0]), "=&v"(out[1]), "=&v"(out[2]), "=&v"(out[3])
+        : "v"(a[0]), "v"(a[1]), "i"(OA), "i"(OB)
+        : "memory");
+  } else {
+    static_assert(NA == 1, "1, 2 or 4 rows per operand");
+    asm volatile(
+        "ds_read_b128 %0, %2 offset:%3\n\t"
+        "ds_read_b128 %1, %2 offset:%4\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(out[0]), "=&v"(out[1])
+        : "v"(a[0]), "i"(OA), "i"(OB)
+        : "memory");
+  }
+}
+
+// acc0 += A0 B0 and acc1 += A1 B1 over the NS k-steps (8 d values each) of
+// one 32-row MFMA tile, where the A rows of k-step s come from LDS at lane
+// byte address a[s] + OFF0 (A0) and a[s] + OFF1 (A1) and the B operands from
+// registers: the reads in batches of NA k-steps (lds_rows: 2 NA reads, one
+// wait), each accumulator in k-step order.
+template <int NS, int NA, int OFF0, int OFF1>
+__device__ __forceinline__ void mfma_rows2(const uint32_t (&a)[NS], const u32x4 (&b0)[NS],
+                                           const u32x4 (&b1)[NS], f32x16& acc0, f32x16& acc1) {
+  static_assert(NS % NA == 0, "whole batches");
+#pragma unroll
+  for (int h = 0; h < NS / NA; ++h) {
+    uint32_t ah[NA];
+#pragma unroll
+    for (int i = 0; i < NA; ++i) ah[i] = a[h * NA + i];
+    u32x4 r[2 * NA];
+    lds_rows<NA, OFF0, OFF1>(ah, r);
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      acc0 = mfma32(r[i], b0[h * NA + i], acc0);
+      acc1 = mfma32(r[NA + i], b1[h * NA + i], acc1);
+    }
+  }
 }
 
 // Byte address in LDS of a pointer into a __shared__ array.
