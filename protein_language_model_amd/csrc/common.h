@@ -226,21 +226,42 @@ __device__ __forceinline__ bool wave_any(bool pred) { return __ballot(pred) != 0
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
 
+// Quad placement of the cooperative epilogue (below), per head dim: quad q
+// (4 consecutive lanes) of a wave's 64 units takes the row-major units
+// 4 p(q) .. 4 p(q) + 3 of the wave's stretch, p(q) being nibble q of this
+// constant. A quad then writes contiguous 16-byte pieces of one row (whole
+// rows' halves at d <= 32) to global memory, and the permutation puts the
+// four quads that share a ds_read_b128 cycle on disjoint banks of the fp32
+// tile. On gfx950 such a cycle serves the quads of one half-wave whose quad
+// index (lane bits 2..4) has one parity (fitted to single-pattern kernels
+// measured with SQ_LDS_BANK_CONFLICT); the permutations were searched and
+// checked against that rule for all four reads of a unit at a row pitch of
+// D + 4 floats (at d = 64: row 4 h + 8 b2 + 2 parity + b1 of quad bits
+// (h; b2 b1 b0)). The writes that fill the tile (8 consecutive lanes per
+// cycle over 32 banks) are conflict-free at that pitch too.
+template <int D>
+__device__ constexpr uint64_t store_quad_perm() {
+  return D == 16   ? 0xfedcba9876543210ull
+         : D == 32 ? 0xefd2184b697c5a03ull
+         : D == 64 ? 0xfdce5764b98a1320ull
+                   : 0xda1c0efb39627458ull;
+}
+
 // Cooperative epilogue: fp32 tile F[rows][D + 4] in LDS (row = position
-// pos0 + row inside the sequence; rows a multiple of 16) -> optional inverse
-// rotation -> bf16 global. Unit u (8 rotary pairs of one row) is row
-// u % 16 + 16 (u / (16 NU)), pair block (u / 16) % NU: the 16 lanes that one
-// ds_read_b128 cycle serves read 16 consecutive rows at one column, which
-// the row pitch of D + 4 floats (4 mod 64 banks at d = 64 and 128, 36 at
-// d = 32, 20 at d = 16) places on 16 disjoint groups of 4 banks.
+// pos0 + row inside the sequence; rows * D / 16 a multiple of 64) ->
+// optional inverse rotation -> bf16 global. A unit is 8 rotary pairs of one
+// row (16 bytes of each half), placed by store_quad_perm.
 template <int D, bool ROPE>
 __device__ __forceinline__ void store_rows(const float* F, int rows, int pos0, int L,
                                            uint16_t* G, int rs, const float2* rope,
                                            bool rotate, int tid) {
   constexpr int FP = D + 4;
   constexpr int NU = D / 16;  // units per row
+  constexpr uint64_t kPerm = store_quad_perm<D>();
   for (int u = tid; u < rows * NU; u += 256) {
-    const int row = (u & 15) + 16 * (u / (16 * NU)), j0 = ((u >> 4) % NU) * 8, pos = pos0 + row;
+    const int l = u & 63;
+    const int k = (u - l) + 4 * (int)((kPerm >> (4 * (l >> 2))) & 15) + (l & 3);
+    const int row = k / NU, j0 = (k % NU) * 8, pos = pos0 + row;
     if (pos >= L) continue;
     float lo[8], hi[8];
 #pragma unroll
