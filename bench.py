@@ -231,12 +231,13 @@ def attention_block(args):
         mark(1)
         if fused:
             q, k, v = qkv[:, 0], qkv[:, 1], qkv[:, 2]
-            E.esm_attn_rotate_planned(q, k, B, maxL, plan, base, q_rot=q, k_rot=k,
-                                      softmax_scale=scale)
+            E.esm_attn_rotate_planned(None, k, B, maxL, plan, base, k_rot=k, softmax_scale=scale)
+            o, lse, _ = E.esm_attn_fwd_rotq_planned(q, k, v, B, maxL, plan, scale, base, q_rot=q)
         else:
             q, k, v = qkv[:, 0].contiguous(), qkv[:, 1].contiguous(), qkv[:, 2].contiguous()
-            q, k = E.esm_attn_rotate_planned(q, k, B, maxL, plan, base, softmax_scale=scale)
-        o, lse = E.esm_attn_fwd_planned(q, k, v, B, maxL, plan, scale)
+            _, k = E.esm_attn_rotate_planned(None, k, B, maxL, plan, base, softmax_scale=scale)
+            o, lse, q = E.esm_attn_fwd_rotq_planned(q, k, v, B, maxL, plan, scale, base,
+                                                    q_rot=torch.empty_like(q))
         mark(2)
         F.linear(o.view(T, hid), wo, bo)
         dout = torch.mm(dy, wo).view(T, H, d)
@@ -337,9 +338,9 @@ def packing_study(args):
         q, k, v, do = (buf[n][:T] for n in ("q", "k", "v", "do"))
         qr, kr, o, dq, dk, dv = (outs[n][:T] for n in ("qr", "kr", "o", "dq", "dk", "dv"))
         E.esm_attn_plan(cu, T, maxL, H, d, base, plan=plan)
-        E.esm_attn_rotate_planned(q, k, B, maxL, plan, base, q_rot=qr, k_rot=kr,
-                                  softmax_scale=scale)
-        E.esm_attn_fwd_planned(qr, kr, v, B, maxL, plan, scale, out=o, lse=lse[:H * T].view(H, T))
+        E.esm_attn_rotate_planned(None, k, B, maxL, plan, base, k_rot=kr, softmax_scale=scale)
+        E.esm_attn_fwd_rotq_planned(q, kr, v, B, maxL, plan, scale, base, out=o,
+                                    lse=lse[:H * T].view(H, T), q_rot=qr)
         E.esm_attn_bwd_planned(qr, kr, v, o, do, lse[:H * T].view(H, T), B, maxL, plan, scale,
                                base, dq=dq, dk=dk, dv=dv, drow=drow[:4 * H * T])
 
@@ -493,12 +494,13 @@ def fp8_study(args):
             attn = float(np.median([e[1].elapsed_time(e[2]) * 1e3 for e in ev]))
             return prep, attn
 
-        def bf16(mid=None):
-            E.esm_attn_rotate_planned(q, k, B, maxL, plan, W.ROPE_BASE, q_rot=qr, k_rot=kr,
+        def bf16(mid=None):  # k rotation pass, then the forward that rotates q itself
+            E.esm_attn_rotate_planned(None, k, B, maxL, plan, W.ROPE_BASE, k_rot=kr,
                                       softmax_scale=1.0 / math.sqrt(d))
             if mid is not None:
                 mid.record(st)
-            E.esm_attn_fwd_planned(qr, kr, v, B, maxL, plan, out=o, lse=lse)
+            E.esm_attn_fwd_rotq_planned(q, kr, v, B, maxL, plan, None, W.ROPE_BASE, out=o,
+                                        lse=lse)
 
         def fp8(mid=None):
             E.esm_attn_quantize_fp8_planned(q, k, B, maxL, plan, qs, ks, W.ROPE_BASE, q8=q8,
@@ -593,10 +595,10 @@ def main():
             return
         E.esm_attn_plan(cu, T, maxL, H, d, base, plan=plan)
         mark(1)
-        E.esm_attn_rotate_planned(q, k, B, maxL, plan, base, q_rot=qr, k_rot=kr,
-                                  softmax_scale=scale)
+        E.esm_attn_rotate_planned(None, k, B, maxL, plan, base, k_rot=kr, softmax_scale=scale)
         mark(2)
-        E.esm_attn_fwd_planned(qr, kr, v, B, maxL, plan, scale, out=o, lse=lse)
+        E.esm_attn_fwd_rotq_planned(q, kr, v, B, maxL, plan, scale, base, out=o, lse=lse,
+                                    q_rot=qr)
         mark(3)
         E.esm_attn_bwd_planned(qr, kr, v, o, do, lse, B, maxL, plan, scale, base, dq=dq,
                                drow=drow, passes=E.PASS_DQ)

@@ -95,7 +95,7 @@
 extern "C" {
 #endif
 
-#define ESM_ATTN_ABI_VERSION 5
+#define ESM_ATTN_ABI_VERSION 6
 
 typedef int32_t esm_attn_status_t;
 #define ESM_ATTN_OK 0
@@ -114,7 +114,7 @@ const char* esm_attn_status_string(esm_attn_status_t status);
 /* Workspace bytes that esm_attn_fwd / esm_attn_bwd need for these sizes
  * (a pure host computation; 0 for arguments the calls would reject). The
  * workspace holds the plan (rotary cos/sin table and work-item schedule), the
- * rotated q^ and k^ (bf16 [T][H][d] each) and, for the backward, drow
+ * rotated k^ and, for the backward, q^ (bf16 [T][H][d] each) and drow
  * ([H][T] entries of 16 bytes: LSE * log2(e) and the row sum
  * D = rowsum(dO * O), each negated and split into three bf16 values). */
 size_t esm_attn_fwd_workspace_bytes(int32_t batch, int32_t total_tokens,
@@ -222,7 +222,9 @@ esm_attn_status_t esm_attn_plan(const int32_t* cu_seqlens, int32_t batch,
  * q_rot == q and k_rot == k with equal strides (a fused layer rotates q and
  * k inside its [T][3][H][d] projection output); q_rot == q without
  * k_rot == k, or in place with different strides, is
- * ESM_ATTN_ERR_INVALID_ARGUMENT. Otherwise outputs must not overlap inputs. */
+ * ESM_ATTN_ERR_INVALID_ARGUMENT. Otherwise outputs must not overlap inputs.
+ * q = q_rot = NULL rotates k alone (for esm_attn_fwd_rotq_planned, which
+ * rotates the queries itself); k_rot == k is then in place. */
 esm_attn_status_t esm_attn_rotate_planned(
     const uint16_t* q, const uint16_t* k, int32_t in_row_stride,
     int32_t batch, int32_t total_tokens, int32_t max_seqlen,
@@ -240,6 +242,29 @@ esm_attn_status_t esm_attn_fwd_planned(
     int32_t batch, int32_t total_tokens, int32_t max_seqlen,
     int32_t num_heads, int32_t head_dim, float softmax_scale,
     uint16_t* o, float* lse,
+    const void* plan, size_t plan_bytes, void* stream);
+
+/* Forward that rotates the queries itself: q is the unrotated query, with
+ * k_rot (esm_attn_rotate_planned's k_rot, e.g. from its k-alone mode) and v
+ * at token row stride qkv_row_stride. Each work item turns and scales its
+ * own query rows exactly as esm_attn_rotate_planned does (the plan's table,
+ * the same float32 operations, one rounding to bf16), so o and lse are
+ * bitwise those of esm_attn_rotate_planned followed by esm_attn_fwd_planned;
+ * the rotation pass then moves half the bytes. softmax_scale and rope_base
+ * as for esm_attn_rotate_planned (rope_base = 0: no rotation). If q_rot is
+ * not NULL, the rotated rows q^ are written there with stride
+ * qkv_row_stride, for the backward: rows of tokens inside a sequence's
+ * first max_seqlen tokens, bitwise the rotation pass's q_rot (others are not
+ * written). q_rot == q rotates in place (each item's query rows are read by
+ * that item alone, before it writes them); otherwise q_rot must not overlap
+ * an input. The operation is esm_attn_fwd's, defined at the top of this
+ * file. */
+esm_attn_status_t esm_attn_fwd_rotq_planned(
+    const uint16_t* q, const uint16_t* k_rot, const uint16_t* v,
+    int32_t qkv_row_stride,
+    int32_t batch, int32_t total_tokens, int32_t max_seqlen,
+    int32_t num_heads, int32_t head_dim, float softmax_scale, float rope_base,
+    uint16_t* o, float* lse, uint16_t* q_rot,
     const void* plan, size_t plan_bytes, void* stream);
 
 /* Split-KV forward: the same result as esm_attn_fwd_planned (to fp32

@@ -40,8 +40,8 @@ esm_attn_status_t check_sizes(int32_t B, int32_t T, int32_t maxL, int32_t H, int
   return ESM_ATTN_OK;
 }
 
-// Plan = rotary table + schedule. The one-shot calls append the rotated q~
-// and k~ ([T][H][d] bf16 each) and, for the backward, drow ([H][T] entries
+// Plan = rotary table + schedule. The one-shot calls append the rotated k~
+// and, for the backward, q~ ([T][H][d] bf16 each) and drow ([H][T] entries
 // of 16 bytes: -LSE log2 e, then -D, each split into three bf16 values).
 Layout make_layout(int32_t B, int32_t T, int32_t maxL, int32_t H, int32_t d, bool bwd) {
   Layout l;
@@ -60,7 +60,7 @@ Layout make_layout(int32_t B, int32_t T, int32_t maxL, int32_t H, int32_t d, boo
   l.pos = take((size_t)(T > 0 ? T : 1) * sizeof(int32_t));
   l.plan = off;
   const size_t elems = (size_t)T * H * d;
-  l.qrot = take(elems * sizeof(uint16_t));
+  if (bwd) l.qrot = take(elems * sizeof(uint16_t));  // (the forward rotates q in place of use)
   l.krot = take(elems * sizeof(uint16_t));
   if (bwd) l.drow = take((size_t)T * H * kDrowEntryBytes);
   l.total = off;
@@ -211,11 +211,13 @@ esm_attn_status_t esm_attn_rotate_planned(const uint16_t* q, const uint16_t* k,
   if ((s = check_stride(in_row_stride, total_tokens, num_heads, head_dim)) != ESM_ATTN_OK ||
       (s = check_stride(out_row_stride, total_tokens, num_heads, head_dim)) != ESM_ATTN_OK)
     return s;
-  // in place: both outputs on their inputs, with the same stride
-  const bool qin = q_rot == q, kin = k_rot == k;
+  // k alone: q and q_rot both null
+  const bool k_only = q == nullptr && q_rot == nullptr;
+  // in place: both outputs on their inputs (or k_rot on k alone), with the same stride
+  const bool qin = k_only ? k_rot == k : q_rot == q, kin = k_rot == k;
   if (qin != kin || (qin && in_row_stride != out_row_stride)) return ESM_ATTN_ERR_INVALID_ARGUMENT;
   if (total_tokens == 0) return ESM_ATTN_OK;
-  const void* ptrs[] = {q, k, q_rot, k_rot, plan};
+  const void* ptrs[] = {k, k_rot, plan, k_only ? k : q, k_only ? k_rot : q_rot};
   for (const void* p : ptrs)
     if (p == nullptr || !aligned16(p)) return ESM_ATTN_ERR_INVALID_ARGUMENT;
   const Layout l = make_layout(batch, total_tokens, max_seqlen, num_heads, head_dim, false);
@@ -270,6 +272,49 @@ esm_attn_status_t esm_attn_fwd_planned(const uint16_t* q_rot, const uint16_t* k_
   a.ld_qkv = qkv_row_stride;
   fill_common(&a, total_tokens, num_heads, softmax_scale);
   if (launch_fwd(head_dim, a, l.n_slots, false, reinterpret_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return ESM_ATTN_ERR_HIP;
+  return ESM_ATTN_OK;
+}
+
+esm_attn_status_t esm_attn_fwd_rotq_planned(const uint16_t* q, const uint16_t* k_rot,
+                                            const uint16_t* v, int32_t qkv_row_stride,
+                                            int32_t batch, int32_t total_tokens,
+                                            int32_t max_seqlen, int32_t num_heads,
+                                            int32_t head_dim, float softmax_scale,
+                                            float rope_base, uint16_t* o, float* lse,
+                                            uint16_t* q_rot, const void* plan, size_t plan_bytes,
+                                            void* stream) {
+  esm_attn_status_t s = check_sizes(batch, total_tokens, max_seqlen, num_heads, head_dim);
+  if (s != ESM_ATTN_OK) return s;
+  if ((s = check_scalars(softmax_scale, rope_base)) != ESM_ATTN_OK) return s;
+  if ((s = check_stride(qkv_row_stride, total_tokens, num_heads, head_dim)) != ESM_ATTN_OK)
+    return s;
+  if (total_tokens == 0) return ESM_ATTN_OK;
+  const void* ptrs[] = {q, k_rot, v, o, lse, plan};
+  for (const void* p : ptrs)
+    if (p == nullptr || !aligned16(p)) return ESM_ATTN_ERR_INVALID_ARGUMENT;
+  if (q_rot != nullptr && !aligned16(q_rot)) return ESM_ATTN_ERR_INVALID_ARGUMENT;
+  const Layout l = make_layout(batch, total_tokens, max_seqlen, num_heads, head_dim, false);
+  if (plan_bytes < l.plan) return ESM_ATTN_ERR_WORKSPACE_TOO_SMALL;
+  if (max_seqlen == 0) return ESM_ATTN_OK;  // every sequence is empty
+  const char* ws = static_cast<const char*>(plan);
+  AttnArgs a = {};
+  a.q = q;  // raw: each item rotates its own query rows
+  a.k = k_rot;
+  a.v = v;
+  a.out = o;
+  a.lse = lse;
+  a.q_out = q_rot;
+  // the table region is always passed (the kernel loads from it unconditionally);
+  // rope_base = 0 switches the rotation off
+  a.rope = reinterpret_cast<const float2*>(ws + l.rope);
+  a.rope_base = rope_base;
+  a.q_mul = softmax_scale * kLog2e;  // as in esm_attn_rotate_planned
+  a.items = reinterpret_cast<const Item*>(ws + l.items);
+  a.ld_qkv = qkv_row_stride;
+  fill_common(&a, total_tokens, num_heads, softmax_scale);
+  if (launch_fwd_rotq(head_dim, a, l.n_slots, reinterpret_cast<hipStream_t>(stream)) !=
       hipSuccess)
     return ESM_ATTN_ERR_HIP;
   return ESM_ATTN_OK;
@@ -501,21 +546,19 @@ esm_attn_status_t esm_attn_fwd(const uint16_t* q, const uint16_t* k, const uint1
                : ESM_ATTN_ERR_HIP;
   }
   char* ws = static_cast<char*>(workspace);
-  uint16_t* qr = reinterpret_cast<uint16_t*>(ws + l.qrot);
   uint16_t* kr = reinterpret_cast<uint16_t*>(ws + l.krot);
   if ((s = esm_attn_plan(cu_seqlens, batch, total_tokens, max_seqlen, num_heads, head_dim,
                          rope_base, ws, l.plan, stream)) != ESM_ATTN_OK)
     return s;
   const int32_t ld = num_heads * head_dim;
-  // the rotation pass also applies softmax_scale log2(e) to q, so it runs
-  // with the rotary embedding off too
-  if ((s = esm_attn_rotate_planned(q, k, ld, batch, total_tokens, max_seqlen, num_heads,
-                                   head_dim, softmax_scale, rope_base, qr, kr, ld, ws, l.plan,
-                                   stream)) != ESM_ATTN_OK)
+  // k~ by the rotation pass; the forward rotates (and scales) its own query rows
+  if ((s = esm_attn_rotate_planned(nullptr, k, ld, batch, total_tokens, max_seqlen, num_heads,
+                                   head_dim, softmax_scale, rope_base, nullptr, kr, ld, ws,
+                                   l.plan, stream)) != ESM_ATTN_OK)
     return s;
-  return esm_attn_fwd_planned(qr, kr, v, ld, batch, total_tokens,
-                              max_seqlen, num_heads, head_dim, softmax_scale, o, lse, ws, l.plan,
-                              stream);
+  return esm_attn_fwd_rotq_planned(q, kr, v, ld, batch, total_tokens, max_seqlen, num_heads,
+                                   head_dim, softmax_scale, rope_base, o, lse, nullptr, ws, l.plan,
+                                   stream);
 }
 
 esm_attn_status_t esm_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,

@@ -89,10 +89,20 @@ constexpr float kLazyBound = 65536.0f;  // 2^16: largest block sum of P kept
 // rotation pass does (the rotary table built in LDS with the plan's formula),
 // and the at most two key blocks of the sequence sit in the two LDS stages
 // for the whole item.
-template <int D, bool SPLIT, bool SMALL = false>
+//
+// ROTQ: q is the raw query; each item rotates and scales its own query rows
+// in registers with the plan's rotary table, the same float32 operations as
+// the rotation pass (so O and LSE are bitwise those of the rotation pass
+// followed by the plain forward), and writes those q~ rows to q_out when
+// asked (for the backward), right after the first block's barrier so that
+// the writes drain under the block's work. Only k then needs the rotation
+// pass. q_out may be q itself: an item's query rows are read by no other
+// workgroup, and its own waves load them before the first block barrier and
+// store them after it.
+template <int D, bool SPLIT, bool SMALL = false, bool ROTQ = false>
 __global__ __launch_bounds__(256, SMALL ? 2 : FwdCfg<D>::OCC) void fwd_kernel(AttnArgs a) {
   using C = FwdCfg<D>;
-  static_assert(!(SPLIT && SMALL), "one mode");
+  static_assert((int)SPLIT + (int)SMALL + (int)ROTQ <= 1, "one mode");
   static_assert(!SMALL || (C::BN == 64 && C::NSTAGE * C::BN >= kSmallMaxLen), "small path");
   // (the small path adds the rotary table of its positions: float2 [128][D/2])
   constexpr int TAB = SMALL ? kSmallMaxLen * (D / 2) * 4 : 0;
@@ -200,13 +210,34 @@ __global__ __launch_bounds__(256, SMALL ? 2 : FwdCfg<D>::OCC) void fwd_kernel(At
   u32x4 qreg[C::NS];
 #pragma unroll
   for (int s = 0; s < C::NS; ++s) qreg[s] = ld16(Qg + qc * rs + 16 * s + 8 * g);
-  if constexpr (SMALL) {
-    // q~ = bf16(fl32(q_mul fl32(R(p) q))), as the rotation pass computes it;
-    // lane (r, g) holds d = 16 s + 8 g + e, whose rotary partner d + D/2 is
-    // in k-step s + NS/2 of the same lane (d >= 32) or in lane ^ 32 (d = 16)
+  // lane (r, g) holds d = 16 s + 8 g + e, whose rotary partner d + D/2 is in
+  // k-step s + NS/2 of the same lane (d >= 32) or in lane ^ 32 (d = 16); the
+  // pairs of rotation step s start at j = 16 s + 8 g (j = 0 at d = 16). The
+  // position of row qc is qc itself (< max_seqlen, the table's rows).
+  constexpr int NR = (C::NS + 1) / 2;  // rotation steps
+  auto pair0 = [&](int s) { return C::NS == 1 ? 0 : 16 * s + 8 * g; };
+  // ROTQ: the (cos, sin) of the lane's pairs come from the plan's table in
+  // global memory. They are loaded here, next to the q rows and outside any
+  // branch, so that the prologue waits for both at once (a load under a
+  // branch is awaited at the branch's end: one more memory round trip per
+  // item each). The table pointer is always valid memory; with the rotation
+  // off its contents are not used.
+  float2 csq[ROTQ ? NR : 1][8];
+  if constexpr (ROTQ) {
+#pragma unroll
+    for (int s = 0; s < NR; ++s) load_cs8(a.rope, (int64_t)qc * (D / 2) + pair0(s), csq[s]);
+    // (an empty asm that takes the values keeps the compiler from sinking
+    // the loads into the branch below)
+#pragma unroll
+    for (int s = 0; s < NR; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(csq[s][e].x), "+v"(csq[s][e].y));
+  }
+  if constexpr (SMALL || ROTQ) {
+    // q~ = bf16(fl32(q_mul fl32(R(p) q))), as the rotation pass computes it
     const bool rope = a.rope_base != 0.f;
 #pragma unroll
-    for (int s = 0; s < (C::NS + 1) / 2; ++s) {
+    for (int s = 0; s < NR; ++s) {
       u32x4 xl = qreg[s], xh;
       if constexpr (C::NS == 1) {
 #pragma unroll
@@ -222,7 +253,7 @@ __global__ __launch_bounds__(256, SMALL ? 2 : FwdCfg<D>::OCC) void fwd_kernel(At
       float lo[8], hi[8];
       unpack8(xl, lo);
       unpack8(xh, hi);
-      if (rope) rotate8<false, false>(lo, hi, tab + qc * (D / 2) + (C::NS == 1 ? 0 : 16 * s + 8 * g));
+      if (rope) rotate8<false, false>(lo, hi, SMALL ? tab + qc * (D / 2) + pair0(s) : csq[s]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         lo[e] *= a.q_mul;
@@ -235,7 +266,7 @@ __global__ __launch_bounds__(256, SMALL ? 2 : FwdCfg<D>::OCC) void fwd_kernel(At
         qreg[s + C::NS / 2] = pack8(hi);
       }
     }
-    __syncthreads();  // the prologue's LDS tiles are complete
+    if constexpr (SMALL) __syncthreads();  // the prologue's LDS tiles are complete
   }
 #pragma unroll
   for (int s = 0; s < C::NS; ++s)
@@ -276,6 +307,16 @@ __global__ __launch_bounds__(256, SMALL ? 2 : FwdCfg<D>::OCC) void fwd_kernel(At
       wait_vmem<0>();
     block_barrier();
     if (kb + C::NSTAGE - 1 < nkb) issue(kb + C::NSTAGE - 1, next);
+    if constexpr (ROTQ) {
+      // q~ rows for the backward, written under the first block's work (at
+      // the item's end they measured as an extra serial cost); every wave
+      // has consumed its own q loads before this barrier, so in place is safe
+      if (kb == 0 && a.q_out != nullptr && qi < L) {
+        uint16_t* Qo = a.q_out + base + (int64_t)qi * rs;
+#pragma unroll
+        for (int s = 0; s < C::NS; ++s) st16(Qo + 16 * s + 8 * g, qreg[s]);
+      }
+    }
     const uint16_t* Ks = lds + stage * C::STAGE;
     const uint16_t* Vs = Ks + C::TILE;
     stage = stage + 1 == C::NSTAGE ? 0 : stage + 1;
@@ -446,6 +487,18 @@ hipError_t launch_fwd_small(int head_dim, const AttnArgs& a, hipStream_t stream)
     case 16: fwd_kernel<16, false, true><<<n, 256, 0, stream>>>(a); break;
     case 32: fwd_kernel<32, false, true><<<n, 256, 0, stream>>>(a); break;
     case 64: fwd_kernel<64, false, true><<<n, 256, 0, stream>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_rotq(int head_dim, const AttnArgs& a, int64_t n_slots, hipStream_t stream) {
+  const unsigned n = (unsigned)n_slots;
+  switch (head_dim) {
+    case 16: fwd_kernel<16, false, false, true><<<n, 256, 0, stream>>>(a); break;
+    case 32: fwd_kernel<32, false, false, true><<<n, 256, 0, stream>>>(a); break;
+    case 64: fwd_kernel<64, false, false, true><<<n, 256, 0, stream>>>(a); break;
+    case 128: fwd_kernel<128, false, false, true><<<n, 256, 0, stream>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -28,7 +28,7 @@ hipError_t launch_prep(const PrepArgs& a, hipStream_t stream);
 struct RotArgs {
   const uint16_t* q;    // may equal q_rot (in place, same row stride)
   const uint16_t* k;    // may equal k_rot
-  uint16_t* q_rot;
+  uint16_t* q_rot;      // null: k alone is rotated (q unread)
   uint16_t* k_rot;
   int32_t ld_in;        // elements between consecutive tokens' rows of q, k
   int32_t ld_out;       // ... of q_rot, k_rot
@@ -85,6 +85,12 @@ struct AttnArgs {
   int32_t B, max_seqlen;
   float rope_base;      // 0 = no rotation
   float q_mul;          // fl32(softmax_scale * log2(e)), as in the rotation pass
+  // forward that rotates its own query rows (launch_fwd_rotq): q is the raw
+  // query, rotated and scaled as the rotation pass does with the table `rope`
+  // (always a readable [max_seqlen][d/2] region; rope_base = 0: no rotation)
+  // and q_mul; q~ rows are written to q_out when it is not null (same row
+  // stride as q; q_out == q is allowed)
+  uint16_t* q_out;
 };
 
 // Longest sequence of the small-batch path (one 128-row work item).
@@ -93,6 +99,9 @@ constexpr int kSmallMaxLen = 128;
 hipError_t launch_fwd(int head_dim, const AttnArgs& a, int64_t n_slots, bool split,
                       hipStream_t stream);
 hipError_t launch_fwd_fp8(int head_dim, const AttnArgs& a, int64_t n_slots, hipStream_t stream);
+// Forward on raw q (each item rotates its own 128 query rows in registers)
+// and rotated k~; optionally writes q~ for the backward.
+hipError_t launch_fwd_rotq(int head_dim, const AttnArgs& a, int64_t n_slots, hipStream_t stream);
 // Small-batch path (max_seqlen <= kSmallMaxLen, head_dim <= 64): one
 // workgroup per (sequence, head), B * H of them, no plan, q and k rotated
 // inside the kernels. The forward writes o and lse; the backward writes

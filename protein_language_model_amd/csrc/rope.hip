@@ -28,7 +28,8 @@ constexpr int kRotUnits = 4;  // 8-pair units per thread (rotation pass)
 // stretch of memory) and the cos/sin row of a position is reused by every
 // head of the token. Each thread issues the loads of kRotUnits units before
 // any arithmetic. Positions come from the plan (clamped into the table).
-template <int D, bool ROPE>
+// Q false: k alone (the forward that rotates its own query rows needs k~ only).
+template <int D, bool ROPE, bool Q>
 __global__ __launch_bounds__(256) void rotate_kernel(RotArgs a) {
   constexpr int UPR = D / 16;  // units per head row
   const int upt = a.H * UPR;   // units per token
@@ -46,8 +47,10 @@ __global__ __launch_bounds__(256) void rotate_kernel(RotArgs a) {
       const int h = rest / UPR, j0 = (rest % UPR) * 8;
       const int64_t off = t * a.ld_in + h * D + j0;
       offo[x] = t * a.ld_out + h * D + j0;
-      ql[x] = ld16(a.q + off);
-      qh[x] = ld16(a.q + off + D / 2);
+      if (Q) {
+        ql[x] = ld16(a.q + off);
+        qh[x] = ld16(a.q + off + D / 2);
+      }
       kl[x] = ld16(a.k + off);
       kh[x] = ld16(a.k + off + D / 2);
       if (ROPE) {
@@ -60,19 +63,21 @@ __global__ __launch_bounds__(256) void rotate_kernel(RotArgs a) {
   for (int x = 0; x < kRotUnits; ++x) {
     const int64_t u = u0 + 256 * x;
     if (u < total) {
-      u32x4 q0 = ql[x], q1 = qh[x], k0 = kl[x], k1 = kh[x];
+      u32x4 k0 = kl[x], k1 = kh[x];
       float lo[8], hi[8];
-      unpack8(q0, lo);
-      unpack8(q1, hi);
-      if (ROPE) rotate8<false, false>(lo, hi, cs[x]);
-      // q~ = bf16(fl32(q_mul * fl32(R(p) q))): one more fp32 rounding, then one to bf16
+      if (Q) {
+        unpack8(ql[x], lo);
+        unpack8(qh[x], hi);
+        if (ROPE) rotate8<false, false>(lo, hi, cs[x]);
+        // q~ = bf16(fl32(q_mul * fl32(R(p) q))): one more fp32 rounding, then one to bf16
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        lo[e] *= a.q_mul;
-        hi[e] *= a.q_mul;
+        for (int e = 0; e < 8; ++e) {
+          lo[e] *= a.q_mul;
+          hi[e] *= a.q_mul;
+        }
+        st16(a.q_rot + offo[x], pack8(lo));
+        st16(a.q_rot + offo[x] + D / 2, pack8(hi));
       }
-      q0 = pack8(lo);
-      q1 = pack8(hi);
       if (ROPE) {
         unpack8(k0, lo);
         unpack8(k1, hi);
@@ -80,8 +85,6 @@ __global__ __launch_bounds__(256) void rotate_kernel(RotArgs a) {
         k0 = pack8(lo);
         k1 = pack8(hi);
       }
-      st16(a.q_rot + offo[x], q0);
-      st16(a.q_rot + offo[x] + D / 2, q1);
       st16(a.k_rot + offo[x], k0);
       st16(a.k_rot + offo[x] + D / 2, k1);
     }
@@ -151,10 +154,15 @@ static hipError_t launch_rotate_d(bool rope, const RotArgs& a, hipStream_t st) {
   const int64_t units = (int64_t)a.T * a.H * (D / 16);
   const unsigned grid = (unsigned)((units + 256 * kRotUnits - 1) / (256 * kRotUnits));
   if (grid == 0) return hipSuccess;
-  if (rope)
-    rotate_kernel<D, true><<<grid, 256, 0, st>>>(a);
+  const bool q = a.q_rot != nullptr;
+  if (rope && q)
+    rotate_kernel<D, true, true><<<grid, 256, 0, st>>>(a);
+  else if (q)
+    rotate_kernel<D, false, true><<<grid, 256, 0, st>>>(a);
+  else if (rope)
+    rotate_kernel<D, true, false><<<grid, 256, 0, st>>>(a);
   else
-    rotate_kernel<D, false><<<grid, 256, 0, st>>>(a);
+    rotate_kernel<D, false, false><<<grid, 256, 0, st>>>(a);
   return hipGetLastError();
 }
 

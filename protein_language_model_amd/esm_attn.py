@@ -45,6 +45,7 @@ EXPORTED = (
     "esm_attn_plan",
     "esm_attn_rotate_planned",
     "esm_attn_fwd_planned",
+    "esm_attn_fwd_rotq_planned",
     "esm_attn_bwd_planned",
     "esm_attn_check_cu_seqlens_host",
     "esm_attn_schedule_host",
@@ -108,6 +109,9 @@ def lib():
     L.esm_attn_fwd_planned.restype = i32
     L.esm_attn_fwd_planned.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp,
                                        u64, vp]
+    L.esm_attn_fwd_rotq_planned.restype = i32
+    L.esm_attn_fwd_rotq_planned.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, f32,
+                                            vp, vp, vp, vp, u64, vp]
     L.esm_attn_bwd_planned.restype = i32
     L.esm_attn_bwd_planned.argtypes = [vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, f32,
                                        f32, vp, vp, vp, i32, vp, i32, vp, u64, vp]
@@ -336,19 +340,27 @@ def esm_attn_rotate_planned(q, k, batch, max_seqlen, plan, rope_base=10000.0, q_
     k^ = bf16(R(p) k), with the plan's rotary table; returns (q_rot, k_rot).
     softmax_scale (keyword, required) must be the one later given to the
     planned forward and backward on these operands. q and k may be views of a
-    fused [T, 3, H, d] buffer; q_rot=q, k_rot=k rotates in place."""
-    T, H, d = q.shape
-    ld_in = _row_stride(q, k)
-    if q_rot is None:
-        q_rot = torch.empty((T, H, d), dtype=q.dtype, device=q.device)
+    fused [T, 3, H, d] buffer; q_rot=q, k_rot=k rotates in place. q=None
+    rotates k alone (for esm_attn_fwd_rotq_planned) and returns (None, k_rot)."""
+    T, H, d = k.shape
+    if q is None:
+        if q_rot is not None:
+            raise ValueError("q_rot given without q")
+        ld_in = _row_stride(k)
+    else:
+        ld_in = _row_stride(q, k)
+        if q_rot is None:
+            q_rot = torch.empty((T, H, d), dtype=q.dtype, device=q.device)
     if k_rot is None:
         k_rot = torch.empty((T, H, d), dtype=k.dtype, device=k.device)
-    ld_out = _row_stride(q_rot, k_rot)
-    _on_gpu(q.device, q_rot, k_rot)
-    _check_plan(plan, q.device)
-    _check(lib().esm_attn_rotate_planned(_ptr(q), _ptr(k), ld_in, int(batch), T,
+    ld_out = _row_stride(k_rot) if q is None else _row_stride(q_rot, k_rot)
+    _on_gpu(k.device, k_rot, *([] if q is None else [q_rot]))
+    _check_plan(plan, k.device)
+    _check(lib().esm_attn_rotate_planned(None if q is None else _ptr(q), _ptr(k), ld_in,
+                                         int(batch), T,
                                          int(max_seqlen), H, d, float(softmax_scale),
-                                         float(rope_base), _ptr(q_rot),
+                                         float(rope_base),
+                                         None if q is None else _ptr(q_rot),
                                          _ptr(k_rot), ld_out, _ptr(plan), _nbytes(plan),
                                          _stream(stream)))
     return q_rot, k_rot
@@ -374,6 +386,34 @@ def esm_attn_fwd_planned(q_rot, k_rot, v, batch, max_seqlen, plan, softmax_scale
                                       int(max_seqlen), H, d, scale, _ptr(out), _ptr(lse),
                                       _ptr(plan), _nbytes(plan), _stream(stream)))
     return out, lse
+
+
+def esm_attn_fwd_rotq_planned(q, k_rot, v, batch, max_seqlen, plan, softmax_scale=None,
+                              rope_base=10000.0, out=None, lse=None, q_rot=None, stream=None):
+    """Forward on the unrotated q, the rotated k^ (esm_attn_rotate_planned
+    with q=None) and v, which share one token row stride: each work item
+    rotates and scales its own query rows as the rotation pass does, so
+    (out, lse) are bitwise those of the rotation pass followed by
+    esm_attn_fwd_planned. If q_rot is given (same row stride; q_rot=q is
+    in place), the rotated q^ is written there for the backward. Returns
+    (out, lse, q_rot)."""
+    T, H, d = v.shape
+    ld = _row_stride(q, k_rot, v, *([] if q_rot is None else [q_rot]))
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty((T, H, d), dtype=v.dtype, device=v.device)
+    _check_packed((T, H, d), out)
+    if lse is None:
+        lse = torch.empty((H, T), dtype=torch.float32, device=v.device)
+    _check_lse(lse, H, T)
+    _on_gpu(v.device, out, lse)
+    _check_plan(plan, v.device)
+    _check(lib().esm_attn_fwd_rotq_planned(_ptr(q), _ptr(k_rot), _ptr(v), ld, int(batch), T,
+                                           int(max_seqlen), H, d, scale, float(rope_base),
+                                           _ptr(out), _ptr(lse),
+                                           None if q_rot is None else _ptr(q_rot), _ptr(plan),
+                                           _nbytes(plan), _stream(stream)))
+    return out, lse, q_rot
 
 
 def esm_attn_fwd_split_planned(q_rot, k_rot, v, batch, max_seqlen, plan, n_split,
@@ -578,10 +618,13 @@ class _Attention(torch.autograd.Function):
         T, H, d = _check_qkv(q, k, v)
         B = _check_cu(cu_seqlens, q.device)
         plan = esm_attn_plan(cu_seqlens, T, max_seqlen, H, d, rope_base)
-        # (always: the pass also applies softmax_scale log2(e) to q)
-        q_rot, k_rot = esm_attn_rotate_planned(q, k, B, max_seqlen, plan, rope_base,
-                                               softmax_scale=scale)
-        o, lse = esm_attn_fwd_planned(q_rot, k_rot, v, B, max_seqlen, plan, scale)
+        # k^ by the rotation pass; the forward rotates and scales q itself and
+        # writes q^ for the backward
+        _, k_rot = esm_attn_rotate_planned(None, k, B, max_seqlen, plan, rope_base,
+                                           softmax_scale=scale)
+        q_rot = torch.empty_like(q)
+        o, lse, _ = esm_attn_fwd_rotq_planned(q, k_rot, v, B, max_seqlen, plan, scale, rope_base,
+                                              q_rot=q_rot)
         ctx.save_for_backward(q_rot, k_rot, v, o, lse, plan)
         ctx.args = (B, max_seqlen, scale, rope_base)
         return o
@@ -613,10 +656,12 @@ class _AttentionQKV(torch.autograd.Function):
         B = _check_cu(cu_seqlens, qkv.device)
         if plan is None:
             plan = esm_attn_plan(cu_seqlens, T, max_seqlen, H, d, rope_base)
-        esm_attn_rotate_planned(q, k, B, max_seqlen, plan, rope_base, q_rot=q, k_rot=k,
+        # k rotated in place by the rotation pass, q by the forward itself
+        esm_attn_rotate_planned(None, k, B, max_seqlen, plan, rope_base, k_rot=k,
                                 softmax_scale=scale)
         ctx.mark_dirty(qkv)
-        o, lse = esm_attn_fwd_planned(q, k, v, B, max_seqlen, plan, scale)
+        o, lse, _ = esm_attn_fwd_rotq_planned(q, k, v, B, max_seqlen, plan, scale, rope_base,
+                                              q_rot=q)
         ctx.save_for_backward(qkv, o, lse, plan)
         ctx.args = (B, max_seqlen, H, d, scale, rope_base)
         ctx.set_materialize_grads(False)

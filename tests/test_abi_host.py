@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported():
     for n in names:
         assert hasattr(lib, n), n
     assert set(E.EXPORTED) == set(names)
-    assert E.esm_attn_abi_version() == 5
+    assert E.esm_attn_abi_version() == 6
 
 
 def test_single_hip_runtime_is_mapped():
@@ -48,9 +48,9 @@ def test_workspace_sizes():
     fwd = E.esm_attn_fwd_workspace_bytes(16, 16384, 1024, 20, 64)
     bwd = E.esm_attn_bwd_workspace_bytes(16, 16384, 1024, 20, 64)
     plan = E.esm_attn_plan_bytes(16, 16384, 1024, 20, 64)
-    qk = 2 * 16384 * 20 * 64 * 2            # rotated q~ and k~, bf16
-    assert fwd >= plan + qk
-    assert bwd >= fwd + 16384 * 20 * 16  # drow: -LSE log2(e) and -D, 16 bytes a row
+    x = 16384 * 20 * 64 * 2                 # one bf16 [T][H][d] tensor
+    assert fwd >= plan + x                  # rotated k~ (the forward rotates q itself)
+    assert bwd >= fwd + x + 16384 * 20 * 16  # q~; drow: -LSE log2(e) and -D, 16 bytes a row
     assert plan >= 1024 * 32 * 8            # rotary table
     assert E.esm_attn_plan_bytes(16, 16384, 1024, 20, 48) == 0
     assert E.esm_attn_fwd_workspace_bytes(16, 16384, 1024, 20, 48) == 0   # bad head_dim
@@ -170,6 +170,48 @@ def test_in_place_rotation_rules():
     # in place, one stride: only the (too small) plan is left to reject
     assert L.esm_attn_rotate_planned(p, q, 96, 1, T, T, 2, 16, 0.125, 1e4, p, q, 96, p, 4,
                                      None) == E.ERR_WORKSPACE_TOO_SMALL
+
+
+def test_k_only_rotation_and_rotq_forward_validation():
+    """k alone (q = q_rot = NULL) and the forward that rotates q itself are
+    validated on the host like the other planned calls (fake device
+    pointers: a launch would fault, so every case must be rejected)."""
+    L = E.lib()
+    p, q, r, T = 1 << 12, 1 << 13, 1 << 14, 8
+    # k alone, out of place / in place: only the (too small) plan is left to reject
+    assert L.esm_attn_rotate_planned(None, q, 32, 1, T, T, 2, 16, 0.125, 1e4, None, r, 32, p, 4,
+                                     None) == E.ERR_WORKSPACE_TOO_SMALL
+    assert L.esm_attn_rotate_planned(None, q, 96, 1, T, T, 2, 16, 0.125, 1e4, None, q, 96, p, 4,
+                                     None) == E.ERR_WORKSPACE_TOO_SMALL
+    # k alone in place with different strides; q_rot without q; q without q_rot
+    assert L.esm_attn_rotate_planned(None, q, 96, 1, T, T, 2, 16, 0.125, 1e4, None, q, 32, p,
+                                     1 << 30, None) == E.ERR_INVALID_ARGUMENT
+    assert L.esm_attn_rotate_planned(None, q, 32, 1, T, T, 2, 16, 0.125, 1e4, r, q + 4096, 32, p,
+                                     1 << 30, None) == E.ERR_INVALID_ARGUMENT
+    assert L.esm_attn_rotate_planned(r, q, 32, 1, T, T, 2, 16, 0.125, 1e4, None, q + 4096, 32, p,
+                                     1 << 30, None) == E.ERR_INVALID_ARGUMENT
+    f = L.esm_attn_fwd_rotq_planned
+    # (q, k_rot, v, ld, B, T, maxL, H, d, scale, base, o, lse, q_rot, plan, plan_bytes, stream)
+    assert f(p, q, r, 32, 1, T, T, 2, 16, 0.125, 1e4, p, q, None, p, 4,
+             None) == E.ERR_WORKSPACE_TOO_SMALL
+    assert f(p, q, r, 32, 1, T, T, 2, 16, 0.125, 1e4, p, q, p, p, 4,
+             None) == E.ERR_WORKSPACE_TOO_SMALL          # in place
+    assert f(p, q, r, 32, 1, T, T, 2, 16, float("nan"), 1e4, p, q, None, p, 1 << 30,
+             None) == E.ERR_INVALID_ARGUMENT
+    assert f(p, q, r, 32, 1, T, T, 2, 16, 0.125, -1.0, p, q, None, p, 1 << 30,
+             None) == E.ERR_INVALID_ARGUMENT
+    assert f(p, q, r, 32, 1, T, T, 2, 16, 0.125, 1e4, p, q, p + 2, p, 1 << 30,
+             None) == E.ERR_INVALID_ARGUMENT             # misaligned q_rot
+    assert f(p, None, r, 32, 1, T, T, 2, 16, 0.125, 1e4, p, q, None, p, 1 << 30,
+             None) == E.ERR_INVALID_ARGUMENT             # no k_rot
+    assert f(p, q, r, 24, 1, T, T, 2, 16, 0.125, 1e4, p, q, None, p, 1 << 30,
+             None) == E.ERR_INVALID_ARGUMENT             # stride below H*d
+    assert f(p, q, r, 1 << 28, 1, T, T, 2, 16, 0.125, 1e4, p, q, None, p, 1 << 30,
+             None) == E.ERR_UNSUPPORTED
+    assert f(p, q, r, 32, 1, T, T, 2, 48, 0.125, 1e4, p, q, None, p, 1 << 30,
+             None) == E.ERR_UNSUPPORTED                  # head_dim
+    assert f(None, None, None, 32, 1, 0, 0, 2, 16, 0.125, 1e4, None, None, None, None, 0,
+             None) == E.OK                               # empty batch
 
 
 def test_split_forward_and_merge_validation():
@@ -332,7 +374,11 @@ def test_binding_rejects_host_tensors():
     with pytest.raises(ValueError, match="GPU"):
         E.esm_attn_rotate_planned(q, q, 1, 8, plan, softmax_scale=0.125)
     with pytest.raises(ValueError, match="GPU"):
+        E.esm_attn_rotate_planned(None, q, 1, 8, plan, softmax_scale=0.125)
+    with pytest.raises(ValueError, match="GPU"):
         E.esm_attn_fwd_planned(q, q, q, 1, 8, plan)
+    with pytest.raises(ValueError, match="GPU"):
+        E.esm_attn_fwd_rotq_planned(q, q, q, 1, 8, plan)
     with pytest.raises(ValueError, match="GPU"):
         E.esm_attn_bwd_planned(q, q, q, q, q, lse, 1, 8, plan,
                                drow=torch.zeros(4 * 2 * 8, dtype=torch.float32))
