@@ -134,6 +134,29 @@ def _source_sha256():
     return h.hexdigest()
 
 
+def forward_step(E, q, k, v, B, maxL, plan, scale, base, q_rot, k_rot, out=None, lse=None,
+                 mid=None):
+    """The forward half of a training step after the plan: the rotation pass
+    and the forward, with q rotated inside the forward where the library
+    does so (E.fwd_rotates_q: d <= 64) and by the rotation pass otherwise.
+    q_rot / k_rot receive the rotated operands for the backward (q_rot = q,
+    k_rot = k rotates in place). mid() runs between the two calls. Returns
+    (o, lse)."""
+    if E.fwd_rotates_q(v.shape[-1]):
+        E.esm_attn_rotate_planned(None, k, B, maxL, plan, base, k_rot=k_rot, softmax_scale=scale)
+        if mid is not None:
+            mid()
+        o, lse, _ = E.esm_attn_fwd_rotq_planned(q, k_rot, v, B, maxL, plan, scale, base, out=out,
+                                                lse=lse, q_rot=q_rot)
+    else:
+        E.esm_attn_rotate_planned(q, k, B, maxL, plan, base, q_rot=q_rot, k_rot=k_rot,
+                                  softmax_scale=scale)
+        if mid is not None:
+            mid()
+        o, lse = E.esm_attn_fwd_planned(q_rot, k_rot, v, B, maxL, plan, scale, out=out, lse=lse)
+    return o, lse
+
+
 def measured_traffic(workload, kernel_name):
     """HBM bytes per launch of a kernel from the committed rocprofv3 counter
     summary (FETCH_SIZE and WRITE_SIZE, each scaled by the reading of a plain
@@ -229,15 +252,14 @@ def attention_block(args):
         E.esm_attn_plan(cu, T, maxL, H, d, base, plan=plan)
         qkv = F.linear(x, wqkv, bqkv).view(T, 3, H, d)
         mark(1)
-        if fused:
+        if fused:   # q, k rotated in place inside the projection output
             q, k, v = qkv[:, 0], qkv[:, 1], qkv[:, 2]
-            E.esm_attn_rotate_planned(None, k, B, maxL, plan, base, k_rot=k, softmax_scale=scale)
-            o, lse, _ = E.esm_attn_fwd_rotq_planned(q, k, v, B, maxL, plan, scale, base, q_rot=q)
+            o, lse = forward_step(E, q, k, v, B, maxL, plan, scale, base, q, k)
         else:
             q, k, v = qkv[:, 0].contiguous(), qkv[:, 1].contiguous(), qkv[:, 2].contiguous()
-            _, k = E.esm_attn_rotate_planned(None, k, B, maxL, plan, base, softmax_scale=scale)
-            o, lse, q = E.esm_attn_fwd_rotq_planned(q, k, v, B, maxL, plan, scale, base,
-                                                    q_rot=torch.empty_like(q))
+            q_rot, k_rot = torch.empty_like(q), torch.empty_like(k)
+            o, lse = forward_step(E, q, k, v, B, maxL, plan, scale, base, q_rot, k_rot)
+            q, k = q_rot, k_rot
         mark(2)
         F.linear(o.view(T, hid), wo, bo)
         dout = torch.mm(dy, wo).view(T, H, d)
@@ -338,9 +360,8 @@ def packing_study(args):
         q, k, v, do = (buf[n][:T] for n in ("q", "k", "v", "do"))
         qr, kr, o, dq, dk, dv = (outs[n][:T] for n in ("qr", "kr", "o", "dq", "dk", "dv"))
         E.esm_attn_plan(cu, T, maxL, H, d, base, plan=plan)
-        E.esm_attn_rotate_planned(None, k, B, maxL, plan, base, k_rot=kr, softmax_scale=scale)
-        E.esm_attn_fwd_rotq_planned(q, kr, v, B, maxL, plan, scale, base, out=o,
-                                    lse=lse[:H * T].view(H, T), q_rot=qr)
+        forward_step(E, q, k, v, B, maxL, plan, scale, base, qr, kr, out=o,
+                     lse=lse[:H * T].view(H, T))
         E.esm_attn_bwd_planned(qr, kr, v, o, do, lse[:H * T].view(H, T), B, maxL, plan, scale,
                                base, dq=dq, dk=dk, dv=dv, drow=drow[:4 * H * T])
 
@@ -494,13 +515,9 @@ def fp8_study(args):
             attn = float(np.median([e[1].elapsed_time(e[2]) * 1e3 for e in ev]))
             return prep, attn
 
-        def bf16(mid=None):  # k rotation pass, then the forward that rotates q itself
-            E.esm_attn_rotate_planned(None, k, B, maxL, plan, W.ROPE_BASE, k_rot=kr,
-                                      softmax_scale=1.0 / math.sqrt(d))
-            if mid is not None:
-                mid.record(st)
-            E.esm_attn_fwd_rotq_planned(q, kr, v, B, maxL, plan, None, W.ROPE_BASE, out=o,
-                                        lse=lse)
+        def bf16(mid=None):  # the bf16 training path's rotation and forward
+            forward_step(E, q, k, v, B, maxL, plan, 1.0 / math.sqrt(d), W.ROPE_BASE, qr, kr,
+                         out=o, lse=lse, mid=None if mid is None else (lambda: mid.record(st)))
 
         def fp8(mid=None):
             E.esm_attn_quantize_fp8_planned(q, k, B, maxL, plan, qs, ks, W.ROPE_BASE, q8=q8,
@@ -595,10 +612,8 @@ def main():
             return
         E.esm_attn_plan(cu, T, maxL, H, d, base, plan=plan)
         mark(1)
-        E.esm_attn_rotate_planned(None, k, B, maxL, plan, base, k_rot=kr, softmax_scale=scale)
-        mark(2)
-        E.esm_attn_fwd_rotq_planned(q, kr, v, B, maxL, plan, scale, base, out=o, lse=lse,
-                                    q_rot=qr)
+        forward_step(E, q, k, v, B, maxL, plan, scale, base, qr, kr, out=o, lse=lse,
+                     mid=lambda: mark(2))
         mark(3)
         E.esm_attn_bwd_planned(qr, kr, v, o, do, lse, B, maxL, plan, scale, base, dq=dq,
                                drow=drow, passes=E.PASS_DQ)

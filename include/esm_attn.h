@@ -114,7 +114,9 @@ const char* esm_attn_status_string(esm_attn_status_t status);
 /* Workspace bytes that esm_attn_fwd / esm_attn_bwd need for these sizes
  * (a pure host computation; 0 for arguments the calls would reject). The
  * workspace holds the plan (rotary cos/sin table and work-item schedule), the
- * rotated k^ and, for the backward, q^ (bf16 [T][H][d] each) and drow
+ * rotated k^ and, for the backward and for the forward at head_dim 128, q^
+ * (bf16 [T][H][d] each; the forward up to head_dim 64 rotates q inside the
+ * attention kernel, as esm_attn_fwd_rotq_planned) and, for the backward, drow
  * ([H][T] entries of 16 bytes: LSE * log2(e) and the row sum
  * D = rowsum(dO * O), each negated and split into three bf16 values). */
 size_t esm_attn_fwd_workspace_bytes(int32_t batch, int32_t total_tokens,

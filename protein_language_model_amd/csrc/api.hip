@@ -27,6 +27,14 @@ struct Layout {
 
 bool head_dim_ok(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
+// The one-shot forward rotates q inside the attention kernel (and k alone in
+// the rotation pass) up to d = 64. At d = 128 the rotary table of a long
+// sequence (8192 positions x 512 bytes = 4 MB) no longer stays in L2 next to
+// the K/V each XCD streams, and the kernel's table loads cost more than the
+// rotation pass's q half (4 x 8192 tokens, H = 40: forward +266 us, rotation
+// pass -125 us).
+bool fwd_rotates_q(int32_t d) { return d <= 64; }
+
 // Scalar checks shared by the calls and the workspace queries.
 esm_attn_status_t check_sizes(int32_t B, int32_t T, int32_t maxL, int32_t H, int32_t d) {
   if (B < 1 || H < 1 || T < 0 || maxL < 0) return ESM_ATTN_ERR_INVALID_ARGUMENT;
@@ -40,9 +48,10 @@ esm_attn_status_t check_sizes(int32_t B, int32_t T, int32_t maxL, int32_t H, int
   return ESM_ATTN_OK;
 }
 
-// Plan = rotary table + schedule. The one-shot calls append the rotated k~
-// and, for the backward, q~ ([T][H][d] bf16 each) and drow ([H][T] entries
-// of 16 bytes: -LSE log2 e, then -D, each split into three bf16 values).
+// Plan = rotary table + schedule. The one-shot calls append the rotated k~,
+// q~ (except for a forward that rotates q itself), both [T][H][d] bf16, and
+// for the backward drow ([H][T] entries of 16 bytes: -LSE log2 e, then -D,
+// each split into three bf16 values).
 Layout make_layout(int32_t B, int32_t T, int32_t maxL, int32_t H, int32_t d, bool bwd) {
   Layout l;
   l.n_chunks = (int32_t)schedule_num_chunks(B, H);
@@ -60,7 +69,7 @@ Layout make_layout(int32_t B, int32_t T, int32_t maxL, int32_t H, int32_t d, boo
   l.pos = take((size_t)(T > 0 ? T : 1) * sizeof(int32_t));
   l.plan = off;
   const size_t elems = (size_t)T * H * d;
-  if (bwd) l.qrot = take(elems * sizeof(uint16_t));  // (the forward rotates q in place of use)
+  if (bwd || !fwd_rotates_q(d)) l.qrot = take(elems * sizeof(uint16_t));
   l.krot = take(elems * sizeof(uint16_t));
   if (bwd) l.drow = take((size_t)T * H * kDrowEntryBytes);
   l.total = off;
@@ -551,14 +560,23 @@ esm_attn_status_t esm_attn_fwd(const uint16_t* q, const uint16_t* k, const uint1
                          rope_base, ws, l.plan, stream)) != ESM_ATTN_OK)
     return s;
   const int32_t ld = num_heads * head_dim;
-  // k~ by the rotation pass; the forward rotates (and scales) its own query rows
-  if ((s = esm_attn_rotate_planned(nullptr, k, ld, batch, total_tokens, max_seqlen, num_heads,
-                                   head_dim, softmax_scale, rope_base, nullptr, kr, ld, ws,
-                                   l.plan, stream)) != ESM_ATTN_OK)
+  if (fwd_rotates_q(head_dim)) {
+    // k~ by the rotation pass; the forward rotates (and scales) its own query rows
+    if ((s = esm_attn_rotate_planned(nullptr, k, ld, batch, total_tokens, max_seqlen, num_heads,
+                                     head_dim, softmax_scale, rope_base, nullptr, kr, ld, ws,
+                                     l.plan, stream)) != ESM_ATTN_OK)
+      return s;
+    return esm_attn_fwd_rotq_planned(q, kr, v, ld, batch, total_tokens, max_seqlen, num_heads,
+                                     head_dim, softmax_scale, rope_base, o, lse, nullptr, ws,
+                                     l.plan, stream);
+  }
+  uint16_t* qr = reinterpret_cast<uint16_t*>(ws + l.qrot);
+  if ((s = esm_attn_rotate_planned(q, k, ld, batch, total_tokens, max_seqlen, num_heads,
+                                   head_dim, softmax_scale, rope_base, qr, kr, ld, ws, l.plan,
+                                   stream)) != ESM_ATTN_OK)
     return s;
-  return esm_attn_fwd_rotq_planned(q, kr, v, ld, batch, total_tokens, max_seqlen, num_heads,
-                                   head_dim, softmax_scale, rope_base, o, lse, nullptr, ws, l.plan,
-                                   stream);
+  return esm_attn_fwd_planned(qr, kr, v, ld, batch, total_tokens, max_seqlen, num_heads,
+                              head_dim, softmax_scale, o, lse, ws, l.plan, stream);
 }
 
 esm_attn_status_t esm_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,

@@ -1,7 +1,8 @@
 // Backward attention kernels for gfx950. P is recomputed from the LSE the
-// forward stored, so no L x L matrix is kept. The rotation pass stores q~
-// multiplied by softmax_scale * log2(e), so S' = q~ . k~ is the score in log2
-// units and P = exp2(S' - LSE log2 e).
+// forward stored, so no L x L matrix is kept. q~ (from the rotation pass, or
+// written by the forward that rotates its own query rows) carries
+// softmax_scale * log2(e), so S' = q~ . k~ is the score in log2 units and
+// P = exp2(S' - LSE log2 e).
 //
 // Two deterministic passes, no atomics:
 //   dq pass : one workgroup per 128 queries of a (sequence, head) (lane owns a
@@ -22,7 +23,7 @@
 // values vary along the lane's 16 rows, so the dq pass stores them already
 // split (drow: one 16-byte entry per row, -lse2 then -D) and the dkv pass
 // reads them from LDS.
-// q~ and k~ come rotated from the rotation pass. The streamed operands (k~
+// q~ and k~ arrive rotated. The streamed operands (k~
 // and v in the dq pass; q~, dO, LSE and D in the dkv pass) are copied from
 // global memory into swizzled LDS tiles by global_load_lds, in a ring of
 // three LDS stages (the copy of block b + 2 is issued right after the barrier
@@ -336,12 +337,9 @@ __device__ __forceinline__ void small_prologue(const AttnArgs& a, uint16_t* lds,
     }
     uint16_t* Qs = lds + (p / C::BQ) * C::STAGE;
     const int row = p % C::BQ;
-    st16(Qs + tile_off<D>(row, c), ql);
-    st16(Qs + tile_off<D>(row, c + D / 16), qh);
-    st16(Qs + C::TILE + tile_off<D>(row, c), ol);
-    st16(Qs + C::TILE + tile_off<D>(row, c + D / 16), oh);
-    st16(KTs + tile_off<D>(p, c), kl);
-    st16(KTs + tile_off<D>(p, c + D / 16), kh);
+    st_row_halves<D>(Qs, row, c, ql, qh);
+    st_row_halves<D>(Qs + C::TILE, row, c, ol, oh);
+    st_row_halves<D>(KTs, p, c, kl, kh);
   }
   for (int p = tid; p < kSmallMaxLen; p += 256) {
     float lse2 = 0.f, Dq = 0.f;

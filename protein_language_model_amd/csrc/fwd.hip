@@ -2,8 +2,9 @@
 // 128 queries of one (sequence, head); each wave owns 32 queries.
 //
 // Data flow per item:
-//   q~ rows (rotated once per token by the rotation pass) go straight from
-//   global memory into the MFMA B-operand registers, kept for the whole item.
+//   q~ rows (rotated once per token by the rotation pass, or rotated here in
+//   the ROTQ mode below) sit in the MFMA B-operand registers for the whole
+//   item.
 //   For each block of 64 keys (32 at d = 128) the k~ and v rows are copied
 //   from global memory into swizzled LDS tiles by global_load_lds (no register
 //   staging, no vector instructions), in a ring of two LDS stages: the copy
@@ -17,8 +18,9 @@
 //   Lane (q, g) of a wave holds the scores of query q against 16 keys per
 //   32-key tile; a row's values are split over lanes q and q + 32.
 //
-// Scores in log2 units: the rotation pass stores q~ already multiplied by
-// softmax_scale * log2(e), so S' = q~ . k~ = S log2(e) and P = exp2(S' - m).
+// Scores in log2 units: q~ is already multiplied by softmax_scale * log2(e)
+// (by the rotation pass or the ROTQ prologue), so S' = q~ . k~ = S log2(e)
+// and P = exp2(S' - m).
 //
 // Softmax (online, one pass over the keys). The running reference m is the
 // exact row maximum of the first key block. Later blocks are exponentiated
@@ -193,10 +195,8 @@ __global__ __launch_bounds__(256, SMALL ? 2 : FwdCfg<D>::OCC) void fwd_kernel(At
           kh = pack8(hi);
         }
       }
-      st16(Ks + tile_off<D>(row, c), kl);
-      st16(Ks + tile_off<D>(row, c + D / 16), kh);
-      st16(Ks + C::TILE + tile_off<D>(row, c), vl);
-      st16(Ks + C::TILE + tile_off<D>(row, c + D / 16), vh);
+      st_row_halves<D>(Ks, row, c, kl, kh);
+      st_row_halves<D>(Ks + C::TILE, row, c, vl, vh);
     }
   } else {
     issue(0, 0);

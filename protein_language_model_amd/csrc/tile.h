@@ -33,6 +33,24 @@ __device__ __forceinline__ int tile_off(int row, int c) {
   return row * D + 8 * (c ^ swz<D>(row));
 }
 
+// Stores the two rotary halves of 8 pairs of tile row `row` (logical chunks c
+// and c + D/16, c < D/16) with two ds_write_b128. On gfx950 one cycle of a
+// 16-byte LDS write serves 8 consecutive lanes over 32 banks (128 bytes;
+// measured with single-pattern kernels and SQ_LDS_BANK_CONFLICT). With
+// consecutive lanes on consecutive (row, c) the rows of one cycle span two
+// 128-byte windows of the tile; rows of the second window store their upper
+// half first, so that each cycle fills one window's worth of distinct banks
+// (conflict-free for d = 16, 32, 64 at any swizzle of the tile).
+template <int D>
+__device__ __forceinline__ void st_row_halves(uint16_t* T, int row, int c, const u32x4& lo,
+                                              const u32x4& hi) {
+  static_assert(D <= 64, "row halves of one 128-byte window");
+  constexpr int kRowsPerWindow = 64 / D;
+  const bool second = ((row / kRowsPerWindow) & 1) != 0;
+  st16(T + tile_off<D>(row, second ? c + D / 16 : c), second ? hi : lo);
+  st16(T + tile_off<D>(row, second ? c : c + D / 16), second ? lo : hi);
+}
+
 // Lane index computed where it is used: the asm keeps the compiler from
 // hoisting it (and values derived from it) out of a loop, where they would
 // stay live, or be spilled, across the whole loop.

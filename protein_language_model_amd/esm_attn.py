@@ -609,6 +609,14 @@ def esm_attn_bucket_batches(lengths, boundaries, budget, padded=False):
     return [order[offsets[b]:offsets[b + 1]].copy() for b in range(nb.value)]
 
 
+def fwd_rotates_q(head_dim):
+    """Whether a training step should rotate q inside the forward
+    (esm_attn_rotate_planned on k alone + esm_attn_fwd_rotq_planned) rather
+    than in the rotation pass: up to d = 64, as the one-shot forward does (at
+    d = 128 the rotary table of a long sequence competes with K/V for L2)."""
+    return head_dim <= 64
+
+
 class _Attention(torch.autograd.Function):
     """The plan (schedule + rotary table) and the rotated q^, k^ are made once
     in forward and kept for backward in place of q and k."""
@@ -618,13 +626,18 @@ class _Attention(torch.autograd.Function):
         T, H, d = _check_qkv(q, k, v)
         B = _check_cu(cu_seqlens, q.device)
         plan = esm_attn_plan(cu_seqlens, T, max_seqlen, H, d, rope_base)
-        # k^ by the rotation pass; the forward rotates and scales q itself and
-        # writes q^ for the backward
-        _, k_rot = esm_attn_rotate_planned(None, k, B, max_seqlen, plan, rope_base,
-                                           softmax_scale=scale)
-        q_rot = torch.empty_like(q)
-        o, lse, _ = esm_attn_fwd_rotq_planned(q, k_rot, v, B, max_seqlen, plan, scale, rope_base,
-                                              q_rot=q_rot)
+        if fwd_rotates_q(d):
+            # k^ by the rotation pass; the forward rotates and scales q itself
+            # and writes q^ for the backward
+            _, k_rot = esm_attn_rotate_planned(None, k, B, max_seqlen, plan, rope_base,
+                                               softmax_scale=scale)
+            q_rot = torch.empty_like(q)
+            o, lse, _ = esm_attn_fwd_rotq_planned(q, k_rot, v, B, max_seqlen, plan, scale,
+                                                  rope_base, q_rot=q_rot)
+        else:
+            q_rot, k_rot = esm_attn_rotate_planned(q, k, B, max_seqlen, plan, rope_base,
+                                                   softmax_scale=scale)
+            o, lse = esm_attn_fwd_planned(q_rot, k_rot, v, B, max_seqlen, plan, scale)
         ctx.save_for_backward(q_rot, k_rot, v, o, lse, plan)
         ctx.args = (B, max_seqlen, scale, rope_base)
         return o
@@ -656,12 +669,17 @@ class _AttentionQKV(torch.autograd.Function):
         B = _check_cu(cu_seqlens, qkv.device)
         if plan is None:
             plan = esm_attn_plan(cu_seqlens, T, max_seqlen, H, d, rope_base)
-        # k rotated in place by the rotation pass, q by the forward itself
-        esm_attn_rotate_planned(None, k, B, max_seqlen, plan, rope_base, k_rot=k,
-                                softmax_scale=scale)
         ctx.mark_dirty(qkv)
-        o, lse, _ = esm_attn_fwd_rotq_planned(q, k, v, B, max_seqlen, plan, scale, rope_base,
-                                              q_rot=q)
+        if fwd_rotates_q(d):
+            # k rotated in place by the rotation pass, q by the forward itself
+            esm_attn_rotate_planned(None, k, B, max_seqlen, plan, rope_base, k_rot=k,
+                                    softmax_scale=scale)
+            o, lse, _ = esm_attn_fwd_rotq_planned(q, k, v, B, max_seqlen, plan, scale,
+                                                  rope_base, q_rot=q)
+        else:
+            esm_attn_rotate_planned(q, k, B, max_seqlen, plan, rope_base, q_rot=q, k_rot=k,
+                                    softmax_scale=scale)
+            o, lse = esm_attn_fwd_planned(q, k, v, B, max_seqlen, plan, scale)
         ctx.save_for_backward(qkv, o, lse, plan)
         ctx.args = (B, max_seqlen, H, d, scale, rope_base)
         ctx.set_materialize_grads(False)
