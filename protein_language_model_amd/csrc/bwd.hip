@@ -294,11 +294,13 @@ struct DkvCfg {
 template <int D, typename C>
 __device__ __forceinline__ void small_prologue(const AttnArgs& a, uint16_t* lds, uint16_t* KTs,
                                                uint16_t* DSs, int L, int seq0, int h, int tid) {
+  constexpr int TP = small_tab_pitch<D>();
   float2* tab = reinterpret_cast<float2*>(DSs + kSmallMaxLen * kSmallMaxLen);
   const bool rope = a.rope_base != 0.f;
   for (int i = tid; i < L * (D / 2); i += 256)
-    tab[i] = rope ? rope_cs(i / (D / 2), i % (D / 2), D, (double)a.rope_base)
-                  : make_float2(1.f, 0.f);
+    tab[(i / (D / 2)) * TP + i % (D / 2)] =
+        rope ? rope_cs(i / (D / 2), i % (D / 2), D, (double)a.rope_base)
+             : make_float2(1.f, 0.f);
   for (int i = tid; i < kSmallMaxLen * kSmallMaxLen / 8; i += 256) st16(DSs + 8 * i, zero4());
   __syncthreads();
   const int rs = a.ld_qkv, rso = a.H * D;
@@ -319,7 +321,7 @@ __device__ __forceinline__ void small_prologue(const AttnArgs& a, uint16_t* lds,
       float lo[8], hi[8];
       unpack8(ql, lo);
       unpack8(qh, hi);
-      if (rope) rotate8<false, false>(lo, hi, tab + p * (D / 2) + j0);
+      if (rope) rotate8<false, false>(lo, hi, tab + p * TP + j0);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         lo[e] *= a.q_mul;
@@ -330,7 +332,7 @@ __device__ __forceinline__ void small_prologue(const AttnArgs& a, uint16_t* lds,
       if (rope) {
         unpack8(kl, lo);
         unpack8(kh, hi);
-        rotate8<false, false>(lo, hi, tab + p * (D / 2) + j0);
+        rotate8<false, false>(lo, hi, tab + p * TP + j0);
         kl = pack8(lo);
         kh = pack8(hi);
       }
@@ -379,7 +381,8 @@ __global__ __launch_bounds__(256, SMALL ? 1 : DkvCfg<D>::OCC) void bwd_dkv_kerne
   static_assert(!SMALL || (C::BQ == 64 && C::BK == kSmallMaxLen && C::NSTAGE >= 2), "small path");
   constexpr int KT = SMALL ? kSmallMaxLen * D : 0;                    // k~ tile [128][D]
   constexpr int DS = SMALL ? kSmallMaxLen * kSmallMaxLen : 0;         // dS tile [128][128]
-  constexpr int TAB = SMALL ? kSmallMaxLen * (D / 2) * 4 : 0;         // float2 [128][D/2]
+  constexpr int TP = small_tab_pitch<D>();
+  constexpr int TAB = SMALL ? kSmallMaxLen * TP * 4 : 0;              // float2 [128][TP]
   __shared__ __attribute__((aligned(1024))) uint16_t lds[C::LDS + KT + DS + TAB];
 
   Item it;
@@ -601,7 +604,7 @@ __global__ __launch_bounds__(256, SMALL ? 1 : DkvCfg<D>::OCC) void bwd_dkv_kerne
     __syncthreads();
     store_rows<D, ROPE>(F, kSmallMaxLen, 0, L,
                         a.dq + (int64_t)it.seq0 * a.ld_grad + (int64_t)h * D, a.ld_grad, rope,
-                        true, tid);
+                        true, tid, TP);
     __syncthreads();
   }
 
@@ -616,7 +619,8 @@ __global__ __launch_bounds__(256, SMALL ? 1 : DkvCfg<D>::OCC) void bwd_dkv_kerne
   }
   __syncthreads();
   const int64_t baseg = (int64_t)it.seq0 * a.ld_grad + (int64_t)h * D;
-  store_rows<D, ROPE>(F, C::BK, k0, L, a.dk + baseg, a.ld_grad, rope, true, tid);
+  constexpr int rope_pitch = SMALL ? TP : D / 2;
+  store_rows<D, ROPE>(F, C::BK, k0, L, a.dk + baseg, a.ld_grad, rope, true, tid, rope_pitch);
   __syncthreads();
 #pragma unroll
   for (int dt = 0; dt < C::ND; ++dt) {
@@ -627,7 +631,7 @@ __global__ __launch_bounds__(256, SMALL ? 1 : DkvCfg<D>::OCC) void bwd_dkv_kerne
     }
   }
   __syncthreads();
-  store_rows<D, ROPE>(F, C::BK, k0, L, a.dv + baseg, a.ld_grad, rope, false, tid);
+  store_rows<D, ROPE>(F, C::BK, k0, L, a.dv + baseg, a.ld_grad, rope, false, tid, rope_pitch);
 }
 
 hipError_t launch_bwd_small(int head_dim, const AttnArgs& a, hipStream_t st) {

@@ -250,11 +250,12 @@ __device__ constexpr uint64_t store_quad_perm() {
 // Cooperative epilogue: fp32 tile F[rows][D + 4] in LDS (row = position
 // pos0 + row inside the sequence; rows * D / 16 a multiple of 64) ->
 // optional inverse rotation -> bf16 global. A unit is 8 rotary pairs of one
-// row (16 bytes of each half), placed by store_quad_perm.
+// row (16 bytes of each half), placed by store_quad_perm. The rotary table
+// `rope` has rope_pitch entries per position.
 template <int D, bool ROPE>
 __device__ __forceinline__ void store_rows(const float* F, int rows, int pos0, int L,
                                            uint16_t* G, int rs, const float2* rope,
-                                           bool rotate, int tid) {
+                                           bool rotate, int tid, int rope_pitch = D / 2) {
   constexpr int FP = D + 4;
   constexpr int NU = D / 16;  // units per row
   constexpr uint64_t kPerm = store_quad_perm<D>();
@@ -271,7 +272,7 @@ __device__ __forceinline__ void store_rows(const float* F, int rows, int pos0, i
     }
     if (ROPE && rotate) {
       float2 cs[8];
-      load_cs8(rope, pos * (D / 2) + j0, cs);
+      load_cs8(rope, pos * rope_pitch + j0, cs);
       rotate8<true, false>(lo, hi, cs);
     }
     st16(G + pos * rs + j0, pack8(lo));

@@ -107,7 +107,8 @@ __global__ __launch_bounds__(256, SMALL ? 2 : FwdCfg<D>::OCC) void fwd_kernel(At
   static_assert((int)SPLIT + (int)SMALL + (int)ROTQ <= 1, "one mode");
   static_assert(!SMALL || (C::BN == 64 && C::NSTAGE * C::BN >= kSmallMaxLen), "small path");
   // (the small path adds the rotary table of its positions: float2 [128][D/2])
-  constexpr int TAB = SMALL ? kSmallMaxLen * (D / 2) * 4 : 0;
+  constexpr int TP = small_tab_pitch<D>();
+  constexpr int TAB = SMALL ? kSmallMaxLen * TP * 4 : 0;
   __shared__ __attribute__((aligned(1024))) uint16_t lds[C::LDS + TAB];
 
   if (SPLIT && (int)blockIdx.x >= a.n_items) return;  // grid padding
@@ -173,8 +174,9 @@ __global__ __launch_bounds__(256, SMALL ? 2 : FwdCfg<D>::OCC) void fwd_kernel(At
     float2* tw = reinterpret_cast<float2*>(lds + C::LDS);
     const bool rope = a.rope_base != 0.f;
     for (int i = tid; i < L * (D / 2); i += 256)
-      tw[i] = rope ? rope_cs(i / (D / 2), i % (D / 2), D, (double)a.rope_base)
-                   : make_float2(1.f, 0.f);
+      tw[(i / (D / 2)) * TP + i % (D / 2)] =
+          rope ? rope_cs(i / (D / 2), i % (D / 2), D, (double)a.rope_base)
+               : make_float2(1.f, 0.f);
     __syncthreads();
     for (int u = tid; u < nkb * C::BN * (D / 16); u += 256) {
       const int p = u / (D / 16), c = u % (D / 16), j0 = 8 * c;
@@ -190,7 +192,7 @@ __global__ __launch_bounds__(256, SMALL ? 2 : FwdCfg<D>::OCC) void fwd_kernel(At
           float lo[8], hi[8];
           unpack8(kl, lo);
           unpack8(kh, hi);
-          rotate8<false, false>(lo, hi, tab + p * (D / 2) + j0);
+          rotate8<false, false>(lo, hi, tab + p * TP + j0);
           kl = pack8(lo);
           kh = pack8(hi);
         }
@@ -253,7 +255,7 @@ __global__ __launch_bounds__(256, SMALL ? 2 : FwdCfg<D>::OCC) void fwd_kernel(At
       float lo[8], hi[8];
       unpack8(xl, lo);
       unpack8(xh, hi);
-      if (rope) rotate8<false, false>(lo, hi, SMALL ? tab + qc * (D / 2) + pair0(s) : csq[s]);
+      if (rope) rotate8<false, false>(lo, hi, SMALL ? tab + qc * TP + pair0(s) : csq[s]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         lo[e] *= a.q_mul;
