@@ -129,7 +129,12 @@ size_t esm_attn_bwd_workspace_bytes(int32_t batch, int32_t total_tokens,
 /* Forward. q, k, v: pre-rotation inputs, bf16 [T][H][d] (device).
  * cu_seqlens: int32 [batch+1] (device). softmax_scale: usually 1/sqrt(d);
  * any finite value. rope_base: usually 10000; 0 = no rotary embedding.
- * Writes o (bf16 [T][H][d]) and lse (fp32 [H][T], natural log). */
+ * Writes o (bf16 [T][H][d]) and lse (fp32 [H][T], natural log). Runs the
+ * planned steps in its workspace (plan; k, or q and k at head_dim 128,
+ * rotated by the rotation pass; the forward, which rotates q itself up to
+ * head_dim 64), or, when every sequence fits one 128-row work item and
+ * head_dim <= 64, one small-batch kernel; the results are the same either
+ * way (bitwise for o and lse). */
 esm_attn_status_t esm_attn_fwd(
     const uint16_t* q, const uint16_t* k, const uint16_t* v,
     const int32_t* cu_seqlens,

@@ -12,7 +12,9 @@ Functions keep the C names:
   esm_attn_bwd(q, k, v, o, d_o, lse, cu_seqlens, max_seqlen, softmax_scale,
                rope_base) -> (dq, dk, dv)
 the planned steps (esm_attn_plan, esm_attn_rotate_planned,
-esm_attn_fwd_planned, esm_attn_bwd_planned), the workspace queries,
+esm_attn_fwd_planned, esm_attn_fwd_rotq_planned -- the forward that rotates
+q itself, used up to d = 64, see fwd_rotates_q -- and esm_attn_bwd_planned),
+the workspace queries,
 esm_attn_check_cu_seqlens_host, esm_attn_schedule_host, the host batch former
 esm_attn_bucket_batches, the split-KV, merge and FP8 calls, and the autograd
 wrappers `attention` (packed q, k, v) and `attention_qkv` (one fused projection
