@@ -62,7 +62,10 @@ def compare(gpu, inp, seqs=None, heads=None, sharpened=False, grads_exact=True, 
 
     exact (float64 operands, the definition):
       dq, dk, dv: relative Frobenius <= 2e-2 (unless grads_exact is False);
-      O: max-abs <= 1e-2, except on a sharpened softmax (sharpened=True:
+      O: elementwise <= 1e-2 + ulp/2 (O is stored in bf16: even the exact O
+      rounds by up to half an ulp, oracle.tolerances.o_bound; below |O| = 2
+      that is at most 2^-8 over the literal 1e-2), except on a sharpened
+      softmax (sharpened=True:
       q, k x 3 or a scale several times 1/sqrt(d)), where rounding the
       rotated operands to bf16 alone moves O by about 0.1 for any kernel that
       feeds bf16 matrix units; there the exact-mode O error is reported, not
@@ -90,16 +93,15 @@ def compare(gpu, inp, seqs=None, heads=None, sharpened=False, grads_exact=True, 
         report[mode + ".o_maxabs"] = float(err.max()) if err.size else 0.0
         lerr = np.abs(gpu["lse"][heads][:, rows] - LSE[heads][:, rows])
         report[mode + ".lse_maxabs"] = float(lerr.max()) if lerr.size else 0.0
-        if mode == "bf16_operands":
+        if mode == "bf16_operands" or not sharpened:
             ex = err - T.o_bound(orf)
             if ex.size and ex.max() > 0:
                 at = np.unravel_index(int(ex.argmax()), ex.shape)
                 raise AssertionError((label, mode, "excess", float(ex.max()), "at", at,
                                       "gpu", float(og[at]), "oracle", float(orf[at]),
                                       "elements over", int((ex > 0).sum()), "of", ex.size))
+        if mode == "bf16_operands":
             assert report[mode + ".lse_maxabs"] <= LSE_ATOL, (label, report)
-        elif not sharpened:
-            assert report[mode + ".o_maxabs"] <= O_ATOL, (label, mode, report)
         if with_bwd:
             dq, dk, dv = oracle.backward(q, k, v, do, cu, s, base, mode=mode, seqs=seqs,
                                          heads=heads)

@@ -46,3 +46,46 @@ def test_maximum_sequence_length(device, d):
     rot = oracle.rope_rotate(dk, np.arange(L), base)
     gap_k = np.abs(rot.sum(axis=0))
     assert (gap_k <= 1e-2 * np.abs(dk).sum(axis=0)).all(), float(gap_k.max())
+
+
+def _one_shot(inp, device, maxL):
+    import torch
+    from gpu_helpers import to_dev, bf16_f64
+    from protein_language_model_amd import esm_attn as E
+    q, k, v, do = (to_dev(inp[n], device) for n in ("q", "k", "v", "do"))
+    cu = torch.from_numpy(inp["cu_seqlens"]).to(device)
+    s, base = inp["scale"], inp["rope_base"]
+    o, lse = E.esm_attn_fwd(q, k, v, cu, maxL, s, base)
+    dq, dk, dv = E.esm_attn_bwd(q, k, v, o, do, lse, cu, maxL, s, base)
+    torch.cuda.synchronize()
+    out = {n: bf16_f64(t) for n, t in (("o", o), ("dq", dq), ("dk", dk), ("dv", dv))}
+    out["lse"] = lse.cpu().numpy().astype(np.float64)
+    return out
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_overstated_max_seqlen(device, d):
+    """max_seqlen is an upper bound on the lengths: overstating it changes
+    the plan's launch bound and the rotary table's extent, never a result
+    (bitwise equal on the planned path). Raising it from within the
+    small-batch path's 128 tokens to above them switches to the planned
+    kernels: O, LSE, dk, dv bitwise equal, dq to fp32 rounding."""
+    name = {32: "esm2_150m", 64: "esm2_650m", 128: "esm2_15b"}[d]
+    inp = W.make_inputs(name, lengths=[300, 45, 0, 129, 1], num_heads=2)
+    say("case overstated max_seqlen", d)
+    ref = _one_shot(inp, device, 300)
+    for maxL in (301, 1000, 4096):
+        got = _one_shot(inp, device, maxL)
+        for n in ("o", "lse", "dq", "dk", "dv"):
+            np.testing.assert_array_equal(got[n], ref[n], err_msg="%s max_seqlen %d" % (n, maxL))
+    compare(ref, inp, label="overstated max_seqlen d%d" % d)
+    small = W.make_inputs(name, lengths=[100, 7, 64, 0], num_heads=2)
+    a = _one_shot(small, device, 100)
+    b = _one_shot(small, device, 128)
+    c = _one_shot(small, device, 129)   # planned path for d <= 64
+    for n in ("o", "lse", "dq", "dk", "dv"):
+        np.testing.assert_array_equal(a[n], b[n], err_msg=n)
+    for n in ("o", "lse", "dk", "dv"):
+        np.testing.assert_array_equal(a[n], c[n], err_msg=n)
+    assert relf(a["dq"], c["dq"]) <= 1e-3
+    compare(a, small, label="small batch d%d" % d)
