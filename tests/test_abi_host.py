@@ -429,3 +429,30 @@ def test_noalloc_forward_rejects_before_touching_the_gpu():
     assert "no-allocation" in E.status_string(E.ERR_SCRATCH_TOO_SMALL)
     # the 650M-shaped training batch fits
     assert E.esm_attn_fwd_workspace_bytes(16, 16384, 1024, 20, 64) <= E.NOALLOC_SCRATCH_BYTES
+
+
+def test_schedule_of_malformed_cu_seqlens_stays_in_bounds():
+    """The schedule code the planning kernels run (schedule.h, shared with this
+    host model) clamps a malformed cu_seqlens: entries past total_tokens,
+    decreasing or negative entries and lengths above max_seqlen give items
+    whose rows lie inside [0, total_tokens) and whose lengths stay within
+    [1, max_seqlen], so the kernels' row accesses stay in bounds whatever
+    the contents (the values are then wrong, as documented)."""
+    rng = np.random.default_rng(5)
+    for trial in range(200):
+        B = int(rng.integers(1, 12))
+        T = int(rng.integers(0, 3000))
+        maxL = int(rng.integers(0, 1100))
+        H = int(rng.integers(1, 5))
+        cu = rng.integers(-500, T + 700, size=B + 1).astype(np.int32)
+        if trial % 3 == 0:
+            cu = np.sort(cu)  # monotone but out of range and over max_seqlen
+        items = E.esm_attn_schedule_host(cu, T, maxL, H, 128)
+        live = items[items[:, 1] > 0]
+        assert (items[items[:, 1] <= 0] == -1).all()
+        if live.size:
+            seq0, L, h, blk = live.T
+            assert (seq0 >= 0).all() and (seq0 + L <= T).all(), (cu, T)
+            assert (L <= maxL).all() and (L >= 1).all()
+            assert (h >= 0).all() and (h < H).all()
+            assert (blk >= 0).all() and (blk * 128 < L).all()
