@@ -352,6 +352,43 @@ def _full_size_samples(name, inp):
 FULL = ["esm2_8m", "esm2_150m", "esm2_650m", "esm2_3b", "esm2_15b", "esm2_15b_ragged"]
 
 
+def _gradient_identities(gpu, inp, dk_identity=True):
+    """Identities of every (sequence, head) that hold at any size, checked on
+    all of them: the rows of P sum to 1, so sum_j dv_j = sum_i dO_i; and
+    sum_j dS_ij = 0 for every query, so sum_j R(p_j) dk_j = 0. Bounds: each
+    dv_j carries one bf16 rounding (2^-9 relative) and each query's
+    probabilities, as the kernels round them, sum to 1 within 2^-8 (the LSE
+    reading plus the bf16 rounding of P); the dk sum cancels terms of
+    bf16-rounded dS and dk, bounded by 1e-2 of sum_j |dk_j|.
+    dk_identity=False skips the second on a sharpened softmax: there O is the
+    mean under the bf16-rounded forward probabilities while dS uses the
+    unrounded ones, so sum_j dS_ij = dO_i . (O_exact - O_i) is no longer small
+    next to the dk terms (a float64 model of that rounding on a sixtieth of
+    the 3B-shaped pairs gives gaps up to 0.46 against 0.65 measured)."""
+    cu, base = inp["cu_seqlens"], inp["rope_base"]
+    lengths = np.diff(cu)
+    starts = cu[:-1][lengths > 0]
+    if starts.size == 0:
+        return
+    do = oracle.bf16_bits_to_f64(inp["do"])
+    pos = np.arange(inp["T"]) - np.repeat(cu[:-1], lengths)
+    dv, dk = gpu["dv"], gpu["dk"]
+    rot = oracle.rope_rotate(dk, pos, base)
+    sum_dv = np.add.reduceat(dv, starts, axis=0)
+    sum_do = np.add.reduceat(do, starts, axis=0)
+    abs_dv = np.add.reduceat(np.abs(dv), starts, axis=0)
+    abs_do = np.add.reduceat(np.abs(do), starts, axis=0)
+    gap_v = np.abs(sum_dv - sum_do)
+    ex_v = gap_v - (2.0 ** -8 * (abs_dv + abs_do) + 1e-6)
+    assert ex_v.max() <= 0, ("sum dv", float(ex_v.max()), float(gap_v.max()))
+    gap_k = np.abs(np.add.reduceat(rot, starts, axis=0))
+    ex_k = gap_k - 1e-2 * np.add.reduceat(np.abs(dk), starts, axis=0)
+    if dk_identity:
+        assert ex_k.max() <= 0, ("sum R dk", float(ex_k.max()), float(gap_k.max()))
+    say("identities over %d sequences x %d heads: sum dv gap %.3g, sum R dk gap %.3g"
+        % (starts.size, inp["H"], float(gap_v.max()), float(gap_k.max())))
+
+
 @pytest.mark.parametrize("name", FULL)
 def test_full_size_sampled_parity(device, name):
     inp = W.make_inputs(name)
@@ -361,6 +398,7 @@ def test_full_size_sampled_parity(device, name):
     gpu = run_gpu(inp, device)
     for key in ("o", "lse", "dq", "dk", "dv"):
         assert np.isfinite(gpu[key]).all(), key
+    _gradient_identities(gpu, inp, dk_identity=(name != "esm2_3b"))
     # the 3B-shaped workload multiplies q and k by 3 (sharpened softmax): its
     # O against the exact oracle is reported, its gradients are asserted
     compare(gpu, inp, seqs=seqs, heads=heads, sharpened=(name == "esm2_3b"), label=name)
